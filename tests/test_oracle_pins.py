@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each test checks the oracle against something the pages print, a closed form,
+an invariant, a library routine or brute force -- never against a retyped copy
+of its own formula.  Together they are chosen so that a dropped term, a wrong
+sign, a wrong axis or a transposed operand anywhere in the five steps fails at
+least one of them.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _round_sig(x, sig):
+    return float(f"{x:.{sig}g}")
+
+
+# ---- the worked example on page "量化：只压权重，与训练后量化（PTQ）" -------------
+
+@pytest.fixture(scope="module")
+def worked():
+    g = _gold("worked_example.json")
+    X = np.array(g["X"], np.float32)
+    W = np.array(g["W"], np.float32)
+    return g, X, W
+
+
+def test_worked_example_maxima_and_s(worked):
+    g, X, W = worked
+    ax = oracle.calib_absmax(X)
+    aw = oracle.weight_rowmax(W)
+    np.testing.assert_array_equal(ax, np.array(g["amax_x"], np.float32))
+    np.testing.assert_array_equal(aw, np.array(g["amax_w"], np.float32))
+    s, inv_s = oracle.smooth_factors(ax, aw, g["alpha"])
+    got = [_round_sig(v, g["s"]["sig_digits"]) for v in s]
+    assert got == g["s"]["values"]
+    # After smoothing, channel j of X' and row j of W' share the max sqrt(ax*aw).
+    xp = X * inv_s[None, :]
+    wp = s[:, None] * W
+    xmax = np.abs(xp).max(axis=0)
+    wmax = np.abs(wp).max(axis=1)
+    d = g["smoothed_channel_max"]["decimals"]
+    assert [round(float(v), d) for v in xmax] == g["smoothed_channel_max"]["values"]
+    assert [round(float(v), d) for v in wmax] == g["smoothed_channel_max"]["values"]
+
+
+def test_worked_example_steps_and_codes(worked):
+    g, X, W = worked
+    xq0, xs0 = oracle.quant_act(X, None, oracle.PER_TENSOR)
+    ax = oracle.calib_absmax(X)
+    s, inv_s = oracle.smooth_factors(ax, oracle.weight_rowmax(W), g["alpha"])
+    xq1, xs1 = oracle.quant_act(X, inv_s, oracle.PER_TENSOR)
+    st = g["per_tensor_step"]
+    assert round(float(xs0[0]), st["before_decimals"]) == st["before"]
+    assert round(float(xs1[0]), st["after_decimals"]) == st["after"]
+    assert xq0[:, 0].tolist() == g["channel1_codes"]["before"]
+    assert xq1[:, 0].tolist() == g["channel1_codes"]["after"]
+
+
+@pytest.mark.parametrize("gran,key", [(oracle.PER_TENSOR, "per_tensor_act_per_channel_w"),
+                                      (oracle.PER_TOKEN, "per_token_act_per_channel_w")])
+def test_worked_example_relative_errors(worked, gran, key):
+    """The four printed errors pin: per-output-channel weight scales, the
+    activation granularity, the smoothing direction, the dequant epilogue and
+    the relative Frobenius metric all at once (other readings give other
+    numbers)."""
+    g, X, W = worked
+    e = g["relative_error_percent"][key]
+    Y = oracle.matmul_f64(X, W)
+    base = oracle.w8a8_linear(X, W, None, gran)
+    smooth = oracle.w8a8_linear(X, W, g["alpha"], gran)
+    assert round(100 * oracle.rel_fro(base["y32"], Y), e["before_decimals"]) == e["before"]
+    assert round(100 * oracle.rel_fro(smooth["y32"], Y), e["after_decimals"]) == e["after"]
+
+
+# ---- printed constants ---------------------------------------------------------
+
+def test_per_tensor_outlier_step_and_levels():
+    """Page "4.2 W8A8 量化与 SmoothQuant" section 1.2: one channel at 100, the
+    others within 1 -> step 100/127 ~ 0.79 and only 2-3 usable levels
+    (2^8 * m_i / m ~ 2.56) for the small channels."""
+    c = _gold("printed_constants.json")["per_tensor_outlier_step"]
+    rng = np.random.default_rng(7)
+    X = rng.uniform(-1, 1, size=(256, 8)).astype(np.float32)
+    X[:, 3] = rng.uniform(-c["channel_max"], c["channel_max"], size=256).astype(np.float32)
+    X[0, 3] = c["channel_max"]
+    X[1, 0], X[2, 0] = 1.0, -1.0
+    xq, xs = oracle.quant_act(X, None, oracle.PER_TENSOR)
+    assert round(float(xs[0]), c["step_decimals"]) == c["step"]
+    levels = 2 ** 8 * c["other_channel_max"] / c["channel_max"]
+    assert 2 <= levels <= 3
+    small = np.delete(xq, 3, axis=1)
+    distinct = np.unique(small)
+    assert set(distinct.tolist()) <= {-1, 0, 1}
+    assert len(distinct) == 3  # three codes: 2-3 levels as printed
+    assert xq[0, 3] == 127
+
+
+def test_int4_outlier_row():
+    """Page "GBDQ权重与平滑激活量化": 4-bit symmetric scale of the printed row
+    is 89.4/7 ~ 12.8 and every small value codes to 0."""
+    c = _gold("printed_constants.json")["int4_outlier_row"]
+    codes, scale = oracle.quant_sym(np.array(c["row"], np.float32), c["bits"])
+    assert round(scale, c["scale_decimals"]) == c["scale"]
+    big = int(np.argmax(np.abs(c["row"])))
+    assert codes[big] == c["qmax"]
+    assert all(v == c["codes_small_values"] for i, v in enumerate(codes) if i != big)
+
+
+# ---- closed forms of the smoothing factor ----------------------------------------
+
+def _maxima(K, seed):
+    rng = np.random.default_rng(seed)
+    ax = rng.uniform(0.05, 200.0, K).astype(np.float32)
+    aw = rng.uniform(0.001, 0.2, K).astype(np.float32)
+    return ax, aw
+
+
+def test_alpha_zero_closed_form():
+    """alpha = 0: s_j = 1 / max|W_j| (page "4.2 ..." section 4), and then every
+    smoothed weight row has max 1 (up to one fp32 rounding)."""
+    ax, aw = _maxima(513, 1)
+    s, inv_s = oracle.smooth_factors(ax, aw, 0.0)
+    expect = np.array([float(Fraction(1) / Fraction(float(b))) for b in aw], np.float64).astype(np.float32)
+    np.testing.assert_array_equal(s, expect)
+    W = np.random.default_rng(2).normal(0, 0.05, (513, 33)).astype(np.float32)
+    aw2 = oracle.weight_rowmax(W)
+    s2, _ = oracle.smooth_factors(ax, aw2, 0.0)
+    rowmax = np.abs(s2[:, None] * W).max(axis=1)
+    np.testing.assert_allclose(rowmax, 1.0, rtol=2 ** -23, atol=0)
+
+
+def test_alpha_one_closed_form():
+    """alpha = 1: s_j = max|X_j| (page "4.2 ..." section 4), and then every
+    smoothed activation channel has max 1 (reciprocal form: within 1 ulp)."""
+    ax, aw = _maxima(513, 3)
+    s, inv_s = oracle.smooth_factors(ax, aw, 1.0)
+    np.testing.assert_array_equal(s, ax)
+    X = np.random.default_rng(4).normal(0, 3, (64, 513)).astype(np.float32)
+    ax2 = oracle.calib_absmax(X)
+    _, inv2 = oracle.smooth_factors(ax2, aw, 1.0)
+    colmax = np.abs(X * inv2[None, :]).max(axis=0)
+    np.testing.assert_allclose(colmax, 1.0, rtol=2.5 * 2 ** -23, atol=0)
+
+
+def test_alpha_half_is_sqrt_ratio():
+    """alpha = 0.5 is the square root of the ratio of the maxima (page
+    "SmoothQuant大模型平滑量化技术", scale derivation): compare with the exactly
+    rounded sqrt of the exact rational ratio."""
+    ax, aw = _maxima(257, 5)
+    s, _ = oracle.smooth_factors(ax, aw, 0.5)
+    ratio = ax.astype(np.float64) / aw.astype(np.float64)
+    np.testing.assert_allclose(s, np.sqrt(ratio), rtol=2 ** -23)
+
+
+@pytest.mark.parametrize("alpha", [0.25, 0.4, 0.5, 0.6, 0.75, 0.9])
+def test_general_alpha_balance_invariant(alpha):
+    """Derived from the scale formula: after smoothing, channel j of X' has max
+    (ax_j aw_j)^(1-alpha) and row j of W' has max (ax_j aw_j)^alpha."""
+    rng = np.random.default_rng(11)
+    X = rng.normal(0, 1, (128, 96)).astype(np.float32)
+    X[:, [5, 40]] *= 80.0
+    W = rng.normal(0, 0.02, (96, 48)).astype(np.float32)
+    ax, aw = oracle.calib_absmax(X), oracle.weight_rowmax(W)
+    s, inv_s = oracle.smooth_factors(ax, aw, alpha)
+    xmax = np.abs(X * inv_s[None, :]).max(axis=0).astype(np.float64)
+    wmax = np.abs(s[:, None] * W).max(axis=1).astype(np.float64)
+    p = ax.astype(np.float64) * aw.astype(np.float64)
+    np.testing.assert_allclose(xmax, p ** (1 - alpha), rtol=4e-7)
+    np.testing.assert_allclose(wmax, p ** alpha, rtol=4e-7)
+    np.testing.assert_allclose(s, oracle.smooth_factors_f64(ax, aw, alpha), rtol=2 ** -23)
+
+
+def test_floor_on_dead_channels():
+    ax = np.array([0.0, 1.0, 0.0], np.float32)
+    aw = np.array([0.5, 0.0, 0.0], np.float32)
+    s, inv_s = oracle.smooth_factors(ax, aw, 0.5)
+    assert np.all(np.isfinite(s)) and np.all(np.isfinite(inv_s)) and np.all(s > 0)
+
+
+# ---- exact identity (fp64) --------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_equivalence_identity_fp64(cfg):
+    """X diag(s)^-1 diag(s) W = X W (page "大模型训练、适配与推理" section 3.5):
+    in fp64 the two products agree to rounding, rel err <= 1e-12, on each
+    configuration's recipe (reduced sizes)."""
+    inp = synth.make(cfg, M=48, K=192, N=40, calib_chunks=2 if synth.CONFIGS[cfg].calib_chunks else 0,
+                     chunk_tokens=64)
+    x, w = synth.to_numpy(inp.x), synth.to_numpy(inp.w)
+    ax = oracle.calib_absmax(synth.to_numpy(inp.calib))
+    for a in synth.CONFIGS[cfg].alphas:
+        s, _ = oracle.smooth_factors(ax, oracle.weight_rowmax(w), a)
+        y = oracle.matmul_f64(x, w)
+        ys = oracle.smoothed_product_f64(x, w, s)
+        assert oracle.rel_fro(ys, y) <= 1e-12
+
+
+# ---- quantizer properties -----------------------------------------------------------
+
+def test_round_half_to_even():
+    """Ties go to the even code (numpy rounding in the demo of page
+    "SmoothQuant大模型平滑量化技术"); with row max 127 the multiplier is exactly 1."""
+    X = np.array([[127.0, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5, 126.5, 4.5, 0.0, 0.0, 0.0]], np.float32)
+    xq, xs = oracle.quant_act(X, None, oracle.PER_TOKEN)
+    assert xs[0] == np.float32(1.0)
+    assert xq[0].tolist() == [127, 2, 4, -2, 0, 2, 0, 126, 4, 0, 0, 0]
+
+
+def test_quantizer_properties():
+    rng = np.random.default_rng(3)
+    X = (rng.standard_t(4, (37, 200)) * rng.uniform(0.01, 50, (37, 1))).astype(np.float32)
+    X[5] = 0.0
+    xq, xs = oracle.quant_act(X, None, oracle.PER_TOKEN)
+    xqn, xsn = oracle.quant_act(-X, None, oracle.PER_TOKEN)
+    np.testing.assert_array_equal(xqn, -xq)        # odd symmetry
+    np.testing.assert_array_equal(xsn, xs)
+    assert xs[5] == 0 and not xq[5].any()            # all-zero token
+    nz = np.arange(37) != 5
+    assert (np.abs(xq[nz]).max(axis=1) == 127).all()  # row max maps to +-127
+    assert xq.min() >= -127
+    # reconstruction error at most half a step (plus fp32 rounding slack)
+    err = np.abs(xq.astype(np.float64) * xs[:, None] - X)
+    assert (err <= 0.5 * xs[:, None].astype(np.float64) * (1 + 1e-5) + 1e-30).all()
+
+
+def test_reciprocal_vs_division_rarely_differ():
+    """The fp32 reciprocal-multiply realisation of x / scale agrees with the
+    exact rounding of x * 127 / a except at rare rounding boundaries."""
+    rng = np.random.default_rng(9)
+    X = rng.normal(0, 1, (512, 1024)).astype(np.float32)
+    xq, xs = oracle.quant_act(X, None, oracle.PER_TOKEN)
+    a = np.abs(X).max(axis=1).astype(np.float64)
+    exact = np.clip(np.rint(X.astype(np.float64) * 127.0 / a[:, None]), -127, 127)
+    frac = float((exact != xq).mean())
+    assert frac < 1e-4
+    assert np.abs(exact - xq).max() <= 1
+
+
+def test_weight_codes_are_per_output_channel_and_transposed():
+    rng = np.random.default_rng(5)
+    W = rng.normal(0, 0.02, (64, 24)).astype(np.float32)
+    W[:, 7] *= 30.0           # one loud output column
+    s = rng.uniform(0.5, 2.0, 64).astype(np.float32)
+    wq, ws = oracle.quant_weight(W, s)
+    assert wq.shape == (24, 64)
+    wp = s[:, None] * W
+    np.testing.assert_allclose(ws, np.abs(wp).max(axis=0) / 127.0, rtol=2 ** -23)
+    assert (np.abs(wq).max(axis=1) == 127).all()
+    # dequantized weights reproduce W' to half a step per output channel
+    err = np.abs(wq.T.astype(np.float64) * ws[None, :] - wp)
+    assert (err <= 0.5 * ws[None, :] * (1 + 1e-5)).all()
+
+
+# ---- integer GEMM by brute force -------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 7, 37), (9, 3, 64), (4, 6, 130)])
+def test_gemm_brute_force(M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    xq = rng.integers(-127, 128, (M, K), dtype=np.int64).astype(np.int8)
+    wq = rng.integers(-127, 128, (N, K), dtype=np.int64).astype(np.int8)
+    xq[0, :] = 127
+    wq[0, :] = -127
+    acc = oracle.gemm_i8(xq, wq, nthreads=3)
+    X = xq.tolist()
+    Wl = wq.tolist()
+    for i in range(M):
+        for k in range(N):
+            assert acc[i, k] == sum(X[i][j] * Wl[k][j] for j in range(K))
+
+
+def test_gemm_extreme_accumulator():
+    K = 12288
+    xq = np.full((2, K), 127, np.int8)
+    wq = np.full((3, K), -127, np.int8)
+    xq[1] = -127
+    acc = oracle.gemm_i8(xq, wq, nthreads=2)
+    assert acc[0, 0] == -K * 127 * 127 and acc[1, 2] == K * 127 * 127
+
+
+# ---- dequant and bf16 --------------------------------------------------------------
+
+def test_dequant_indices_exact():
+    """With power-of-two scales every product is exact, so y[i, k] must equal
+    acc[i, k] * 2^-i * 2^-2k exactly: pins which scale goes with which axis."""
+    M, N = 6, 5
+    rng = np.random.default_rng(1)
+    acc = rng.integers(-(2 ** 20), 2 ** 20, (M, N)).astype(np.int32)
+    xs = np.array([2.0 ** -i for i in range(M)], np.float32)
+    ws = np.array([2.0 ** (-2 * k) for k in range(N)], np.float32)
+    y32, ybf = oracle.dequant(acc, xs, oracle.PER_TOKEN, ws)
+    for i in range(M):
+        for k in range(N):
+            assert Fraction(float(y32[i, k])) == Fraction(int(acc[i, k])) * Fraction(1, 2 ** (i + 2 * k))
+    y32t, _ = oracle.dequant(acc, xs[:1], oracle.PER_TENSOR, ws)
+    np.testing.assert_array_equal(y32t[0], y32[0])
+
+
+def test_bf16_rounding_matches_torch():
+    """fp32 -> bf16 round to nearest even agrees with torch's conversion on
+    ties, near-ties, subnormals and large values."""
+    rng = np.random.default_rng(0)
+    base = rng.normal(0, 1, 4000).astype(np.float32)
+    u = base.view(np.uint32)
+    ties = ((u & 0xFFFF0000) | 0x8000).view(np.float32)
+    near = ((u & 0xFFFF0000) | 0x7FFF).view(np.float32)
+    odd_ties = ((u | 0x00010000) & 0xFFFF0000 | 0x8000).view(np.float32)
+    special = np.array([0.0, -0.0, 1e-40, -3e-39, 3.0e38, 1.0, 1.00390625, 1.01171875], np.float32)
+    x = np.concatenate([base, ties, near, odd_ties, special])
+    ours = oracle.f32_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+# ---- calibration resume and the direction of the effect ----------------------------
+
+def test_calibration_chunked_equals_single_pass():
+    inp = synth.make(2, M=16, K=256, N=8, calib_chunks=6, chunk_tokens=40)
+    c = synth.to_numpy(inp.calib)
+    whole = oracle.calib_absmax(c)
+    amax = None
+    for part in np.array_split(c, 5):
+        amax = oracle.calib_absmax(part, amax)
+    np.testing.assert_array_equal(whole, amax)
+    # resuming twice over the same data changes nothing (max is idempotent)
+    np.testing.assert_array_equal(oracle.calib_absmax(c, whole), whole)
+    # and matches numpy's reduction
+    np.testing.assert_array_equal(whole, np.abs(oracle.bf16_to_f32(c)).max(axis=0))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 5])
+def test_smoothing_reduces_error_on_outliers(cfg):
+    """On outlier-bearing inputs the smoothed W8A8 output is closer to X W than
+    plain per-tensor W8A8 (direction given by the accuracy table of page
+    "4.2 W8A8 量化与 SmoothQuant" section 7.2 and the worked example)."""
+    c = synth.CONFIGS[cfg]
+    inp = synth.make(cfg, M=64, K=256, N=64, calib_chunks=2 if c.calib_chunks else 0, chunk_tokens=128)
+    x, w = synth.to_numpy(inp.x), synth.to_numpy(inp.w)
+    cal = synth.to_numpy(inp.calib)
+    y = oracle.matmul_f64(x, w)
+    gran = oracle.PER_TENSOR if c.gran == "per_tensor" else oracle.PER_TOKEN
+    base = oracle.rel_fro(oracle.w8a8_linear(x, w, None, oracle.PER_TENSOR)["y32"], y)
+    for a in c.alphas:
+        sm = oracle.rel_fro(oracle.w8a8_linear(x, w, a, gran, calib=cal)["y32"], y)
+        assert sm < base
