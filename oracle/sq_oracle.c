@@ -101,10 +101,15 @@ static void sym_scale(float m, float qmax, float *scale, float *r)
     *r = (m > 0.0f) ? qmax / m : 0.0f;
 }
 
-/* code = clip(round_half_even(v * r), -qmax, qmax) */
+/* code = clip(round_half_even(v * r), -qmax, qmax).  When the group max m is
+ * so small that qmax / m overflows to +inf (m below about 3.7e-37), v * r is
+ * +-inf for v != 0 (clipped to +-qmax) and 0 * inf = NaN for v == 0, which is
+ * taken as code 0. */
 static int sym_code(float v, float r, float qmax)
 {
     float t = rintf(v * r);
+    if (t != t)
+        t = 0.0f;
     if (t > qmax)
         t = qmax;
     if (t < -qmax)

@@ -357,3 +357,14 @@ def test_smoothing_reduces_error_on_outliers(cfg):
     for a in c.alphas:
         sm = oracle.rel_fro(oracle.w8a8_linear(x, w, a, gran, calib=cal)["y32"], y)
         assert sm < base
+
+
+def test_tiny_group_where_multiplier_overflows():
+    """A group whose max is below 127/FLT_MAX: the multiplier is +inf, zero
+    elements code to 0 and non-zero ones saturate with their sign."""
+    X = np.zeros((1, 16), np.float32)
+    X[0, :4] = [1e-38, -5e-39, 0.0, 2e-45]
+    xq, xs = oracle.quant_act(X, None, oracle.PER_TOKEN)
+    assert xq[0, :4].tolist() == [127, -127, 0, 127]
+    assert not xq[0, 4:].any()
+    assert xs[0] == np.float32(np.float32(1e-38) / np.float32(127.0))
