@@ -1,0 +1,199 @@
+/*
+ * sq.h -- C ABI of the SmoothQuant W8A8 linear-layer library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (page "大模型训练、适配与推理" section 3.5; page "4.2 W8A8 量化与
+ * SmoothQuant" sections 3, 4 and 7.1; page "量化：只压权重，与训练后量化（PTQ）"
+ * section on SmoothQuant W8A8): for a linear layer Y = X W, with X[M,K]
+ * (tokens x input channels) and W[K,N] (input channel j = row j), pick one
+ * factor s_j per input channel, divide activation channel j by s_j and
+ * multiply weight row j by s_j.  The product is unchanged in exact arithmetic,
+ * but the activation outlier channels shrink, so both sides quantize well to
+ * 8 bits.  Five calls implement the five steps:
+ *
+ *   1. sq_calib_absmax    per-input-channel max|X| over calibration tokens
+ *   2. sq_smooth_factors  s_j = max|X_j|^alpha / max|W_j|^(1-alpha)
+ *   3. sq_quant_weight    diag(s) W, one symmetric INT8 scale per output channel
+ *   4. sq_quant_act       X diag(s)^-1, one symmetric INT8 scale per token
+ *                         (or per tensor), scales computed at run time
+ *   5. sq_gemm_w8a8       INT8 x INT8 -> int32 GEMM, then
+ *                         y = (acc * x_scale_i) * w_scale_k rounded to bf16
+ *
+ * Arithmetic contract (what the kernels compute, bit for bit):
+ *   - bf16 inputs widen exactly to fp32;
+ *   - s_j is evaluated in fp64 from a = max(amax_x_j, 1e-5f) and
+ *     b = max(amax_w_j, 1e-5f) as a^alpha / b^(1-alpha) (exponents 0, 1/2 and
+ *     1 use the exact forms 1, sqrt, identity; others use fp64 pow) and rounded
+ *     once to fp32; inv_s_j = 1/s_j correctly rounded in fp32;
+ *   - a quantization group (a weight column, a token row or the whole
+ *     activation tensor) with max magnitude m gets scale = fl(m/127) and
+ *     multiplier r = fl(127/m) (0 when m = 0); each value v becomes
+ *     clamp(round_half_even(fl(v * r)), -127, 127);
+ *   - smoothed values are fl(s_j * w) and fl(x * inv_s_j), single roundings;
+ *   - the GEMM accumulates exactly in int32 (K <= 131072 keeps
+ *     |acc| <= K * 127^2 < 2^31), and the epilogue is
+ *     fl(fl(float(acc) * x_scale_i) * w_scale_k), then round-to-nearest-even
+ *     to bf16.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless stated.  Matrices are row-major; ld*
+ *     is the row stride in elements.  Outputs are dense (no stride).
+ *   - Every call is asynchronous on `stream` (NULL = the default stream of the
+ *     current device) and returns after enqueueing.  Buffers must stay valid
+ *     until the stream's work completes.  Calls on one stream are ordered.
+ *   - The caller owns all memory.  The library allocates nothing and keeps no
+ *     mutable global state except a per-thread error message.
+ *   - Arguments are validated before anything is enqueued; a failed check
+ *     returns a negative sq_status, enqueues nothing and records a message for
+ *     sq_last_error().  A launch failure returns SQ_ERR_HIP.
+ *   - Requirements checked: non-NULL required pointers; sizes >= 0;
+ *     K % 16 == 0 and K <= 131072; ld >= row length; matrix base pointers and
+ *     row strides 16-byte aligned (ld * element size % 16 == 0).  M, N and the
+ *     token count T may be any non-negative value (ragged tails are handled).
+ *     Empty problems (a zero size) enqueue nothing and return SQ_OK, except
+ *     sq_gemm_w8a8 with K = 0, which writes y = 0.
+ *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
+ */
+#ifndef SQ_H
+#define SQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SQ_OK = 0,
+    SQ_ERR_INVALID_ARG = -1, /* bad pointer, size, stride or alignment */
+    SQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype, granularity) */
+    SQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than sq_workspace_size() */
+    SQ_ERR_HIP = -4          /* the HIP runtime reported an error at launch */
+} sq_status;
+
+typedef enum { SQ_F32 = 0, SQ_BF16 = 1 } sq_dtype;
+
+typedef enum {
+    SQ_PER_TOKEN = 0, /* one activation scale per row of X   (x_scale has M entries) */
+    SQ_PER_TENSOR = 1 /* one activation scale for all of X   (x_scale has 1 entry)   */
+} sq_act_gran;
+
+typedef enum {
+    SQ_OP_CALIB_ABSMAX = 0,
+    SQ_OP_SMOOTH_FACTORS = 1,
+    SQ_OP_QUANT_WEIGHT = 2,
+    SQ_OP_QUANT_ACT = 3,
+    SQ_OP_GEMM_W8A8 = 4
+} sq_op;
+
+/*
+ * Step 1 -- calibration absmax (page "4.2 W8A8 量化与 SmoothQuant" section 7.1:
+ * activation statistics come from calibration data, one max|X_j| per input
+ * channel; page "量化：只压权重..." SmoothQuant W8A8: X_j is measured on the
+ * calibration set).
+ *
+ *   x     [T, K] row-major, dtype xt (SQ_BF16 or SQ_F32), row stride ldx.
+ *   amax  [K] fp32, IN/OUT running maximum: amax[j] = max(amax[j], max_t |x[t,j]|).
+ *         Zero it before the first chunk; call again with further chunks to
+ *         continue (any chunking gives the same result).  Entries must be
+ *         non-negative (0 or a previous result).
+ */
+sq_status sq_calib_absmax(const void *x, sq_dtype xt, int64_t T, int64_t K, int64_t ldx,
+                          float *amax, hipStream_t stream);
+
+/*
+ * Step 2 -- smoothing factors (page "大模型训练、适配与推理" section 3.5; page
+ * "4.2 W8A8 量化与 SmoothQuant" section 4; W_j is row j of W, the row that
+ * multiplies activation channel j).
+ *
+ *   amax_x  [K] fp32 from step 1.
+ *   w       [K, N] row-major, dtype wt, row stride ldw; or NULL.
+ *   alpha   migration strength in [0, 1].
+ *   s       [K] fp32 out: s_j.
+ *   inv_s   [K] fp32 out: 1/s_j (what step 4 multiplies by).
+ *   amax_w  [K] fp32: if w != NULL, optional output of max_k |W[j,k]| (may be
+ *           NULL); if w == NULL, required INPUT (reuse of a previous result,
+ *           e.g. to try several alpha without re-reading W).
+ */
+sq_status sq_smooth_factors(const float *amax_x, const void *w, sq_dtype wt, int64_t K, int64_t N,
+                            int64_t ldw, float alpha, float *s, float *inv_s, float *amax_w,
+                            hipStream_t stream);
+
+/*
+ * Step 3 -- smoothed weights, per-output-channel symmetric INT8 (page "4.2 W8A8
+ * 量化与 SmoothQuant" section 7.1: the weights W' = diag(s) W are quantized
+ * statically per channel; the channel is the output column, the reading that
+ * reproduces the worked example of page "量化：只压权重...").
+ *
+ *   w        [K, N] row-major, dtype wt, row stride ldw.
+ *   s        [K] fp32, or NULL to quantize W unsmoothed.
+ *   wq       [N, K] int8 out, dense: output channel k's K codes are contiguous
+ *            (the layout sq_gemm_w8a8 reads).
+ *   w_scale  [N] fp32 out: max_j |W'[j,k]| / 127.
+ *   ws       device workspace of at least sq_workspace_size(SQ_OP_QUANT_WEIGHT,
+ *            0, N, K, 0) bytes, 16-byte aligned; its contents are scratch.
+ */
+sq_status sq_quant_weight(const void *w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
+                          const float *s, int8_t *wq, float *w_scale, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Step 4 -- fused smoothing and activation quantization (page "大模型训练、适配
+ * 与推理" section 3.5: X'_ij = X_ij / s_j; page "4.2 W8A8 量化与 SmoothQuant"
+ * section 7.1: per-token scales computed at run time; page "量化：只压权重..."
+ * worked example: per-tensor and per-token activation scales).
+ *
+ *   x        [M, K] row-major, dtype xt, row stride ldx.
+ *   inv_s    [K] fp32 from step 2, or NULL to quantize X unsmoothed.
+ *   g        SQ_PER_TOKEN (x_scale[M]) or SQ_PER_TENSOR (x_scale[1]).
+ *   xq       [M, K] int8 out, dense.
+ *   x_scale  fp32 out (see g).
+ *   ws       workspace of sq_workspace_size(SQ_OP_QUANT_ACT, M, 0, K, g) bytes
+ *            (0 for SQ_PER_TOKEN, where ws may be NULL).
+ */
+sq_status sq_quant_act(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx,
+                       const float *inv_s, sq_act_gran g, int8_t *xq, float *x_scale, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Step 5 -- INT8 GEMM with int32 accumulation and the dequantization epilogue
+ * (page "4.2 W8A8 量化与 SmoothQuant" section 6: the runtime kernel is a plain
+ * INT8 GEMM; page "量化：只压权重..." SmoothQuant W8A8: the activation scale
+ * must be constant along the reduction so it can be applied after the GEMM;
+ * page "GBDQ权重与平滑激活量化": the product is dequantized to BF16).
+ *
+ *   xq, x_scale, g  from step 4 (xq [M, K] dense).
+ *   wq, w_scale     from step 3 (wq [N, K] dense).
+ *   y               [M, N] out, dense, dtype yt: SQ_BF16 (the deployed output)
+ *                   or SQ_F32 (the fp32 value before the bf16 rounding).
+ *   acc_out         [M, N] int32 out, or NULL: the exact accumulators (for
+ *                   verification; costs an extra 4 bytes per output).
+ *   ws              workspace of sq_workspace_size(SQ_OP_GEMM_W8A8, M, N, K, g)
+ *                   bytes (may be 0).
+ */
+sq_status sq_gemm_w8a8(const int8_t *xq, const float *x_scale, sq_act_gran g, const int8_t *wq,
+                       const float *w_scale, int64_t M, int64_t N, int64_t K, void *y, sq_dtype yt,
+                       int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace the call `op` needs for these sizes (0 if none).
+ * Sizes the call does not use are ignored. */
+size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran g);
+
+/* Static English name of a status code. */
+const char *sq_status_str(sq_status status);
+
+/* Message of the last failed call on this host thread ("" if none).  Valid
+ * until the next library call on the same thread. */
+const char *sq_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char *sq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SQ_H */

@@ -1,0 +1,227 @@
+"""SmoothQuant W8A8 linear layer on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libsq.so`` (the C ABI declared in include/sq.h).
+Each function has the name of the C entry point, takes torch tensors that
+live on the GPU, passes their device pointers, strides and the current HIP
+stream, and raises ``SqError`` with the library's message when the call is
+rejected.  No computation happens in Python: every step runs in the HIP
+kernels, and the module refuses to work without the built library.
+
+Build the library first: ``python -m post_quantization_act_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
+    "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
+    "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
+    "sq_gemm_w8a8", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libsq.so")
+
+SQ_F32, SQ_BF16 = 0, 1
+SQ_PER_TOKEN, SQ_PER_TENSOR = 0, 1
+SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, SQ_OP_GEMM_W8A8 = range(5)
+
+EXPORTED_SYMBOLS = (
+    "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
+    "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version",
+)
+
+
+class SqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{sq_status_str(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m post_quantization_act_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    sz = ctypes.c_size_t
+    L.sq_calib_absmax.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    L.sq_smooth_factors.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp]
+    L.sq_quant_weight.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.sq_quant_act.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
+    L.sq_gemm_w8a8.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
+    for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8"):
+        getattr(L, f).restype = ctypes.c_int
+    L.sq_workspace_size.argtypes = [i32, i64, i64, i64, i32]
+    L.sq_workspace_size.restype = sz
+    L.sq_status_str.argtypes = [i32]
+    L.sq_status_str.restype = ctypes.c_char_p
+    L.sq_last_error.argtypes = []
+    L.sq_last_error.restype = ctypes.c_char_p
+    L.sq_version.argtypes = []
+    L.sq_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def sq_status_str(status: int) -> str:
+    return lib().sq_status_str(int(status)).decode()
+
+
+def sq_last_error() -> str:
+    return lib().sq_last_error().decode()
+
+
+def sq_version() -> str:
+    return lib().sq_version().decode()
+
+
+def sq_workspace_size(op: int, M: int, N: int, K: int, gran: int = SQ_PER_TOKEN) -> int:
+    return int(lib().sq_workspace_size(int(op), int(M), int(N), int(K), int(gran)))
+
+
+# ---- marshalling helpers -----------------------------------------------------------
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch.Tensor, got {type(t)}")
+    if t.numel() > 0 and t.device.type != "cuda":
+        raise ValueError("libsq takes device tensors; got a tensor on " + str(t.device))
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() > 0 else ctypes.c_void_p(t.data_ptr() or None)
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return SQ_BF16
+    if t.dtype == torch.float32:
+        return SQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    if device is None or device.type != "cuda":
+        return ctypes.c_void_p(None)
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _rows(t):
+    """(rows, cols, row stride) of a 2-D tensor whose last axis is contiguous."""
+    if t.dim() != 2:
+        raise ValueError(f"expected a 2-D tensor, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("the last axis must be contiguous")
+    return t.shape[0], t.shape[1], (t.stride(0) if t.shape[0] > 1 else t.shape[1])
+
+
+def _dense(t, name, shape, dtype):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise SqError(rc, sq_last_error())
+
+
+def _dev(*ts):
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            return t.device
+    return None
+
+
+# ---- the five entry points ---------------------------------------------------------
+
+def sq_calib_absmax(x: torch.Tensor, amax: torch.Tensor, stream=None) -> None:
+    """amax[j] = max(amax[j], max_t |x[t, j]|) for x [T, K] (bf16 or fp32)."""
+    T, K, ld = _rows(x)
+    _dense(amax, "amax", (K,), torch.float32)
+    _check(lib().sq_calib_absmax(_ptr(x), _dtype(x), T, K, ld, _ptr(amax), _stream(_dev(x, amax), stream)))
+
+
+def sq_smooth_factors(amax_x: torch.Tensor, w: torch.Tensor | None, alpha: float, s: torch.Tensor,
+                      inv_s: torch.Tensor, amax_w: torch.Tensor | None = None, stream=None) -> None:
+    """s, inv_s [K] from amax_x [K] and W [K, N] (or a precomputed amax_w when w is None)."""
+    K = amax_x.shape[0]
+    _dense(amax_x, "amax_x", (K,), torch.float32)
+    _dense(s, "s", (K,), torch.float32)
+    _dense(inv_s, "inv_s", (K,), torch.float32)
+    if amax_w is not None:
+        _dense(amax_w, "amax_w", (K,), torch.float32)
+    if w is not None:
+        Kw, N, ld = _rows(w)
+        if Kw != K:
+            raise ValueError(f"w has {Kw} rows, amax_x has {K} entries")
+        wt = _dtype(w)
+    else:
+        N, ld, wt = 0, 0, SQ_BF16
+    _check(lib().sq_smooth_factors(_ptr(amax_x), _ptr(w), wt, K, N, ld, ctypes.c_float(alpha), _ptr(s),
+                                   _ptr(inv_s), _ptr(amax_w), _stream(_dev(amax_x), stream)))
+
+
+def sq_quant_weight(w: torch.Tensor, s: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor,
+                    ws: torch.Tensor | None, stream=None) -> None:
+    """wq [N, K] int8 and w_scale [N] from W [K, N] smoothed by s [K] (None: unsmoothed)."""
+    K, N, ld = _rows(w)
+    _dense(wq, "wq", (N, K), torch.int8)
+    _dense(w_scale, "w_scale", (N,), torch.float32)
+    if s is not None:
+        _dense(s, "s", (K,), torch.float32)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sq_quant_weight(_ptr(w), _dtype(w), K, N, ld, _ptr(s), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
+                                 _stream(_dev(w), stream)))
+
+
+def sq_quant_act(x: torch.Tensor, inv_s: torch.Tensor | None, gran: int, xq: torch.Tensor,
+                 x_scale: torch.Tensor, ws: torch.Tensor | None = None, stream=None) -> None:
+    """xq [M, K] int8 and x_scale ([M] per token, [1] per tensor) from X [M, K] smoothed by inv_s."""
+    M, K, ld = _rows(x)
+    _dense(xq, "xq", (M, K), torch.int8)
+    _dense(x_scale, "x_scale", (1,) if gran == SQ_PER_TENSOR else (M,), torch.float32)
+    if inv_s is not None:
+        _dense(inv_s, "inv_s", (K,), torch.float32)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sq_quant_act(_ptr(x), _dtype(x), M, K, ld, _ptr(inv_s), int(gran), _ptr(xq), _ptr(x_scale),
+                              _ptr(ws), nbytes, _stream(_dev(x), stream)))
+
+
+def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, gran: int, wq: torch.Tensor, w_scale: torch.Tensor,
+                 y: torch.Tensor, acc_out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                 stream=None) -> None:
+    """y [M, N] (bf16 or fp32) = dequant(Xq [M, K] . Wq [N, K]^T); acc_out [M, N] int32 optional."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    _dense(xq, "xq", (M, K), torch.int8)
+    _dense(wq, "wq", (N, K), torch.int8)
+    _dense(x_scale, "x_scale", (1,) if gran == SQ_PER_TENSOR else (M,), torch.float32)
+    _dense(w_scale, "w_scale", (N,), torch.float32)
+    if y.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("y must be bfloat16 or float32")
+    _dense(y, "y", (M, N), y.dtype)
+    if acc_out is not None:
+        _dense(acc_out, "acc_out", (M, N), torch.int32)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), int(gran), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y),
+                              _dtype(y), _ptr(acc_out), _ptr(ws), nbytes, _stream(_dev(xq), stream)))

@@ -1,0 +1,228 @@
+// C ABI of the SmoothQuant W8A8 library: argument validation, workspace
+// sizing and kernel dispatch.  Nothing here allocates device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "sq.h"
+#include "sq_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sq_status fail(sq_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sq_status ok() {
+    g_last_error.clear();
+    return SQ_OK;
+}
+
+sq_status hip_result(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SQ_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(sq_dtype t) { return t == SQ_BF16 ? 2 : 4; }
+
+bool dtype_ok(sq_dtype t) { return t == SQ_BF16 || t == SQ_F32; }
+
+constexpr int64_t kMaxK = 131072;          // keeps |acc| <= K * 127^2 < 2^31
+constexpr int64_t kMaxMN = (int64_t)1 << 30;
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Shared checks of a [rows, cols] input with row stride ld.
+sq_status check_matrix(const char* fn, const char* name, const void* p, sq_dtype t, int64_t rows, int64_t cols,
+                       int64_t ld) {
+    if (!dtype_ok(t)) return fail(SQ_ERR_UNSUPPORTED, "%s: %s dtype %d is not SQ_BF16 or SQ_F32", fn, name, (int)t);
+    if (rows < 0 || cols < 0) return fail(SQ_ERR_INVALID_ARG, "%s: %s has negative size", fn, name);
+    if (ld < cols) return fail(SQ_ERR_INVALID_ARG, "%s: %s row stride %lld < row length %lld", fn, name,
+                               (long long)ld, (long long)cols);
+    if (rows > 0 && cols > 0) {
+        if (!p) return fail(SQ_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+        if (!aligned16(p)) return fail(SQ_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);
+        if ((ld * (int64_t)elem_size(t)) % 16 != 0)
+            return fail(SQ_ERR_INVALID_ARG, "%s: %s row stride %lld elements is not a multiple of 16 bytes", fn,
+                        name, (long long)ld);
+    }
+    return SQ_OK;
+}
+
+sq_status check_k(const char* fn, int64_t K) {
+    if (K < 0 || K % 16 != 0 || K > kMaxK)
+        return fail(SQ_ERR_INVALID_ARG, "%s: K = %lld must be a multiple of 16 in [0, %lld]", fn, (long long)K,
+                    (long long)kMaxK);
+    return SQ_OK;
+}
+
+sq_status check_vec(const char* fn, const char* name, const void* p, int64_t n, bool need16 = false) {
+    if (n > 0 && !p) return fail(SQ_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+    if (n > 0 && need16 && !aligned16(p)) return fail(SQ_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);
+    if (n > 0 && (reinterpret_cast<uintptr_t>(p) & 3u))
+        return fail(SQ_ERR_INVALID_ARG, "%s: %s is not 4-byte aligned", fn, name);
+    return SQ_OK;
+}
+
+#define SQ_TRY(expr)                   \
+    do {                               \
+        sq_status _st = (expr);        \
+        if (_st != SQ_OK) return _st;  \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* sq_version(void) { return "0.1.0"; }
+
+const char* sq_last_error(void) { return g_last_error.c_str(); }
+
+const char* sq_status_str(sq_status s) {
+    switch (s) {
+        case SQ_OK: return "SQ_OK";
+        case SQ_ERR_INVALID_ARG: return "SQ_ERR_INVALID_ARG";
+        case SQ_ERR_UNSUPPORTED: return "SQ_ERR_UNSUPPORTED";
+        case SQ_ERR_WORKSPACE: return "SQ_ERR_WORKSPACE";
+        case SQ_ERR_HIP: return "SQ_ERR_HIP";
+    }
+    return "SQ_UNKNOWN_STATUS";
+}
+
+size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran g) {
+    (void)M;
+    (void)K;
+    switch (op) {
+        case SQ_OP_QUANT_WEIGHT: return N > 0 ? round256((size_t)N * sizeof(uint32_t)) : 0;
+        case SQ_OP_QUANT_ACT: return g == SQ_PER_TENSOR ? 256 : 0;
+        default: return 0;
+    }
+}
+
+sq_status sq_calib_absmax(const void* x, sq_dtype xt, int64_t T, int64_t K, int64_t ldx, float* amax,
+                          hipStream_t stream) {
+    const char* fn = "sq_calib_absmax";
+    SQ_TRY(check_k(fn, K));
+    SQ_TRY(check_matrix(fn, "x", x, xt, T, K, ldx));
+    SQ_TRY(check_vec(fn, "amax", amax, K));
+    if (T == 0 || K == 0) return ok();
+    return hip_result(sqk::launch_col_absmax(x, xt == SQ_BF16, T, K, ldx, nullptr,
+                                             reinterpret_cast<uint32_t*>(amax), stream), fn);
+}
+
+sq_status sq_smooth_factors(const float* amax_x, const void* w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
+                            float alpha, float* s, float* inv_s, float* amax_w, hipStream_t stream) {
+    const char* fn = "sq_smooth_factors";
+    SQ_TRY(check_k(fn, K));
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(SQ_ERR_INVALID_ARG, "%s: alpha = %g is not in [0, 1]", fn, alpha);
+    SQ_TRY(check_vec(fn, "amax_x", amax_x, K));
+    SQ_TRY(check_vec(fn, "s", s, K));
+    SQ_TRY(check_vec(fn, "inv_s", inv_s, K));
+    if (w) {
+        if (N <= 0) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld must be positive when w is given", fn, (long long)N);
+        SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw));
+        if (amax_w) SQ_TRY(check_vec(fn, "amax_w", amax_w, K));
+    } else {
+        if (!amax_w && K > 0) return fail(SQ_ERR_INVALID_ARG, "%s: need w or a precomputed amax_w", fn);
+        SQ_TRY(check_vec(fn, "amax_w", amax_w, K));
+    }
+    if (K == 0) return ok();
+    if (w)
+        return hip_result(sqk::launch_row_absmax_factors(w, wt == SQ_BF16, K, N, ldw, amax_x, alpha, s, inv_s,
+                                                         amax_w, stream), fn);
+    return hip_result(sqk::launch_factors(amax_x, amax_w, K, alpha, s, inv_s, stream), fn);
+}
+
+sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw, const float* s, int8_t* wq,
+                          float* w_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "sq_quant_weight";
+    SQ_TRY(check_k(fn, K));
+    if (N > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld too large", fn, (long long)N);
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw));
+    if (s) SQ_TRY(check_vec(fn, "s", s, K));
+    SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
+    if (K > 0 && N > 0) {
+        if (!wq) return fail(SQ_ERR_INVALID_ARG, "%s: wq is NULL", fn);
+        if (!aligned16(wq)) return fail(SQ_ERR_INVALID_ARG, "%s: wq is not 16-byte aligned", fn);
+    }
+    const size_t need = sq_workspace_size(SQ_OP_QUANT_WEIGHT, 0, N, K, SQ_PER_TOKEN);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (N == 0) return ok();
+    uint32_t* colmax = static_cast<uint32_t*>(ws);
+    if (K == 0)  // no input channels: every column max is 0, so every scale is 0
+        return hip_result(sqk::launch_fill_u32(reinterpret_cast<uint32_t*>(w_scale), N, 0u, stream), fn);
+    hipError_t e = sqk::launch_fill_u32(colmax, N, 0u, stream);
+    if (e == hipSuccess) e = sqk::launch_col_absmax(w, wt == SQ_BF16, K, N, ldw, s, colmax, stream);
+    if (e == hipSuccess) e = sqk::launch_quant_weight(w, wt == SQ_BF16, K, N, ldw, s, colmax, wq, w_scale, stream);
+    return hip_result(e, fn);
+}
+
+sq_status sq_quant_act(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const float* inv_s,
+                       sq_act_gran g, int8_t* xq, float* x_scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "sq_quant_act";
+    SQ_TRY(check_k(fn, K));
+    if (g != SQ_PER_TOKEN && g != SQ_PER_TENSOR) return fail(SQ_ERR_UNSUPPORTED, "%s: granularity %d", fn, (int)g);
+    if (M > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
+    SQ_TRY(check_matrix(fn, "x", x, xt, M, K, ldx));
+    if (inv_s) SQ_TRY(check_vec(fn, "inv_s", inv_s, K, true));
+    SQ_TRY(check_vec(fn, "x_scale", x_scale, g == SQ_PER_TENSOR ? (M > 0 ? 1 : 0) : M));
+    if (M > 0 && K > 0) {
+        if (!xq) return fail(SQ_ERR_INVALID_ARG, "%s: xq is NULL", fn);
+        if (!aligned16(xq)) return fail(SQ_ERR_INVALID_ARG, "%s: xq is not 16-byte aligned", fn);
+    }
+    const size_t need = sq_workspace_size(SQ_OP_QUANT_ACT, M, 0, K, g);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (M == 0) return ok();
+    const bool bf = xt == SQ_BF16;
+    if (g == SQ_PER_TOKEN)
+        return hip_result(sqk::launch_quant_act(x, bf, M, K, ldx, inv_s, 0, xq, x_scale, nullptr, stream), fn);
+    uint32_t* gmax = static_cast<uint32_t*>(ws);
+    hipError_t e = sqk::launch_fill_u32(gmax, 1, 0u, stream);
+    if (e == hipSuccess) e = sqk::launch_quant_act(x, bf, M, K, ldx, inv_s, 1, xq, x_scale, gmax, stream);
+    if (e == hipSuccess) e = sqk::launch_quant_act(x, bf, M, K, ldx, inv_s, 2, xq, x_scale, gmax, stream);
+    return hip_result(e, fn);
+}
+
+sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_gran g, const int8_t* wq, const float* w_scale,
+                       int64_t M, int64_t N, int64_t K, void* y, sq_dtype yt, int32_t* acc_out, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "sq_gemm_w8a8";
+    (void)ws;
+    (void)ws_bytes;
+    SQ_TRY(check_k(fn, K));
+    if (g != SQ_PER_TOKEN && g != SQ_PER_TENSOR) return fail(SQ_ERR_UNSUPPORTED, "%s: granularity %d", fn, (int)g);
+    if (!dtype_ok(yt)) return fail(SQ_ERR_UNSUPPORTED, "%s: output dtype %d", fn, (int)yt);
+    if (M < 0 || N < 0 || M > kMaxMN || N > kMaxMN)
+        return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld, N = %lld out of range", fn, (long long)M, (long long)N);
+    if (M == 0 || N == 0) return ok();
+    if (K > 0) {
+        if (!xq || !wq) return fail(SQ_ERR_INVALID_ARG, "%s: xq or wq is NULL", fn);
+        if (!aligned16(xq) || !aligned16(wq))
+            return fail(SQ_ERR_INVALID_ARG, "%s: xq and wq must be 16-byte aligned", fn);
+    }
+    SQ_TRY(check_vec(fn, "x_scale", x_scale, g == SQ_PER_TENSOR ? 1 : M));
+    SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
+    if (!y) return fail(SQ_ERR_INVALID_ARG, "%s: y is NULL", fn);
+    if (!aligned16(y)) return fail(SQ_ERR_INVALID_ARG, "%s: y is not 16-byte aligned", fn);
+    if (acc_out && !aligned16(acc_out)) return fail(SQ_ERR_INVALID_ARG, "%s: acc_out is not 16-byte aligned", fn);
+    return hip_result(sqk::launch_gemm_w8a8(xq, x_scale, g == SQ_PER_TENSOR, wq, w_scale, M, N, K, y, yt == SQ_BF16,
+                                            acc_out, stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device-side helpers shared by the gfx950 kernels of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sqk {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// Element types the kernels read.  A bf16 value is carried as its 16-bit
+// pattern; widening to fp32 places it in the upper half (exact).
+struct bf16_t {
+    uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<bf16_t> {
+    static constexpr int kPerVec = 8;  // elements per 16-byte load
+};
+
+template <>
+struct Elem<float> {
+    static constexpr int kPerVec = 4;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// 16-byte global load (one global_load_dwordx4).
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Widen the 8 consecutive elements at p (16-byte aligned) to fp32.
+__device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
+    uint4 q = ld16(p);
+    v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
+    v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
+    v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
+    v[6] = bf16_lo(q.w); v[7] = bf16_hi(q.w);
+}
+
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    uint4 a = ld16(p), b = ld16(p + 4);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+    v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+    v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+}
+
+// Bounds-checked variant for the ragged end of a row: elements at or beyond
+// `n` (counted from p) read as 0.
+template <typename T>
+__device__ __forceinline__ void load8_tail(const T* p, int64_t n, float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i < n) {
+            if constexpr (sizeof(T) == 2) {
+                v[i] = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+            } else {
+                v[i] = reinterpret_cast<const float*>(p)[i];
+            }
+        } else {
+            v[i] = 0.0f;
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void load8_any(const T* p, int64_t n, float (&v)[8]) {
+    if (n >= 8) load8(p, v);
+    else load8_tail(p, n, v);
+}
+
+// Max over the wavefront (all 64 lanes end with the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Symmetric INT8 code of v with multiplier r: clamp(rne(fl(v*r)), -127, 127).
+// If the group max is so small that r = 127/max overflowed to +inf, a zero
+// element gives 0 * inf = NaN, which codes to 0 (non-zero ones clamp).
+__device__ __forceinline__ int code8(float v, float r) {
+    float t = __builtin_rintf(v * r);
+    t = (t == t) ? t : 0.0f;
+    t = fminf(fmaxf(t, -127.0f), 127.0f);
+    return static_cast<int>(t);
+}
+
+// Pack four codes (low byte first) into one dword.
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
+           (uint32_t(d) << 24);
+}
+
+// Scale and multiplier of a group with max magnitude m (m >= 0):
+// scale = fl(m / 127), r = fl(127 / m), r = 0 when m = 0.  Both are
+// correctly rounded fp32 divisions.
+__device__ __forceinline__ void group_scale(float m, float& scale, float& r) {
+    scale = m / 127.0f;
+    r = m > 0.0f ? 127.0f / m : 0.0f;
+}
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    bf2 r;
+    r.x = static_cast<__bf16>(lo);
+    r.y = static_cast<__bf16>(hi);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+}  // namespace sqk

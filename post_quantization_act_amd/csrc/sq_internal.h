@@ -1,0 +1,40 @@
+// Internal launchers of the gfx950 kernels (host side).  Each returns the
+// HIP error of its launch; argument validation happens in the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sqk {
+
+hipError_t launch_fill_u32(uint32_t* out, int64_t n, uint32_t v, hipStream_t st);
+
+// out[c] = max(out[c], max_r |row_scale[r] * x[r, c]|) as fp32 bit patterns.
+hipError_t launch_col_absmax(const void* x, bool bf16, int64_t rows, int64_t cols, int64_t ld,
+                             const float* row_scale, uint32_t* out, hipStream_t st);
+
+// amax_w[j] = max_k |w[j, k]| (optional output), then s[j], inv_s[j].
+hipError_t launch_row_absmax_factors(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld,
+                                     const float* amax_x, float alpha, float* s, float* inv_s, float* amax_w,
+                                     hipStream_t st);
+
+hipError_t launch_factors(const float* amax_x, const float* amax_w, int64_t K, float alpha, float* s,
+                          float* inv_s, hipStream_t st);
+
+// Codes of diag(s) W per output column from the column maxima colmax (fp32
+// bits), written transposed to wq[N, K]; w_scale[N].
+hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
+                               const uint32_t* colmax, int8_t* wq, float* w_scale, hipStream_t st);
+
+// Activation quantization.  mode 0: per token.  mode 1: max of |x * inv_s|
+// over the tensor into *gmax (no codes).  mode 2: codes with the scale from
+// *gmax (x_scale[0]).
+hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, const float* inv_s,
+                            int mode, int8_t* xq, float* x_scale, uint32_t* gmax, hipStream_t st);
+
+// INT8 GEMM + dequant epilogue.
+hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                            const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16,
+                            int32_t* acc_out, hipStream_t st);
+
+}  // namespace sqk

@@ -1,0 +1,305 @@
+// Quantization kernels of the SmoothQuant path on gfx950:
+//  - smoothed weights to per-output-channel INT8, transposed to [N, K];
+//  - smoothed activations to per-token (or per-tensor) INT8.
+// Both are HBM-bound: read the bf16/fp32 source once, write one byte per
+// element.
+#include "sq_device.h"
+#include "sq_internal.h"
+
+namespace sqk {
+
+// ---- weights -----------------------------------------------------------------
+//
+// Tile of 128 input channels (j) x 128 output channels (k) per block of 256
+// threads.  Thread (rg, cg) reads an 8 x 8 sub-block: 8 rows j, 8 consecutive
+// k (one 16-byte load per row for bf16).  A wavefront holds 8 row groups x 8
+// column groups, so each load instruction reads 8 full 128-byte lines.
+// Codes are transposed through LDS: the thread writes, for each of its 8
+// columns, the 8 codes along j as one 8-byte word; rows of the LDS tile are
+// padded to 136 bytes so a wavefront's 8-byte writes spread over all banks.
+// The tile then leaves as 16-byte stores of 16 consecutive j of one output
+// channel (wq is [N, K], K contiguous).
+constexpr int kQwTile = 128;
+constexpr int kQwStride = kQwTile + 8;
+
+template <typename T, bool kScaled>
+__global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t K, int64_t N, int64_t ld,
+                                                      const float* __restrict__ s,
+                                                      const uint32_t* __restrict__ colmax,
+                                                      int8_t* __restrict__ wq, float* __restrict__ w_scale) {
+    __shared__ float r_s[kQwTile];
+    __shared__ __align__(16) uint8_t tile[kQwTile * kQwStride];
+
+    const int64_t k0 = (int64_t)blockIdx.x * kQwTile;
+    const int64_t j0 = (int64_t)blockIdx.y * kQwTile;
+    const int t = threadIdx.x;
+    if (t < kQwTile) {
+        const int64_t k = k0 + t;
+        float scale = 0.0f, r = 0.0f;
+        if (k < N) {
+            group_scale(__uint_as_float(colmax[k]), scale, r);
+            if (blockIdx.y == 0) w_scale[k] = scale;
+        }
+        r_s[t] = r;
+    }
+    __syncthreads();
+
+    const int wave = t / kWave, lane = t % kWave;
+    const int cg = (lane % 8) + 8 * (wave % 2);
+    const int rg = (lane / 8) + 8 * (wave / 2);
+    const int64_t kc = k0 + cg * 8;
+    const int64_t ncol = N - kc;
+
+    uint32_t lo[8], hi[8];  // per column cc: codes of rows 0..3 (lo) and 4..7 (hi)
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) lo[cc] = hi[cc] = 0u;
+
+    if (ncol > 0) {
+        float v[8][8];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int64_t j = j0 + rg * 8 + rr;
+            if (j < K) {
+                load8_any(w + j * ld + kc, ncol, v[rr]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[rr][i] = 0.0f;
+            }
+        }
+        float rr_[8];
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) rr_[cc] = r_s[cg * 8 + cc];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int64_t j = j0 + rg * 8 + rr;
+            const float sj = (kScaled && j < K) ? s[j] : 1.0f;
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                const float wp = kScaled ? sj * v[rr][cc] : v[rr][cc];
+                const uint32_t c = uint32_t(code8(wp, rr_[cc])) & 0xFFu;
+                if (rr < 4) lo[cc] |= c << (8 * rr);
+                else hi[cc] |= c << (8 * (rr - 4));
+            }
+        }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+        uint2 word = make_uint2(lo[cc], hi[cc]);
+        *reinterpret_cast<uint2*>(tile + (cg * 8 + cc) * kQwStride + rg * 8) = word;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = t + q * 256;  // 1024 chunks of 16 bytes
+        const int kl = c / 8, jc = c % 8;
+        const int64_t k = k0 + kl;
+        const int64_t j = j0 + jc * 16;
+        if (k < N && j < K) {
+            const uint8_t* src = tile + kl * kQwStride + jc * 16;
+            uint2 a = *reinterpret_cast<const uint2*>(src);
+            uint2 b = *reinterpret_cast<const uint2*>(src + 8);
+            *reinterpret_cast<uint4*>(wq + k * K + j) = make_uint4(a.x, a.y, b.x, b.y);
+        }
+    }
+}
+
+// ---- activations -------------------------------------------------------------
+//
+// WPR wavefronts per token row (1 or 4); blocks of 256 threads hold 4 / WPR
+// rows.  The row is kept in registers: a thread owns NV groups of 8
+// consecutive channels (16-byte loads for bf16), smooths them with inv_s,
+// reduces max|x'| across the wavefront with shuffles (and across the row's
+// wavefronts through LDS), then codes and stores 8 bytes per group.
+template <typename T, int NV, int WPR>
+__global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int64_t M, int64_t K, int64_t ld,
+                                                   const float* __restrict__ inv_s, int mode,
+                                                   int8_t* __restrict__ xq, float* __restrict__ x_scale,
+                                                   uint32_t* __restrict__ gmax) {
+    constexpr int kRowsPerBlock = 4 / WPR;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int row_in_block = wave / WPR;
+    const int t = (wave % WPR) * kWave + lane;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + row_in_block;
+    const bool valid = row < M;
+    const int64_t groups = K / 8;
+
+    float v[NV][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t g = t + (int64_t)q * (WPR * kWave);
+        if (valid && g < groups) {
+            load8(x + row * ld + g * 8, v[q]);
+            if (inv_s) {
+                const float4 a = *reinterpret_cast<const float4*>(inv_s + g * 8);
+                const float4 b = *reinterpret_cast<const float4*>(inv_s + g * 8 + 4);
+                v[q][0] = v[q][0] * a.x; v[q][1] = v[q][1] * a.y;
+                v[q][2] = v[q][2] * a.z; v[q][3] = v[q][3] * a.w;
+                v[q][4] = v[q][4] * b.x; v[q][5] = v[q][5] * b.y;
+                v[q][6] = v[q][6] * b.z; v[q][7] = v[q][7] * b.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[q][i]));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[q][i] = 0.0f;
+        }
+    }
+
+    __shared__ float red[4];
+    if (mode == 1) {
+        // Tensor-wide maximum: one atomic per block.
+        m = wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+            if (bm > 0.0f) atomicMax(gmax, __float_as_uint(bm));
+        }
+        return;
+    }
+
+    float a;
+    if (mode == 2) {
+        a = __uint_as_float(*gmax);
+    } else {
+        m = wave_max(m);
+        if constexpr (WPR > 1) {
+            if (lane == 0) red[wave] = m;
+            __syncthreads();
+            const int w0 = row_in_block * WPR;
+            m = red[w0];
+#pragma unroll
+            for (int i = 1; i < WPR; ++i) m = fmaxf(m, red[w0 + i]);
+        }
+        a = m;
+    }
+    float scale, r;
+    group_scale(a, scale, r);
+    if (mode == 0) {
+        if (valid && t == 0) x_scale[row] = scale;
+    } else if (blockIdx.x == 0 && threadIdx.x == 0) {
+        x_scale[0] = scale;
+    }
+    if (!valid) return;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t g = t + (int64_t)q * (WPR * kWave);
+        if (g < groups) {
+            uint2 word;
+            word.x = pack4(code8(v[q][0], r), code8(v[q][1], r), code8(v[q][2], r), code8(v[q][3], r));
+            word.y = pack4(code8(v[q][4], r), code8(v[q][5], r), code8(v[q][6], r), code8(v[q][7], r));
+            *reinterpret_cast<uint2*>(xq + row * K + g * 8) = word;
+        }
+    }
+}
+
+// Rows longer than the register-resident variants hold (K > 16384): four
+// wavefronts per row loop over it twice, once for the max, once for codes
+// (the second pass re-reads the row, mostly from L2).
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_act_long(const T* __restrict__ x, int64_t M, int64_t K,
+                                                        int64_t ld, const float* __restrict__ inv_s, int mode,
+                                                        int8_t* __restrict__ xq, float* __restrict__ x_scale,
+                                                        uint32_t* __restrict__ gmax) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int64_t row = blockIdx.x;
+    const int64_t groups = K / 8;
+    const T* xr = x + row * ld;
+    __shared__ float red[4];
+    float m = 0.0f;
+    if (mode != 2) {
+        for (int64_t g = threadIdx.x; g < groups; g += 256) {
+            float v[8];
+            load8(xr + g * 8, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(inv_s ? v[i] * inv_s[g * 8 + i] : v[i]));
+        }
+        m = wave_max(m);
+        if (lane == 0) red[wave] = m;
+        __syncthreads();
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if (mode == 1) {
+            if (threadIdx.x == 0 && m > 0.0f) atomicMax(gmax, __float_as_uint(m));
+            return;
+        }
+    }
+    const float a = mode == 2 ? __uint_as_float(*gmax) : m;
+    float scale, r;
+    group_scale(a, scale, r);
+    if (threadIdx.x == 0) {
+        if (mode == 0) x_scale[row] = scale;
+        else if (row == 0) x_scale[0] = scale;
+    }
+    for (int64_t g = threadIdx.x; g < groups; g += 256) {
+        float v[8];
+        load8(xr + g * 8, v);
+        if (inv_s) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = v[i] * inv_s[g * 8 + i];
+        }
+        uint2 word;
+        word.x = pack4(code8(v[0], r), code8(v[1], r), code8(v[2], r), code8(v[3], r));
+        word.y = pack4(code8(v[4], r), code8(v[5], r), code8(v[6], r), code8(v[7], r));
+        *reinterpret_cast<uint2*>(xq + row * K + g * 8) = word;
+    }
+}
+
+// ---- launchers -----------------------------------------------------------------
+
+hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
+                               const uint32_t* colmax, int8_t* wq, float* w_scale, hipStream_t st) {
+    if (K <= 0 || N <= 0) return hipSuccess;
+    dim3 grid((unsigned)((N + kQwTile - 1) / kQwTile), (unsigned)((K + kQwTile - 1) / kQwTile));
+    if (bf16) {
+        const bf16_t* p = static_cast<const bf16_t*>(w);
+        if (s)
+            hipLaunchKernelGGL((k_quant_weight<bf16_t, true>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
+        else
+            hipLaunchKernelGGL((k_quant_weight<bf16_t, false>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
+    } else {
+        const float* p = static_cast<const float*>(w);
+        if (s)
+            hipLaunchKernelGGL((k_quant_weight<float, true>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
+        else
+            hipLaunchKernelGGL((k_quant_weight<float, false>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int NV, int WPR>
+static void launch_act_rows(const T* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode, int8_t* xq,
+                            float* x_scale, uint32_t* gmax, hipStream_t st) {
+    constexpr int rpb = 4 / WPR;
+    const int64_t blocks = (M + rpb - 1) / rpb;
+    hipLaunchKernelGGL((k_quant_act<T, NV, WPR>), dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ld, inv_s,
+                       mode, xq, x_scale, gmax);
+}
+
+template <typename T>
+static void dispatch_act(const T* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode, int8_t* xq,
+                         float* x_scale, uint32_t* gmax, hipStream_t st) {
+    const int64_t groups = K / 8;
+    if (groups <= 1 * kWave) return launch_act_rows<T, 1, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    if (groups <= 2 * kWave) return launch_act_rows<T, 2, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    if (groups <= 4 * kWave) return launch_act_rows<T, 4, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    if (groups <= 8 * kWave) return launch_act_rows<T, 8, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    if (groups <= 4 * 4 * kWave) return launch_act_rows<T, 4, 4>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    if (groups <= 6 * 4 * kWave) return launch_act_rows<T, 6, 4>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    if (groups <= 8 * 4 * kWave) return launch_act_rows<T, 8, 4>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    hipLaunchKernelGGL((k_quant_act_long<T>), dim3((unsigned)M), dim3(256), 0, st, x, M, K, ld, inv_s, mode, xq,
+                       x_scale, gmax);
+}
+
+hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, const float* inv_s,
+                            int mode, int8_t* xq, float* x_scale, uint32_t* gmax, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    if (bf16)
+        dispatch_act(static_cast<const bf16_t*>(x), M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    else
+        dispatch_act(static_cast<const float*>(x), M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    return hipGetLastError();
+}
+
+}  // namespace sqk

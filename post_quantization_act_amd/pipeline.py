@@ -1,0 +1,80 @@
+"""The five calls in order, over device buffers allocated once.
+
+This is orchestration only: it allocates output tensors with torch and calls
+the C entry points; every step of the computation runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR, sq_calib_absmax, sq_gemm_w8a8, sq_quant_act,
+               sq_quant_weight, sq_smooth_factors, sq_workspace_size)
+
+
+@dataclass
+class W8A8Buffers:
+    amax_x: torch.Tensor
+    amax_w: torch.Tensor
+    s: torch.Tensor
+    inv_s: torch.Tensor
+    wq: torch.Tensor
+    w_scale: torch.Tensor
+    xq: torch.Tensor
+    x_scale: torch.Tensor
+    y: torch.Tensor
+    acc: torch.Tensor | None
+    ws_w: torch.Tensor | None
+    ws_a: torch.Tensor | None
+
+    @classmethod
+    def allocate(cls, M: int, N: int, K: int, gran: int, device, y_dtype=torch.bfloat16, with_acc=False):
+        f32 = dict(dtype=torch.float32, device=device)
+
+        def ws(nbytes):
+            return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device) if nbytes else None
+
+        return cls(
+            amax_x=torch.zeros(K, **f32), amax_w=torch.empty(K, **f32), s=torch.empty(K, **f32),
+            inv_s=torch.empty(K, **f32), wq=torch.empty(N, K, dtype=torch.int8, device=device),
+            w_scale=torch.empty(N, **f32), xq=torch.empty(M, K, dtype=torch.int8, device=device),
+            x_scale=torch.empty(1 if gran == SQ_PER_TENSOR else M, **f32),
+            y=torch.empty(M, N, dtype=y_dtype, device=device),
+            acc=torch.empty(M, N, dtype=torch.int32, device=device) if with_acc else None,
+            ws_w=ws(sq_workspace_size(SQ_OP_QUANT_WEIGHT, M, N, K, gran)),
+            ws_a=ws(sq_workspace_size(SQ_OP_QUANT_ACT, M, N, K, gran)),
+        )
+
+
+def calibrate(calib, amax_x: torch.Tensor, reset: bool = True, stream=None) -> None:
+    """Step 1 over one [T, K] tensor or a sequence of chunks."""
+    if reset:
+        amax_x.zero_()
+    chunks = calib if isinstance(calib, (list, tuple)) else [calib]
+    for c in chunks:
+        sq_calib_absmax(c, amax_x, stream=stream)
+
+
+def prepare_weights(w: torch.Tensor, alpha: float | None, b: W8A8Buffers, stream=None) -> None:
+    """Steps 2-3 (alpha=None: unsmoothed weights)."""
+    if alpha is None:
+        sq_quant_weight(w, None, b.wq, b.w_scale, b.ws_w, stream=stream)
+        return
+    sq_smooth_factors(b.amax_x, w, alpha, b.s, b.inv_s, b.amax_w, stream=stream)
+    sq_quant_weight(w, b.s, b.wq, b.w_scale, b.ws_w, stream=stream)
+
+
+def forward(x: torch.Tensor, gran: int, b: W8A8Buffers, smoothed: bool = True, stream=None) -> torch.Tensor:
+    """Steps 4-5 on activations x [M, K]."""
+    sq_quant_act(x, b.inv_s if smoothed else None, gran, b.xq, b.x_scale, b.ws_a, stream=stream)
+    sq_gemm_w8a8(b.xq, b.x_scale, gran, b.wq, b.w_scale, b.y, b.acc, stream=stream)
+    return b.y
+
+
+def smoothquant_w8a8(x, w, calib, alpha: float | None, gran: int, b: W8A8Buffers, stream=None) -> torch.Tensor:
+    """All five steps.  alpha=None runs the unsmoothed W8A8 baseline (no calibration)."""
+    if alpha is not None:
+        calibrate(calib, b.amax_x, stream=stream)
+    prepare_weights(w, alpha, b, stream=stream)
+    return forward(x, gran, b, smoothed=alpha is not None, stream=stream)

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments before it
+enqueues anything.  No call here reaches a kernel launch: each one carries an
+argument that validation refuses (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import post_quantization_act_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "sq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(sq_[a-z0-9_]+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = sq.lib()
+    declared = _declared_symbols()
+    assert set(declared) >= {"sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
+                             "sq_gemm_w8a8", "sq_workspace_size", "sq_status_str", "sq_last_error"}
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(sq.EXPORTED_SYMBOLS)
+
+
+def test_library_is_gfx950_code():
+    out = open(sq.lib_path(), "rb").read()
+    assert b"gfx950" in out
+    assert b"gfx942" not in out and b"sm_" not in out[:0]
+
+
+def test_status_strings_and_version():
+    assert sq.sq_status_str(0) == "SQ_OK"
+    assert sq.sq_status_str(-1) == "SQ_ERR_INVALID_ARG"
+    assert sq.sq_status_str(-3) == "SQ_ERR_WORKSPACE"
+    assert re.match(r"^\d+\.\d+\.\d+$", sq.sq_version())
+
+
+def test_workspace_sizes():
+    assert sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, 4096, 4096) >= 4096 * 4
+    assert sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, 0, 4096) == 0
+    assert sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, 2048, 0, 4096, sq.SQ_PER_TOKEN) == 0
+    assert sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, 2048, 0, 4096, sq.SQ_PER_TENSOR) >= 4
+    assert sq.sq_workspace_size(sq.SQ_OP_CALIB_ABSMAX, 1, 1, 16) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def _L():
+    return sq.lib()
+
+
+def _expect(rc, status, pattern):
+    assert rc == status, (rc, sq.sq_last_error())
+    assert re.search(pattern, sq.sq_last_error()), sq.sq_last_error()
+
+
+def test_calib_rejects_bad_k_and_null():
+    L = _L()
+    _expect(L.sq_calib_absmax(FAKE, sq.SQ_BF16, 8, 20, 20, FAKE, None), -1, "multiple of 16")
+    _expect(L.sq_calib_absmax(None, sq.SQ_BF16, 8, 32, 32, FAKE, None), -1, "x is NULL")
+    _expect(L.sq_calib_absmax(FAKE, sq.SQ_BF16, 8, 32, 16, FAKE, None), -1, "row stride")
+    _expect(L.sq_calib_absmax(MISALIGNED, sq.SQ_BF16, 8, 32, 32, FAKE, None), -1, "aligned")
+    _expect(L.sq_calib_absmax(FAKE, sq.SQ_BF16, 8, 32, 36, FAKE, None), -1, "multiple of 16 bytes")
+    _expect(L.sq_calib_absmax(FAKE, 7, 8, 32, 32, FAKE, None), -2, "dtype")
+    _expect(L.sq_calib_absmax(FAKE, sq.SQ_BF16, 8, 32, 32, None, None), -1, "amax is NULL")
+    _expect(L.sq_calib_absmax(FAKE, sq.SQ_BF16, -1, 32, 32, FAKE, None), -1, "negative")
+
+
+def test_empty_calls_succeed_without_work():
+    L = _L()
+    assert L.sq_calib_absmax(None, sq.SQ_BF16, 0, 32, 32, FAKE, None) == 0
+    assert L.sq_gemm_w8a8(None, None, 0, None, None, 0, 16, 32, None, sq.SQ_BF16, None, None, 0, None) == 0
+    assert sq.sq_last_error() == ""
+
+
+def test_smooth_factors_rejects():
+    L = _L()
+    f = ctypes.c_float
+    _expect(L.sq_smooth_factors(FAKE, FAKE, sq.SQ_BF16, 32, 16, 16, f(1.5), FAKE, FAKE, None, None), -1, "alpha")
+    _expect(L.sq_smooth_factors(FAKE, FAKE, sq.SQ_BF16, 32, 16, 16, f(float("nan")), FAKE, FAKE, None, None), -1,
+            "alpha")
+    _expect(L.sq_smooth_factors(FAKE, None, sq.SQ_BF16, 32, 16, 16, f(0.5), FAKE, FAKE, None, None), -1,
+            "precomputed amax_w")
+    _expect(L.sq_smooth_factors(FAKE, FAKE, sq.SQ_BF16, 32, 0, 16, f(0.5), FAKE, FAKE, None, None), -1,
+            "N = 0")
+    _expect(L.sq_smooth_factors(FAKE, FAKE, sq.SQ_BF16, 32, 16, 16, f(0.5), None, FAKE, None, None), -1,
+            "s is NULL")
+
+
+def test_quant_weight_rejects():
+    L = _L()
+    _expect(L.sq_quant_weight(FAKE, sq.SQ_BF16, 32, 64, 64, FAKE, FAKE, FAKE, None, 0, None), -3, "workspace")
+    _expect(L.sq_quant_weight(FAKE, sq.SQ_BF16, 32, 64, 64, FAKE, FAKE, FAKE, FAKE, 16, None), -3, "workspace")
+    _expect(L.sq_quant_weight(FAKE, sq.SQ_BF16, 32, 64, 64, FAKE, MISALIGNED, FAKE, FAKE, 4096, None), -1, "wq")
+    _expect(L.sq_quant_weight(FAKE, sq.SQ_BF16, 33, 64, 64, FAKE, FAKE, FAKE, FAKE, 4096, None), -1, "K = 33")
+
+
+def test_quant_act_rejects():
+    L = _L()
+    _expect(L.sq_quant_act(FAKE, sq.SQ_BF16, 4, 32, 32, FAKE, 5, FAKE, FAKE, None, 0, None), -2, "granularity")
+    _expect(L.sq_quant_act(FAKE, sq.SQ_BF16, 4, 32, 32, FAKE, sq.SQ_PER_TENSOR, FAKE, FAKE, None, 0, None), -3,
+            "workspace")
+    _expect(L.sq_quant_act(FAKE, sq.SQ_BF16, 4, 32, 32, MISALIGNED, sq.SQ_PER_TOKEN, FAKE, FAKE, None, 0, None),
+            -1, "inv_s")
+    _expect(L.sq_quant_act(FAKE, sq.SQ_BF16, 4, 32, 32, FAKE, sq.SQ_PER_TOKEN, None, FAKE, None, 0, None), -1,
+            "xq is NULL")
+
+
+def test_gemm_rejects():
+    L = _L()
+    _expect(L.sq_gemm_w8a8(FAKE, FAKE, 0, FAKE, FAKE, 4, 4, 24, FAKE, sq.SQ_BF16, None, None, 0, None), -1,
+            "multiple of 16")
+    _expect(L.sq_gemm_w8a8(FAKE, FAKE, 0, FAKE, FAKE, 4, 4, 16 * 8193 + 16 * 8192, FAKE, sq.SQ_BF16, None, None, 0,
+                           None), -1, "multiple of 16|131072")
+    _expect(L.sq_gemm_w8a8(MISALIGNED, FAKE, 0, FAKE, FAKE, 4, 4, 32, FAKE, sq.SQ_BF16, None, None, 0, None), -1,
+            "aligned")
+    _expect(L.sq_gemm_w8a8(FAKE, FAKE, 0, FAKE, FAKE, 4, 4, 32, None, sq.SQ_BF16, None, None, 0, None), -1,
+            "y is NULL")
+    _expect(L.sq_gemm_w8a8(FAKE, FAKE, 0, FAKE, FAKE, 4, 4, 32, FAKE, 9, None, None, 0, None), -2, "output dtype")
+    _expect(L.sq_gemm_w8a8(FAKE, FAKE, 3, FAKE, FAKE, 4, 4, 32, FAKE, sq.SQ_BF16, None, None, 0, None), -2,
+            "granularity")
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 32, dtype=torch.bfloat16)
+    amax = torch.zeros(32)
+    with pytest.raises(ValueError, match="device tensors"):
+        sq.sq_calib_absmax(x, amax)

@@ -1,0 +1,253 @@
+"""GPU parity: every output of the HIP path equals the CPU oracle's, bit for
+bit, on the same seeded inputs (codes, scales, factors, int32 accumulators,
+fp32 and bf16 outputs).  Shapes span several tiles of every kernel and end in
+ragged tails; edge cases cover empty inputs, all-zero rows, alpha = 0 and 1,
+fp32 and bf16 inputs, per-token and per-tensor scales, K beyond the
+register-resident activation path, and every finite bf16 bit pattern."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import post_quantization_act_amd as sq
+import synth
+from post_quantization_act_amd import pipeline
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np(t):
+    return synth.to_numpy(t)
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _run_gpu(x, w, calib, alpha, gran, y_dtype=torch.bfloat16, with_acc=True):
+    M, K = x.shape
+    N = w.shape[1]
+    b = pipeline.W8A8Buffers.allocate(M, N, K, gran, DEV, y_dtype=y_dtype, with_acc=with_acc)
+    pipeline.smoothquant_w8a8(x, w, calib, alpha, gran, b)
+    torch.cuda.synchronize()
+    return b
+
+
+def _compare(b, o, alpha, y_dtype):
+    if alpha is not None:
+        np.testing.assert_array_equal(_np(b.amax_x), o["amax_x"], err_msg="amax_x")
+        np.testing.assert_array_equal(_np(b.amax_w), o["amax_w"], err_msg="amax_w")
+        np.testing.assert_array_equal(_np(b.s), o["s"], err_msg="s")
+        np.testing.assert_array_equal(_np(b.inv_s), o["inv_s"], err_msg="inv_s")
+    np.testing.assert_array_equal(_np(b.w_scale), o["w_scale"], err_msg="w_scale")
+    np.testing.assert_array_equal(_np(b.wq), o["wq"], err_msg="wq")
+    np.testing.assert_array_equal(_np(b.x_scale), o["x_scale"], err_msg="x_scale")
+    np.testing.assert_array_equal(_np(b.xq), o["xq"], err_msg="xq")
+    if b.acc is not None:
+        np.testing.assert_array_equal(_np(b.acc), o["acc"], err_msg="acc")
+    if y_dtype == torch.bfloat16:
+        np.testing.assert_array_equal(_np(b.y), o["ybf16"], err_msg="y bf16")
+    else:
+        np.testing.assert_array_equal(_np(b.y), o["y32"], err_msg="y fp32")
+
+
+def _inputs(M, K, N, dtype, seed, n_out=None, factor=100.0, T=None, kind="normal"):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    n_out = max(1, K // 100) if n_out is None else n_out
+    idx = torch.randperm(K, generator=g)[:n_out]
+    fac = torch.full((n_out,), factor)
+    x = synth.activations(M, K, kind, idx, fac, dtype, g, "cpu")
+    w = synth.weights(K, N, 0.02, dtype, g, "cpu")
+    calib = synth.activations(T if T is not None else max(M, 1), K, kind, idx, fac, dtype, g, "cpu")
+    return x, w, calib
+
+
+CASES = [
+    # M, K, N, dtype, gran, alpha, T
+    (1, 16, 1, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 3),
+    (7, 48, 5, torch.float32, sq.SQ_PER_TENSOR, 0.5, 9),
+    (129, 272, 300, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 200),
+    (300, 144, 260, torch.bfloat16, sq.SQ_PER_TENSOR, 0.75, 77),
+    (64, 4112, 136, torch.bfloat16, sq.SQ_PER_TOKEN, 0.4, 130),
+    (33, 16400, 40, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 40),
+    (5, 8192, 24, torch.float32, sq.SQ_PER_TOKEN, 1.0, 17),
+    (256, 256, 512, torch.bfloat16, sq.SQ_PER_TOKEN, 0.0, 512),
+    (130, 1024, 257, torch.bfloat16, sq.SQ_PER_TOKEN, 0.6, 1000),
+    (520, 512, 130, torch.float32, sq.SQ_PER_TENSOR, 0.5, 64),
+    (96, 12288, 200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 300),
+]
+
+
+@pytest.mark.parametrize("M,K,N,dtype,gran,alpha,T", CASES)
+@pytest.mark.parametrize("y_dtype", [torch.bfloat16, torch.float32])
+def test_pipeline_matches_oracle(M, K, N, dtype, gran, alpha, T, y_dtype):
+    _say(f"case M={M} K={K} N={N} {dtype} gran={gran} alpha={alpha} T={T} y={y_dtype}")
+    x, w, calib = _inputs(M, K, N, dtype, seed=M * 7 + K * 3 + N, T=T)
+    b = _run_gpu(x.to(DEV), w.to(DEV), calib.to(DEV), alpha, gran, y_dtype)
+    o = oracle.w8a8_linear(_np(x), _np(w), alpha, gran, calib=_np(calib), nthreads=8)
+    _compare(b, o, alpha, y_dtype)
+
+
+@pytest.mark.parametrize("gran", [sq.SQ_PER_TOKEN, sq.SQ_PER_TENSOR])
+def test_unsmoothed_baseline_matches_oracle(gran):
+    x, w, calib = _inputs(200, 320, 150, torch.bfloat16, seed=5)
+    b = _run_gpu(x.to(DEV), w.to(DEV), None, None, gran)
+    o = oracle.w8a8_linear(_np(x), _np(w), None, gran, nthreads=8)
+    _compare(b, o, None, torch.bfloat16)
+
+
+@pytest.mark.parametrize("gran,key", [(sq.SQ_PER_TENSOR, "per_tensor_act_per_channel_w"),
+                                      (sq.SQ_PER_TOKEN, "per_token_act_per_channel_w")])
+def test_worked_example_on_gpu(gran, key):
+    """The page's 3x3 example, zero-padded to K = 16 input channels (padding
+    channels are all zero, so they change no maximum and no product)."""
+    g = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    X = np.zeros((3, 16), np.float32)
+    W = np.zeros((16, 2), np.float32)
+    X[:, :3] = np.array(g["X"], np.float32)
+    W[:3, :] = np.array(g["W"], np.float32)
+    xt, wt = torch.from_numpy(X).to(DEV), torch.from_numpy(W).to(DEV)
+    b = _run_gpu(xt, wt, xt, g["alpha"], gran, torch.float32)
+    o = oracle.w8a8_linear(X, W, g["alpha"], gran)
+    _compare(b, o, g["alpha"], torch.float32)
+    Y = oracle.matmul_f64(X, W)
+    e = g["relative_error_percent"][key]
+    assert round(100 * oracle.rel_fro(_np(b.y), Y), e["after_decimals"]) == e["after"]
+    base = _run_gpu(xt, wt, None, None, gran, torch.float32)
+    assert round(100 * oracle.rel_fro(_np(base.y), Y), e["before_decimals"]) == e["before"]
+    if gran == sq.SQ_PER_TENSOR:
+        assert _np(b.xq)[:, 0].tolist() == g["channel1_codes"]["after"]
+        assert _np(base.xq)[:, 0].tolist() == g["channel1_codes"]["before"]
+
+
+def _finite_bf16_patterns():
+    p = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((p.astype(np.uint32) >> 7) & 0xFF) != 0xFF
+    return p[finite]
+
+
+@pytest.mark.parametrize("inv_scale", ["ones", "pow2", "random"])
+def test_exhaustive_bf16_element_map_activations(inv_scale):
+    """Every finite bf16 pattern goes through smoothing and coding, per token
+    (inverse factors <= 1 keep every smoothed value finite).  The first rows
+    hold only subnormal and tiny values, where 127/max overflows."""
+    pats = _finite_bf16_patterns()
+    K = 256
+    rows = -(-pats.size // K)
+    buf = np.zeros(rows * K, np.uint16)
+    buf[:pats.size] = pats
+    X = buf.reshape(rows, K)
+    rng = np.random.default_rng(1)
+    if inv_scale == "ones":
+        inv = np.ones(K, np.float32)
+    elif inv_scale == "pow2":
+        inv = (2.0 ** rng.integers(-20, 1, K)).astype(np.float32)
+    else:
+        inv = rng.uniform(1e-3, 1.0, K).astype(np.float32)
+    xt = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(DEV)
+    it = torch.from_numpy(inv).to(DEV)
+    xq = torch.empty(rows, K, dtype=torch.int8, device=DEV)
+    xs = torch.empty(rows, dtype=torch.float32, device=DEV)
+    sq.sq_quant_act(xt, it, sq.SQ_PER_TOKEN, xq, xs)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quant_act(X, inv, oracle.PER_TOKEN)
+    np.testing.assert_array_equal(_np(xs), os_)
+    np.testing.assert_array_equal(_np(xq), oq)
+
+
+def test_exhaustive_bf16_element_map_weights():
+    """Every finite bf16 pattern goes through weight smoothing and coding."""
+    pats = _finite_bf16_patterns()
+    N = 128
+    K = -(-pats.size // N)
+    K = (K + 15) // 16 * 16
+    buf = np.zeros(K * N, np.uint16)
+    buf[:pats.size] = pats
+    W = buf.reshape(K, N)
+    s = np.random.default_rng(2).uniform(0.25, 1.0, K).astype(np.float32)
+    wt = torch.from_numpy(W.view(np.int16)).view(torch.bfloat16).to(DEV)
+    st = torch.from_numpy(s).to(DEV)
+    wq = torch.empty(N, K, dtype=torch.int8, device=DEV)
+    ws = torch.empty(N, dtype=torch.float32, device=DEV)
+    work = torch.empty(sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, N, K), dtype=torch.uint8, device=DEV)
+    sq.sq_quant_weight(wt, st, wq, ws, work)
+    torch.cuda.synchronize()
+    oq, os_ = oracle.quant_weight(W, s)
+    np.testing.assert_array_equal(_np(ws), os_)
+    np.testing.assert_array_equal(_np(wq), oq)
+
+
+def test_calibration_chunks_and_resume():
+    x, w, calib = _inputs(8, 1024, 8, torch.bfloat16, seed=3, T=1000)
+    ct = calib.to(DEV)
+    a1 = torch.zeros(1024, device=DEV)
+    sq.sq_calib_absmax(ct, a1)
+    a2 = torch.zeros(1024, device=DEV)
+    for part in torch.split(ct, [1, 300, 77, 622]):
+        sq.sq_calib_absmax(part, a2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(a1), _np(a2))
+    np.testing.assert_array_equal(_np(a1), oracle.calib_absmax(_np(calib)))
+    sq.sq_calib_absmax(ct, a1)  # idempotent
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(a1), _np(a2))
+
+
+def test_strided_inputs():
+    """Row strides larger than the row (views into wider buffers)."""
+    x, w, calib = _inputs(70, 256, 96, torch.bfloat16, seed=9, T=100)
+    xw = torch.zeros(70, 256 + 64, dtype=torch.bfloat16)
+    xw[:, :256] = x
+    ww = torch.zeros(256, 96 + 8, dtype=torch.bfloat16)
+    ww[:, :96] = w
+    cw = torch.zeros(100, 256 + 16, dtype=torch.bfloat16)
+    cw[:, :256] = calib
+    b = _run_gpu(xw.to(DEV)[:, :256], ww.to(DEV)[:, :96], cw.to(DEV)[:, :256], 0.5, sq.SQ_PER_TOKEN)
+    o = oracle.w8a8_linear(_np(x), _np(w), 0.5, oracle.PER_TOKEN, calib=_np(calib))
+    _compare(b, o, 0.5, torch.bfloat16)
+
+
+def test_zero_rows_and_columns():
+    x, w, calib = _inputs(40, 128, 70, torch.bfloat16, seed=4, T=40)
+    x[3] = 0
+    x[:, 5] = 0
+    calib[:, 5] = 0   # dead input channel: floored maxima
+    w[:, 9] = 0       # dead output channel: scale 0, codes 0, y = 0
+    w[17] = 0
+    b = _run_gpu(x.to(DEV), w.to(DEV), calib.to(DEV), 0.5, sq.SQ_PER_TOKEN)
+    o = oracle.w8a8_linear(_np(x), _np(w), 0.5, oracle.PER_TOKEN, calib=_np(calib))
+    _compare(b, o, 0.5, torch.bfloat16)
+    assert float(_np(b.x_scale)[3]) == 0.0
+    assert float(_np(b.w_scale)[9]) == 0.0
+
+
+def test_k_zero_and_empty():
+    # K = 0: scales are 0 and y = 0
+    xq = torch.empty(4, 0, dtype=torch.int8, device=DEV)
+    wq = torch.empty(3, 0, dtype=torch.int8, device=DEV)
+    xs = torch.ones(4, device=DEV)
+    ws = torch.ones(3, device=DEV)
+    y = torch.full((4, 3), 7.0, dtype=torch.float32, device=DEV)
+    sq.sq_gemm_w8a8(xq, xs, sq.SQ_PER_TOKEN, wq, ws, y)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+    # M = 0 and T = 0 do nothing
+    amax = torch.full((32,), 3.0, device=DEV)
+    sq.sq_calib_absmax(torch.empty(0, 32, dtype=torch.bfloat16, device=DEV), amax)
+    torch.cuda.synchronize()
+    assert (amax == 3.0).all()
+
+
+def test_determinism_repeat_runs():
+    x, w, calib = _inputs(512, 2048, 1024, torch.bfloat16, seed=12, T=1024)
+    xd, wd, cd = x.to(DEV), w.to(DEV), calib.to(DEV)
+    b1 = _run_gpu(xd, wd, cd, 0.5, sq.SQ_PER_TOKEN)
+    b2 = _run_gpu(xd, wd, cd, 0.5, sq.SQ_PER_TOKEN)
+    for name in ("amax_x", "s", "wq", "w_scale", "xq", "x_scale", "acc", "y"):
+        assert torch.equal(getattr(b1, name), getattr(b2, name)), name
