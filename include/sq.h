@@ -47,9 +47,13 @@
  *     returns a negative sq_status, enqueues nothing and records a message for
  *     sq_last_error().  A launch failure returns SQ_ERR_HIP.
  *   - Requirements checked: non-NULL required pointers; sizes >= 0;
- *     K % 16 == 0 and K <= 131072; ld >= row length; matrix base pointers and
- *     row strides 16-byte aligned (ld * element size % 16 == 0).  M, N and the
- *     token count T may be any non-negative value (ragged tails are handled).
+ *     K % 16 == 0 and K <= 131072; ld >= row length; activation inputs (x),
+ *     int8 codes, outputs and per-channel vectors read as vectors (inv_s,
+ *     w_scale) 16-byte aligned, with activation row strides a multiple of 16
+ *     bytes; weight inputs (w) only need element alignment and any row stride
+ *     (rows that are not 16-byte aligned are read element by element, slower).
+ *     M, N and the token count T may be any non-negative value (ragged tails
+ *     are handled).
  *     Empty problems (a zero size) enqueue nothing and return SQ_OK, except
  *     sq_gemm_w8a8 with K = 0, which writes y = 0.
  *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.

@@ -44,15 +44,22 @@ constexpr int64_t kMaxMN = (int64_t)1 << 30;
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Shared checks of a [rows, cols] input with row stride ld.
+// Shared checks of a [rows, cols] input with row stride ld.  Activations
+// (need16) must have 16-byte aligned rows; weights only element alignment
+// (rows that are not 16-byte aligned take a slower element-wise load path).
 sq_status check_matrix(const char* fn, const char* name, const void* p, sq_dtype t, int64_t rows, int64_t cols,
-                       int64_t ld) {
+                       int64_t ld, bool need16 = true) {
     if (!dtype_ok(t)) return fail(SQ_ERR_UNSUPPORTED, "%s: %s dtype %d is not SQ_BF16 or SQ_F32", fn, name, (int)t);
     if (rows < 0 || cols < 0) return fail(SQ_ERR_INVALID_ARG, "%s: %s has negative size", fn, name);
     if (ld < cols) return fail(SQ_ERR_INVALID_ARG, "%s: %s row stride %lld < row length %lld", fn, name,
                                (long long)ld, (long long)cols);
     if (rows > 0 && cols > 0) {
         if (!p) return fail(SQ_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+        if (!need16) {
+            if (reinterpret_cast<uintptr_t>(p) % elem_size(t) != 0)
+                return fail(SQ_ERR_INVALID_ARG, "%s: %s is not aligned to its element size", fn, name);
+            return SQ_OK;
+        }
         if (!aligned16(p)) return fail(SQ_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);
         if ((ld * (int64_t)elem_size(t)) % 16 != 0)
             return fail(SQ_ERR_INVALID_ARG, "%s: %s row stride %lld elements is not a multiple of 16 bytes", fn,
@@ -132,7 +139,7 @@ sq_status sq_smooth_factors(const float* amax_x, const void* w, sq_dtype wt, int
     SQ_TRY(check_vec(fn, "inv_s", inv_s, K));
     if (w) {
         if (N <= 0) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld must be positive when w is given", fn, (long long)N);
-        SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw));
+        SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
         if (amax_w) SQ_TRY(check_vec(fn, "amax_w", amax_w, K));
     } else {
         if (!amax_w && K > 0) return fail(SQ_ERR_INVALID_ARG, "%s: need w or a precomputed amax_w", fn);
@@ -150,7 +157,7 @@ sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t K, int64_t N, int6
     const char* fn = "sq_quant_weight";
     SQ_TRY(check_k(fn, K));
     if (N > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld too large", fn, (long long)N);
-    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw));
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
     if (s) SQ_TRY(check_vec(fn, "s", s, K));
     SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
     if (K > 0 && N > 0) {

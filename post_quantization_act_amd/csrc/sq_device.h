@@ -68,10 +68,18 @@ __device__ __forceinline__ void load8_tail(const T* p, int64_t n, float (&v)[8])
     }
 }
 
-template <typename T>
+// kVec: rows are 16-byte aligned, so a full group is one vector load;
+// otherwise (a weight whose row stride is not a multiple of 16 bytes) every
+// element is loaded on its own.
+template <bool kVec = true, typename T>
 __device__ __forceinline__ void load8_any(const T* p, int64_t n, float (&v)[8]) {
-    if (n >= 8) load8(p, v);
+    if (kVec && n >= 8) load8(p, v);
     else load8_tail(p, n, v);
+}
+
+// True when every row of a matrix starts on a 16-byte boundary.
+__host__ __device__ inline bool rows_aligned16(const void* p, int64_t ld, int64_t elem_bytes) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0 && (ld * elem_bytes) % 16 == 0;
 }
 
 // Max over the wavefront (all 64 lanes end with the result).

@@ -3,6 +3,8 @@
 //  - smoothed activations to per-token (or per-tensor) INT8.
 // Both are HBM-bound: read the bf16/fp32 source once, write one byte per
 // element.
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq_internal.h"
 
@@ -22,7 +24,7 @@ namespace sqk {
 constexpr int kQwTile = 128;
 constexpr int kQwStride = kQwTile + 8;
 
-template <typename T, bool kScaled>
+template <typename T, bool kScaled, bool kVec>
 __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t K, int64_t N, int64_t ld,
                                                       const float* __restrict__ s,
                                                       const uint32_t* __restrict__ colmax,
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, i
         for (int rr = 0; rr < 8; ++rr) {
             const int64_t j = j0 + rg * 8 + rr;
             if (j < K) {
-                load8_any(w + j * ld + kc, ncol, v[rr]);
+                load8_any<kVec>(w + j * ld + kc, ncol, v[rr]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) v[rr][i] = 0.0f;
@@ -252,18 +254,20 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
                                const uint32_t* colmax, int8_t* wq, float* w_scale, hipStream_t st) {
     if (K <= 0 || N <= 0) return hipSuccess;
     dim3 grid((unsigned)((N + kQwTile - 1) / kQwTile), (unsigned)((K + kQwTile - 1) / kQwTile));
+    const bool vec = rows_aligned16(w, ld, bf16 ? 2 : 4);
+    auto go = [&](auto tag, auto scaled, auto vecc) {
+        using T = decltype(tag);
+        hipLaunchKernelGGL((k_quant_weight<T, decltype(scaled)::value, decltype(vecc)::value>), grid, dim3(256), 0,
+                           st, static_cast<const T*>(w), K, N, ld, s, colmax, wq, w_scale);
+    };
+    using TT = std::true_type;
+    using FF = std::false_type;
     if (bf16) {
-        const bf16_t* p = static_cast<const bf16_t*>(w);
-        if (s)
-            hipLaunchKernelGGL((k_quant_weight<bf16_t, true>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
-        else
-            hipLaunchKernelGGL((k_quant_weight<bf16_t, false>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
+        if (s) { if (vec) go(bf16_t{}, TT{}, TT{}); else go(bf16_t{}, TT{}, FF{}); }
+        else { if (vec) go(bf16_t{}, FF{}, TT{}); else go(bf16_t{}, FF{}, FF{}); }
     } else {
-        const float* p = static_cast<const float*>(w);
-        if (s)
-            hipLaunchKernelGGL((k_quant_weight<float, true>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
-        else
-            hipLaunchKernelGGL((k_quant_weight<float, false>), grid, dim3(256), 0, st, p, K, N, ld, s, colmax, wq, w_scale);
+        if (s) { if (vec) go(float{}, TT{}, TT{}); else go(float{}, TT{}, FF{}); }
+        else { if (vec) go(float{}, FF{}, TT{}); else go(float{}, FF{}, FF{}); }
     }
     return hipGetLastError();
 }

@@ -2,6 +2,8 @@
 // smoothing factors.  All of them are HBM-bound streams over a matrix; the
 // loads are 16-byte vectors along the contiguous axis and each wavefront
 // covers whole 128-byte lines.
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq_internal.h"
 
@@ -27,7 +29,7 @@ constexpr int kColLanes = 32;
 constexpr int kRowLanes = 8;
 constexpr int kColsPerBlock = kColLanes * 8;
 
-template <typename T, bool kScaled>
+template <typename T, bool kScaled, bool kVec>
 __global__ __launch_bounds__(256) void k_col_absmax(const T* __restrict__ x, int64_t rows, int64_t cols,
                                                     int64_t ld, const float* __restrict__ row_scale,
                                                     uint32_t* __restrict__ out, int64_t rows_per_block) {
@@ -48,7 +50,7 @@ __global__ __launch_bounds__(256) void k_col_absmax(const T* __restrict__ x, int
         for (; r + (U - 1) * kRowLanes < r_end; r += U * kRowLanes) {
             float v[U][8];
 #pragma unroll
-            for (int u = 0; u < U; ++u) load8_any(base + (r + u * kRowLanes) * ld, ncol, v[u]);
+            for (int u = 0; u < U; ++u) load8_any<kVec>(base + (r + u * kRowLanes) * ld, ncol, v[u]);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const float sc = kScaled ? row_scale[r + u * kRowLanes] : 1.0f;
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void k_col_absmax(const T* __restrict__ x, int
         }
         for (; r < r_end; r += kRowLanes) {
             float v[8];
-            load8_any(base + r * ld, ncol, v);
+            load8_any<kVec>(base + r * ld, ncol, v);
             const float sc = kScaled ? row_scale[r] : 1.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -107,7 +109,7 @@ __device__ __forceinline__ void smooth_factor(float ax, float aw, float alpha, f
 // inv_s_j right away (the row max is the only per-row input the factor
 // needs besides amax_x[j]).  Lanes stride along the row with 16-byte loads,
 // 4 loads in flight per lane, and reduce with cross-lane shuffles.
-template <typename T>
+template <typename T, bool kVec>
 __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict__ w, int64_t K, int64_t N,
                                                             int64_t ld, const float* __restrict__ amax_x,
                                                             float alpha, float* __restrict__ s,
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
     constexpr int U = 4;
     constexpr int step = kWave * 8;
     int64_t c = (int64_t)lane * 8;
-    for (; c + (U - 1) * step + 8 <= N; c += U * step) {
+    for (; kVec && c + (U - 1) * step + 8 <= N; c += U * step) {
         float v[U][8];
 #pragma unroll
         for (int u = 0; u < U; ++u) load8(row + c + u * step, v[u]);
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
     }
     for (; c < N; c += step) {
         float v[8];
-        load8_any(row + c, N - c, v);
+        load8_any<kVec>(row + c, N - c, v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
     }
@@ -189,18 +191,20 @@ hipError_t launch_col_absmax(const void* x, bool bf16, int64_t rows, int64_t col
     const int64_t rpb = rows_per_block_for(rows, col_blocks, 2048);
     const int64_t row_blocks = (rows + rpb - 1) / rpb;
     dim3 grid((unsigned)col_blocks, (unsigned)row_blocks);
+    const bool vec = rows_aligned16(x, ld, bf16 ? 2 : 4);
+    auto go = [&](auto tag, auto scaled, auto vecc) {
+        using T = decltype(tag);
+        hipLaunchKernelGGL((k_col_absmax<T, decltype(scaled)::value, decltype(vecc)::value>), grid, dim3(256), 0, st,
+                           static_cast<const T*>(x), rows, cols, ld, row_scale, out, rpb);
+    };
+    using TT = std::true_type;
+    using FF = std::false_type;
     if (bf16) {
-        const bf16_t* p = static_cast<const bf16_t*>(x);
-        if (row_scale)
-            hipLaunchKernelGGL((k_col_absmax<bf16_t, true>), grid, dim3(256), 0, st, p, rows, cols, ld, row_scale, out, rpb);
-        else
-            hipLaunchKernelGGL((k_col_absmax<bf16_t, false>), grid, dim3(256), 0, st, p, rows, cols, ld, row_scale, out, rpb);
+        if (row_scale) { if (vec) go(bf16_t{}, TT{}, TT{}); else go(bf16_t{}, TT{}, FF{}); }
+        else { if (vec) go(bf16_t{}, FF{}, TT{}); else go(bf16_t{}, FF{}, FF{}); }
     } else {
-        const float* p = static_cast<const float*>(x);
-        if (row_scale)
-            hipLaunchKernelGGL((k_col_absmax<float, true>), grid, dim3(256), 0, st, p, rows, cols, ld, row_scale, out, rpb);
-        else
-            hipLaunchKernelGGL((k_col_absmax<float, false>), grid, dim3(256), 0, st, p, rows, cols, ld, row_scale, out, rpb);
+        if (row_scale) { if (vec) go(float{}, TT{}, TT{}); else go(float{}, TT{}, FF{}); }
+        else { if (vec) go(float{}, FF{}, TT{}); else go(float{}, FF{}, FF{}); }
     }
     return hipGetLastError();
 }
@@ -210,12 +214,14 @@ hipError_t launch_row_absmax_factors(const void* w, bool bf16, int64_t K, int64_
                                      hipStream_t st) {
     if (K <= 0) return hipSuccess;
     const int64_t blocks = (K + 3) / 4;
-    if (bf16)
-        hipLaunchKernelGGL((k_row_absmax_factors<bf16_t>), dim3((unsigned)blocks), dim3(256), 0, st,
-                           static_cast<const bf16_t*>(w), K, N, ld, amax_x, alpha, s, inv_s, amax_w);
-    else
-        hipLaunchKernelGGL((k_row_absmax_factors<float>), dim3((unsigned)blocks), dim3(256), 0, st,
-                           static_cast<const float*>(w), K, N, ld, amax_x, alpha, s, inv_s, amax_w);
+    const bool vec = rows_aligned16(w, ld, bf16 ? 2 : 4);
+    auto go = [&](auto tag, auto vecc) {
+        using T = decltype(tag);
+        hipLaunchKernelGGL((k_row_absmax_factors<T, decltype(vecc)::value>), dim3((unsigned)blocks), dim3(256), 0, st,
+                           static_cast<const T*>(w), K, N, ld, amax_x, alpha, s, inv_s, amax_w);
+    };
+    if (bf16) { if (vec) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{}); }
+    else { if (vec) go(float{}, std::true_type{}); else go(float{}, std::false_type{}); }
     return hipGetLastError();
 }
 
