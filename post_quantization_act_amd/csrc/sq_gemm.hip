@@ -4,19 +4,26 @@
 //   acc[m, n] = sum_k Xq[m, k] * Wq[n, k]        (exact int32)
 //   y[m, n]   = bf16_rne(fl(fl(float(acc) * x_scale[m]) * w_scale[n]))
 //
-// Both operands are K-contiguous (Xq [M, K], Wq [N, K]).  The kernel computes
+// Both operands are K-contiguous (Xq [M, K], Wq [N, K]).  The kernels compute
 // the transposed product D = Wq . Xq^T so that each lane's accumulator
 // registers run along n, which is the contiguous axis of y: four consecutive
 // outputs leave as one 8-byte bf16 store.
 //
-// Block tile BN (n) x BM (m) x 128 (k), 256 threads = 2 x 2 wavefronts, each
-// wavefront owning a (BN/2) x (BM/2) sub-tile of 32 x 32 MFMA blocks.
-// Operand tiles are staged through LDS, double-buffered: while the matrix
-// cores work on stage k, the next stage's 16-byte global loads are in flight
-// in registers and are written to the other LDS buffer afterwards.  LDS rows
-// are 128 bytes (8 chunks of 16 B); chunk c of row r lives at slot
-// c ^ ((r >> 1) & 7), which makes both the 16-byte LDS writes and the
-// fragment reads (16 rows x one chunk per quarter-wave) bank-conflict free.
+// Two kernels:
+//  - k_gemm_ring (K % 128 == 0, operands below 4 GiB): block tile BN x BM,
+//    4 wavefronts in a 2 x 2 grid, each owning (BN/2) x (BM/2) of 32 x 32 MFMA
+//    blocks.  Operand tiles of 128 bytes of k per row ("stages") are copied
+//    from global memory straight into a two-buffer LDS ring with
+//    global_load_lds_dwordx4, so no registers stage them and each row request
+//    is one full 128-byte line.  Each stage is four k-steps of 32; fragments
+//    of k-step s+1 are read from LDS while the matrix cores work on k-step s,
+//    and the only workgroup barrier of a stage sits between k-steps 2 and 3:
+//    after it the next stage is complete in LDS and the buffer of this stage
+//    is free, so the copy of stage k+2 is issued during k-step 3.
+//  - k_gemm_generic: any K % 16 == 0; register-staged double buffer.
+// Blocks are dealt round-robin to the 8 XCDs; tiles are renumbered so each
+// XCD walks a contiguous run of a grouped (m-major within groups of 8 tile
+// rows) raster and concurrent blocks on one XCD share operand panels in its L2.
 #include "sq_device.h"
 #include "sq_internal.h"
 
@@ -24,156 +31,69 @@ namespace sqk {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
 
 constexpr int kBK = 128;  // bytes of k per stage (one 128-byte line per row)
 
+// Slot (in 16-byte units) of chunk c (0..7) of row r inside a stage: chunks are
+// XOR-swizzled by (r >> 1) & 7 so that the 16 rows a quarter-wavefront reads
+// for one MFMA fragment, and the 8 rows x 8 chunks one 1-KB copy writes, hit
+// distinct LDS banks.
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
-template <int BN, int BM, int kOut /*0: bf16, 1: fp32*/, bool kAcc>
-__global__ __launch_bounds__(256) void k_gemm_w8a8(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
-                                                   int per_tensor, const int8_t* __restrict__ wq,
-                                                   const float* __restrict__ w_scale, int M, int N, int K,
-                                                   void* __restrict__ y, int32_t* __restrict__ acc_out,
-                                                   int tiles_n) {
-    constexpr int WN = BN / 2, WM = BM / 2;
-    constexpr int TN = WN / 32, TM = WM / 32;
-    constexpr int A_CHUNKS = BN * 8 / 256;  // 16-byte chunks per thread per stage
-    constexpr int B_CHUNKS = BM * 8 / 256;
-    constexpr int STAGE = (BN + BM) * 8;    // uint4 slots per stage
+// Output tile renumbering: blocks are dealt round-robin to the 8 XCDs, so give
+// each XCD a contiguous run of virtual tile ids, then walk them in groups of
+// `group_m` tile rows (m-major inside a group).
+__device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int group_m, int& tn, int& tm) {
+    const int b = blockIdx.x, nb = gridDim.x;
+    const int xcd = b % 8, l = b / 8, per = nb / 8, rem = nb % 8;
+    const int v = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + l;
+    const int group = group_m * tiles_n;
+    const int g = v / group, first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = v % group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
 
-    __shared__ uint4 lds[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int wave = tid / kWave, lane = tid % kWave;
-    const int wn = wave % 2, wm = wave / 2;
-
-    const int tile = blockIdx.x;
-    const int tn = tile % tiles_n, tm = tile / tiles_n;
-    const int n0 = tn * BN, m0 = tm * BM;
-
-    // Global source rows of this thread's chunks (clamped into the matrix so
-    // ragged edges read valid memory; their results are never stored).
-    const int8_t* a_src[A_CHUNKS];
-    const int8_t* b_src[B_CHUNKS];
-    int a_slot[A_CHUNKS], b_slot[B_CHUNKS], a_kc[A_CHUNKS], b_kc[B_CHUNKS];
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-        const int q = tid + i * 256;
-        const int r = q / 8, c = q % 8;
-        const int n = min(n0 + r, N - 1);
-        a_src[i] = wq + (int64_t)n * K + c * 16;
-        a_kc[i] = c * 16;
-        a_slot[i] = swz(r, c);
-    }
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-        const int q = tid + i * 256;
-        const int r = q / 8, c = q % 8;
-        const int m = min(m0 + r, M - 1);
-        b_src[i] = xq + (int64_t)m * K + c * 16;
-        b_kc[i] = c * 16;
-        b_slot[i] = BN * 8 + swz(r, c);
-    }
-
-    v16i acc[TN][TM];
-#pragma unroll
-    for (int a = 0; a < TN; ++a)
-#pragma unroll
-        for (int b = 0; b < TM; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0;
-
-    uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-    const int nk = (K + kBK - 1) / kBK;
-
-    auto gload = [&](int kt) {
-        const int k0 = kt * kBK;
-        const bool full = k0 + kBK <= K;
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i)
-            ra[i] = (full || k0 + a_kc[i] < K) ? ld16(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i)
-            rb[i] = (full || k0 + b_kc[i] < K) ? ld16(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
-    };
-    auto lstore = [&](int buf) {
-        uint4* base = lds + buf * STAGE;
-#pragma unroll
-        for (int i = 0; i < A_CHUNKS; ++i) base[a_slot[i]] = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) base[b_slot[i]] = rb[i];
-    };
-
-    // Fragment rows of this lane: row (lane % 32) of each 32-row block, chunk
-    // (2 * kstep + lane / 32) within the 128-byte row.
+// Dequantize and store one wavefront's (TN*32) x (TM*32) block of accumulators.
+// 32x32 accumulator layout: the lane holds column (lane % 32) of a 32x32 block
+// (here: m) and rows 8*g + 4*(lane/32) + e, e = 0..3, in registers 4*g + e
+// (here: n).
+template <int TN, int TM, int kOut, bool kAcc>
+__device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
+                                         const float* __restrict__ x_scale, int per_tensor,
+                                         const float* __restrict__ w_scale, int M, int N, void* __restrict__ y,
+                                         int32_t* __restrict__ acc_out) {
     const int fr = lane % 32, fh = lane / 32;
-
-    if (nk > 0) {
-        gload(0);
-        lstore(0);
-    }
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
-        const uint4* base = lds + cur * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
-            const int c = 2 * ks + fh;
-            v4i af[TN], bfr[TM];
-#pragma unroll
-            for (int a = 0; a < TN; ++a) {
-                const uint4 u = base[swz(wn * WN + a * 32 + fr, c)];
-                af[a] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
-            }
-#pragma unroll
-            for (int b = 0; b < TM; ++b) {
-                const uint4 u = base[BN * 8 + swz(wm * WM + b * 32 + fr, c)];
-                bfr[b] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
-            }
-#pragma unroll
-            for (int a = 0; a < TN; ++a)
-#pragma unroll
-                for (int b = 0; b < TM; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bfr[b], acc[a][b], 0, 0, 0);
-        }
-        if (kt + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
-    }
-
-    // Epilogue.  32x32 accumulator layout: lane holds column (lane % 32) of
-    // the block (here: m) and rows 8*g + 4*(lane/32) + e, e = 0..3, in
-    // registers 4*g + e (here: n).
     const bool n_vec = (N % 4) == 0;
     const float xs_t = per_tensor ? x_scale[0] : 0.0f;
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
-        const int m = m0 + wm * WM + b * 32 + fr;
+        const int m = mbase + b * 32 + fr;
         if (m >= M) continue;
         const float xs = per_tensor ? xs_t : x_scale[m];
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * WN + a * 32 + 8 * g + 4 * fh;
+                const int n = nbase + a * 32 + 8 * g + 4 * fh;
                 if (n >= N) continue;
                 int32_t av[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) av[e] = acc[a][b][4 * g + e];
-                float yv[4];
                 if (n_vec) {
                     const float4 ws = *reinterpret_cast<const float4*>(w_scale + n);
-                    yv[0] = ((float)av[0] * xs) * ws.x;
-                    yv[1] = ((float)av[1] * xs) * ws.y;
-                    yv[2] = ((float)av[2] * xs) * ws.z;
-                    yv[3] = ((float)av[3] * xs) * ws.w;
+                    const float y0 = ((float)av[0] * xs) * ws.x;
+                    const float y1 = ((float)av[1] * xs) * ws.y;
+                    const float y2 = ((float)av[2] * xs) * ws.z;
+                    const float y3 = ((float)av[3] * xs) * ws.w;
                     const int64_t off = (int64_t)m * N + n;
                     if constexpr (kOut == 0) {
-                        uint2 pk = make_uint2(pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]));
-                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) = pk;
+                        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) =
+                            make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
                     } else {
-                        *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(yv[0], yv[1], yv[2], yv[3]);
+                        *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(y0, y1, y2, y3);
                     }
                     if constexpr (kAcc) *reinterpret_cast<int4*>(acc_out + off) = make_int4(av[0], av[1], av[2], av[3]);
                 } else {
@@ -195,32 +115,320 @@ __global__ __launch_bounds__(256) void k_gemm_w8a8(const int8_t* __restrict__ xq
     }
 }
 
-template <int BN, int BM>
-static void launch_tiles(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
-                         const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
-                         hipStream_t st) {
-    const int tiles_n = (N + BN - 1) / BN;
-    const int tiles_m = (M + BM - 1) / BM;
-    dim3 grid((unsigned)(tiles_n * tiles_m));
-    const int pt = per_tensor ? 1 : 0;
-    if (y_bf16) {
-        if (acc_out)
-            hipLaunchKernelGGL((k_gemm_w8a8<BN, BM, 0, true>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, M, N, K, y, acc_out, tiles_n);
-        else
-            hipLaunchKernelGGL((k_gemm_w8a8<BN, BM, 0, false>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, M, N, K, y, acc_out, tiles_n);
-    } else {
-        if (acc_out)
-            hipLaunchKernelGGL((k_gemm_w8a8<BN, BM, 1, true>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, M, N, K, y, acc_out, tiles_n);
-        else
-            hipLaunchKernelGGL((k_gemm_w8a8<BN, BM, 1, false>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, M, N, K, y, acc_out, tiles_n);
-    }
+// ---- ring kernel: global -> LDS copies without registers -----------------------
+
+// One 16-byte-per-lane copy from global memory (base + voff) to LDS at
+// lds_off + 16 * lane.  The LDS destination goes through M0; the instruction
+// has no register result (the data lands in LDS), so its completion is
+// tracked only by vmcnt, which the kernel waits on explicitly before the
+// barrier that publishes the stage.
+__device__ __forceinline__ void copy16_to_lds(const int8_t* base, uint32_t voff, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_off), "v"(voff), "s"(base)
+                 : "memory", "m0");
 }
 
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
+
+template <int BN, int BM, int kOut, bool kAcc>
+__global__ __launch_bounds__(256) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
+                                                   int per_tensor, const int8_t* __restrict__ wq,
+                                                   const float* __restrict__ w_scale, int M, int N, int K,
+                                                   void* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
+                                                   int tiles_m, int group_m) {
+    constexpr int WN = BN / 2, WM = BM / 2, TN = WN / 32, TM = WM / 32;
+    constexpr int ROWS = BN + BM;             // rows of a stage: Wq tile rows, then Xq tile rows
+    constexpr int STAGE = ROWS * 8;           // 16-byte slots per stage
+    constexpr int COPIES = ROWS / 8;          // 1-KB copies per stage (8 rows each)
+    constexpr int L = COPIES / 4;             // copies per wavefront per stage
+    constexpr int NMF = TN * TM;              // MFMAs per k-step
+    constexpr int NRD = TN + TM;              // fragment reads per k-step
+    constexpr int DR = (NRD + NMF - 1) / NMF, DD = (L + NMF - 1) / NMF;
+    static_assert(COPIES % 4 == 0 && BN % 8 == 0, "tile");
+    static_assert(2 * STAGE * 16 <= 160 * 1024, "LDS");
+    __shared__ uint4 lds[2 * STAGE];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wn = wave % 2, wm = wave / 2;
+    int tn, tm;
+    tile_of_block(tiles_n, tiles_m, group_m, tn, tm);
+    const int n0 = tn * BN, m0 = tm * BM;
+
+    // Copy j of this wavefront (global copy index i = wave + 4j) fills rows
+    // 8i .. 8i+7 of a stage: lane -> row 8i + lane/8 and LDS chunk lane%8,
+    // which holds logical chunk (lane%8) ^ ((row >> 1) & 7).  Rows past the
+    // matrix edge are clamped to the last row (read, never stored).
+    uint32_t off[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int i = wave + 4 * j;
+        const int r = 8 * i + lane / 8;
+        const int c = (lane % 8) ^ ((r >> 1) & 7);
+        if (r < BN) off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c * 16;
+        else off[j] = (uint32_t)min(m0 + r - BN, M - 1) * (uint32_t)K + c * 16;
+    }
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
+    auto copy = [&](int kt, int j) {
+        const int i = wave + 4 * j;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + ((kt & 1) * STAGE + i * 64) * 16);
+        copy16_to_lds(8 * i < BN ? wq : xq, off[j] + (uint32_t)kt * kBK, la);
+    };
+
+    const int fr = lane % 32, fh = lane / 32;
+    v16i acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0;
+
+    v4i fa[2][TN], fb[2][TM];  // fragments of two consecutive k-steps
+    auto read_frag = [&](int buf, int ks, int q, int sl) {
+        const uint4* base = lds + buf * STAGE;
+        const int c = 2 * ks + fh;
+        if (q < TN) {
+            const uint4 u = base[swz(wn * WN + q * 32 + fr, c)];
+            fa[sl][q] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+        } else {
+            const uint4 u = base[swz(BN + wm * WM + (q - TN) * 32 + fr, c)];
+            fb[sl][q - TN] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+        }
+    };
+    // One k-step: NMF MFMAs on fragment slot `sl`; between them, the reads of
+    // k-step `rks` of LDS buffer `rbuf` into slot `rsl`, and the copies of
+    // stage `ckt`.  sched_barrier keeps this interleaving in program order.
+    auto kstep = [&](int sl, bool rd, int rbuf, int rks, int rsl, bool cp, int ckt) {
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+            const int a = j / TM, b = j % TM;
+            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[sl][a], fb[sl][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < DR; ++u)
+                if (rd && j * DR + u < NRD) read_frag(rbuf, rks, j * DR + u, rsl);
+#pragma unroll
+            for (int u = 0; u < DD; ++u)
+                if (cp && j * DD + u < L) copy(ckt, j * DD + u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = K / kBK;
+    if (nk > 0) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) copy(0, j);
+    }
+    if (nk > 1) {
+#pragma unroll
+        for (int j = 0; j < L; ++j) copy(1, j);
+    }
+    wait_vmcnt0();
+    __syncthreads();
+    if (nk > 0) {
+#pragma unroll
+        for (int q = 0; q < NRD; ++q) read_frag(0, 0, q, 0);
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(0, true, buf, 1, 1, false, 0);
+        kstep(1, true, buf, 2, 0, false, 0);
+        kstep(0, true, buf, 3, 1, false, 0);
+        // Every read of this stage is issued (and completes before the
+        // barrier); this wavefront's copies of stage kt+1 have landed.
+        wait_vmcnt0();
+        __syncthreads();
+        kstep(1, kt + 1 < nk, buf ^ 1, 0, 0, kt + 2 < nk, kt + 2);
+    }
+    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, per_tensor, w_scale, M, N, y,
+                                 acc_out);
+}
+
+// ---- generic kernel: any K % 16 == 0 -------------------------------------------
+
+template <int BN, int BM, int kOut /*0: bf16, 1: fp32*/, bool kAcc>
+__global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
+                                                      int per_tensor, const int8_t* __restrict__ wq,
+                                                      const float* __restrict__ w_scale, int M, int N, int K,
+                                                      void* __restrict__ y, int32_t* __restrict__ acc_out,
+                                                      int tiles_n, int tiles_m, int group_m) {
+    constexpr int WN = BN / 2, WM = BM / 2;
+    constexpr int TN = WN / 32, TM = WM / 32;
+    constexpr int A_CHUNKS = BN * 8 / 256;  // 16-byte chunks per thread per stage
+    constexpr int B_CHUNKS = BM * 8 / 256;
+    constexpr int STAGE = (BN + BM) * 8;    // uint4 slots per stage
+
+    __shared__ uint4 lds[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave, lane = tid % kWave;
+    const int wn = wave % 2, wm = wave / 2;
+    int tn, tm;
+    tile_of_block(tiles_n, tiles_m, group_m, tn, tm);
+    const int n0 = tn * BN, m0 = tm * BM;
+
+    // Source rows of this thread's chunks (clamped into the matrix so ragged
+    // edges read valid memory; their results are never stored).  A chunk past
+    // K reads its row's first chunk and is zeroed when written to LDS.
+    const int8_t* a_src[A_CHUNKS];
+    const int8_t* b_src[B_CHUNKS];
+    int a_slot[A_CHUNKS], b_slot[B_CHUNKS], a_kc[A_CHUNKS], b_kc[B_CHUNKS];
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) {
+        const int q = tid + i * 256;
+        const int r = q / 8, c = q % 8;
+        a_src[i] = wq + (int64_t)min(n0 + r, N - 1) * K;
+        a_kc[i] = c * 16;
+        a_slot[i] = swz(r, c);
+    }
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) {
+        const int q = tid + i * 256;
+        const int r = q / 8, c = q % 8;
+        b_src[i] = xq + (int64_t)min(m0 + r, M - 1) * K;
+        b_kc[i] = c * 16;
+        b_slot[i] = BN * 8 + swz(r, c);
+    }
+
+    v16i acc[TN][TM];
+#pragma unroll
+    for (int a = 0; a < TN; ++a)
+#pragma unroll
+        for (int b = 0; b < TM; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0;
+
+    uint4 ra[A_CHUNKS], rb[B_CHUNKS];
+    const int nk = (K + kBK - 1) / kBK;
+
+    auto gload = [&](int kt) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < A_CHUNKS; ++i) ra[i] = ld16(a_src[i] + (k0 + a_kc[i] < K ? k0 + a_kc[i] : 0));
+#pragma unroll
+        for (int i = 0; i < B_CHUNKS; ++i) rb[i] = ld16(b_src[i] + (k0 + b_kc[i] < K ? k0 + b_kc[i] : 0));
+    };
+    auto lstore = [&](int buf, int kt) {
+        uint4* base = lds + buf * STAGE;
+        const int k0 = kt * kBK;
+        if (k0 + kBK <= K) {
+#pragma unroll
+            for (int i = 0; i < A_CHUNKS; ++i) base[a_slot[i]] = ra[i];
+#pragma unroll
+            for (int i = 0; i < B_CHUNKS; ++i) base[b_slot[i]] = rb[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_CHUNKS; ++i) {
+                const uint32_t mk = k0 + a_kc[i] < K ? 0xFFFFFFFFu : 0u;
+                base[a_slot[i]] = make_uint4(ra[i].x & mk, ra[i].y & mk, ra[i].z & mk, ra[i].w & mk);
+            }
+#pragma unroll
+            for (int i = 0; i < B_CHUNKS; ++i) {
+                const uint32_t mk = k0 + b_kc[i] < K ? 0xFFFFFFFFu : 0u;
+                base[b_slot[i]] = make_uint4(rb[i].x & mk, rb[i].y & mk, rb[i].z & mk, rb[i].w & mk);
+            }
+        }
+    };
+
+    const int fr = lane % 32, fh = lane / 32;
+    v4i af[2][TN], bfr[2][TM];
+    auto rfrag = [&](int buf, int ks, int slot) {
+        const uint4* base = lds + buf * STAGE;
+        const int c = 2 * ks + fh;
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
+            const uint4 u = base[swz(wn * WN + a * 32 + fr, c)];
+            af[slot][a] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+        }
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+            const uint4 u = base[BN * 8 + swz(wm * WM + b * 32 + fr, c)];
+            bfr[slot][b] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+        }
+    };
+
+    if (nk > 0) {
+        gload(0);
+        lstore(0, 0);
+    }
+    __syncthreads();
+    if (nk > 0) rfrag(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < kBK / 32; ++ks) {
+            if (ks < kBK / 32 - 1) rfrag(cur, ks + 1, (ks + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int a = 0; a < TN; ++a)
+#pragma unroll
+                for (int b = 0; b < TM; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[ks & 1][a], bfr[ks & 1][b], acc[a][b], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kt + 1 < nk) {
+            lstore(cur ^ 1, kt + 1);
+            __syncthreads();
+            rfrag(cur ^ 1, 0, 0);
+        }
+    }
+    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, per_tensor, w_scale, M, N, y,
+                                 acc_out);
+}
+
+// ---- launchers ---------------------------------------------------------------------
+
+
+#define SQ_DEFINE_LAUNCH(KERNEL)                                                                                    \
+    template <int BN, int BM>                                                                                      \
+    static void launch_##KERNEL(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,        \
+                                const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out, \
+                                int group_m, hipStream_t st) {                                                     \
+        const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;                                        \
+        const dim3 grid((unsigned)(tiles_n * tiles_m));                                                            \
+        const int pt = per_tensor ? 1 : 0;                                                                         \
+        if (y_bf16) {                                                                                              \
+            if (acc_out)                                                                                           \
+                hipLaunchKernelGGL((KERNEL<BN, BM, 0, true>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, \
+                                   M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                                \
+            else                                                                                                   \
+                hipLaunchKernelGGL((KERNEL<BN, BM, 0, false>), grid, dim3(256), 0, st, xq, x_scale, pt, wq,        \
+                                   w_scale, M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                       \
+        } else {                                                                                                   \
+            if (acc_out)                                                                                           \
+                hipLaunchKernelGGL((KERNEL<BN, BM, 1, true>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, \
+                                   M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                                \
+            else                                                                                                   \
+                hipLaunchKernelGGL((KERNEL<BN, BM, 1, false>), grid, dim3(256), 0, st, xq, x_scale, pt, wq,        \
+                                   w_scale, M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                       \
+        }                                                                                                          \
+    }
+
+SQ_DEFINE_LAUNCH(k_gemm_ring)
+SQ_DEFINE_LAUNCH(k_gemm_generic)
+
 hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
-                            const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16,
+                            const float* w_scale, int64_t M64, int64_t N64, int64_t K64, void* y, bool y_bf16,
                             int32_t* acc_out, hipStream_t st) {
-    if (M <= 0 || N <= 0) return hipSuccess;
-    launch_tiles<256, 128>(xq, x_scale, per_tensor, wq, w_scale, (int)M, (int)N, (int)K, y, y_bf16, acc_out, st);
+    if (M64 <= 0 || N64 <= 0) return hipSuccess;
+    const int M = (int)M64, N = (int)N64, K = (int)K64;
+    const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
+                      (uint64_t)M * (uint64_t)K < (1ull << 32);
+    if (ring) {
+        // 256 x 256 tiles when there are at least two per CU; otherwise
+        // 128 x 128 tiles, two blocks per CU.
+        const int64_t big_tiles = ((N + 255) / 256) * (int64_t)((M + 255) / 256);
+        if (big_tiles >= 512)
+            launch_k_gemm_ring<256, 256>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+        else
+            launch_k_gemm_ring<128, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+    } else {
+        launch_k_gemm_generic<256, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+    }
     return hipGetLastError();
 }
 
