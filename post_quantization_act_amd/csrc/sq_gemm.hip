@@ -24,6 +24,8 @@
 // Blocks are dealt round-robin to the 8 XCDs; tiles are renumbered so each
 // XCD walks a contiguous run of a grouped (m-major within groups of 8 tile
 // rows) raster and concurrent blocks on one XCD share operand panels in its L2.
+#include <type_traits>
+
 #include "sq_device.h"
 #include "sq_internal.h"
 
@@ -60,19 +62,22 @@ __device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int grou
 // 32x32 accumulator layout: the lane holds column (lane % 32) of a 32x32 block
 // (here: m) and rows 8*g + 4*(lane/32) + e, e = 0..3, in registers 4*g + e
 // (here: n).
+// x_scale is read at index m * xs_step: xs_step = 1 per token, 0 per tensor.
+// kOut: 0 bf16, 1 fp32; kAcc: also store the int32 accumulators; kOut >= 2
+// marks N % 4 != 0 (element-wise stores), with the output type kOut - 2.
 template <int TN, int TM, int kOut, bool kAcc>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
-                                         const float* __restrict__ x_scale, int per_tensor,
+                                         const float* __restrict__ x_scale, int xs_step,
                                          const float* __restrict__ w_scale, int M, int N, void* __restrict__ y,
                                          int32_t* __restrict__ acc_out) {
     const int fr = lane % 32, fh = lane / 32;
-    const bool n_vec = (N % 4) == 0;
-    const float xs_t = per_tensor ? x_scale[0] : 0.0f;
+    constexpr bool n_vec = kOut < 2;
+    constexpr int kTy = kOut & 1;
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
         const int m = mbase + b * 32 + fr;
         if (m >= M) continue;
-        const float xs = per_tensor ? xs_t : x_scale[m];
+        const float xs = x_scale[m * xs_step];
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
 #pragma unroll
@@ -82,14 +87,14 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
                 int32_t av[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) av[e] = acc[a][b][4 * g + e];
-                if (n_vec) {
+                if constexpr (n_vec) {
                     const float4 ws = *reinterpret_cast<const float4*>(w_scale + n);
                     const float y0 = ((float)av[0] * xs) * ws.x;
                     const float y1 = ((float)av[1] * xs) * ws.y;
                     const float y2 = ((float)av[2] * xs) * ws.z;
                     const float y3 = ((float)av[3] * xs) * ws.w;
                     const int64_t off = (int64_t)m * N + n;
-                    if constexpr (kOut == 0) {
+                    if constexpr (kTy == 0) {
                         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) =
                             make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
                     } else {
@@ -102,7 +107,7 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
                         if (n + e >= N) break;
                         const float v = ((float)av[e] * xs) * w_scale[n + e];
                         const int64_t off = (int64_t)m * N + n + e;
-                        if constexpr (kOut == 0) {
+                        if constexpr (kTy == 0) {
                             static_cast<uint16_t*>(y)[off] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
                         } else {
                             static_cast<float*>(y)[off] = v;
@@ -111,6 +116,8 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
                     }
                 }
             }
+            // one 32x32 block at a time: keeps the AGPR -> VGPR copies short-lived
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
@@ -133,7 +140,7 @@ __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (
 
 template <int BN, int BM, int kOut, bool kAcc>
 __global__ __launch_bounds__(256) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
-                                                   int per_tensor, const int8_t* __restrict__ wq,
+                                                   int xs_step, const int8_t* __restrict__ wq,
                                                    const float* __restrict__ w_scale, int M, int N, int K,
                                                    void* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
                                                    int tiles_m, int group_m) {
@@ -230,7 +237,10 @@ __global__ __launch_bounds__(256) void k_gemm_ring(const int8_t* __restrict__ xq
 #pragma unroll
         for (int q = 0; q < NRD; ++q) read_frag(0, 0, q, 0);
     }
-    for (int kt = 0; kt < nk; ++kt) {
+    // Steady state (every iteration reads stage kt+1 and copies stage kt+2),
+    // then the last two iterations with those steps switched off.
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) {
         const int buf = kt & 1;
         __builtin_amdgcn_sched_barrier(0);
         kstep(0, true, buf, 1, 1, false, 0);
@@ -240,17 +250,27 @@ __global__ __launch_bounds__(256) void k_gemm_ring(const int8_t* __restrict__ xq
         // barrier); this wavefront's copies of stage kt+1 have landed.
         wait_vmcnt0();
         __syncthreads();
-        kstep(1, kt + 1 < nk, buf ^ 1, 0, 0, kt + 2 < nk, kt + 2);
+        kstep(1, true, buf ^ 1, 0, 0, true, kt + 2);
     }
-    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, per_tensor, w_scale, M, N, y,
+    for (; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        kstep(0, true, buf, 1, 1, false, 0);
+        kstep(1, true, buf, 2, 0, false, 0);
+        kstep(0, true, buf, 3, 1, false, 0);
+        wait_vmcnt0();
+        __syncthreads();
+        kstep(1, kt + 1 < nk, buf ^ 1, 0, 0, false, 0);
+    }
+    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
                                  acc_out);
 }
 
 // ---- generic kernel: any K % 16 == 0 -------------------------------------------
 
-template <int BN, int BM, int kOut /*0: bf16, 1: fp32*/, bool kAcc>
+template <int BN, int BM, int kOut, bool kAcc>
 __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
-                                                      int per_tensor, const int8_t* __restrict__ wq,
+                                                      int xs_step, const int8_t* __restrict__ wq,
                                                       const float* __restrict__ w_scale, int M, int N, int K,
                                                       void* __restrict__ y, int32_t* __restrict__ acc_out,
                                                       int tiles_n, int tiles_m, int group_m) {
@@ -376,7 +396,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__
             rfrag(cur ^ 1, 0, 0);
         }
     }
-    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, per_tensor, w_scale, M, N, y,
+    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
                                  acc_out);
 }
 
@@ -390,21 +410,20 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__
                                 int group_m, hipStream_t st) {                                                     \
         const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;                                        \
         const dim3 grid((unsigned)(tiles_n * tiles_m));                                                            \
-        const int pt = per_tensor ? 1 : 0;                                                                         \
-        if (y_bf16) {                                                                                              \
-            if (acc_out)                                                                                           \
-                hipLaunchKernelGGL((KERNEL<BN, BM, 0, true>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, \
-                                   M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                                \
-            else                                                                                                   \
-                hipLaunchKernelGGL((KERNEL<BN, BM, 0, false>), grid, dim3(256), 0, st, xq, x_scale, pt, wq,        \
-                                   w_scale, M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                       \
-        } else {                                                                                                   \
-            if (acc_out)                                                                                           \
-                hipLaunchKernelGGL((KERNEL<BN, BM, 1, true>), grid, dim3(256), 0, st, xq, x_scale, pt, wq, w_scale, \
-                                   M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                                \
-            else                                                                                                   \
-                hipLaunchKernelGGL((KERNEL<BN, BM, 1, false>), grid, dim3(256), 0, st, xq, x_scale, pt, wq,        \
-                                   w_scale, M, N, K, y, acc_out, tiles_n, tiles_m, group_m);                       \
+        const int step = per_tensor ? 0 : 1; /* x_scale index step */                                              \
+        const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);                                                   \
+        auto go = [&](auto out_c, auto acc_c) {                                                                    \
+            hipLaunchKernelGGL((KERNEL<BN, BM, decltype(out_c)::value, decltype(acc_c)::value>), grid, dim3(256), \
+                               0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n, tiles_m,       \
+                               group_m);                                                                           \
+        };                                                                                                         \
+        using T_ = std::true_type;                                                                                 \
+        using F_ = std::false_type;                                                                                \
+        switch (out) {                                                                                             \
+            case 0: if (acc_out) go(std::integral_constant<int, 0>{}, T_{}); else go(std::integral_constant<int, 0>{}, F_{}); break; \
+            case 1: if (acc_out) go(std::integral_constant<int, 1>{}, T_{}); else go(std::integral_constant<int, 1>{}, F_{}); break; \
+            case 2: if (acc_out) go(std::integral_constant<int, 2>{}, T_{}); else go(std::integral_constant<int, 2>{}, F_{}); break; \
+            default: if (acc_out) go(std::integral_constant<int, 3>{}, T_{}); else go(std::integral_constant<int, 3>{}, F_{}); break; \
         }                                                                                                          \
     }
 
@@ -419,10 +438,11 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
     const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
                       (uint64_t)M * (uint64_t)K < (1ull << 32);
     if (ring) {
-        // 256 x 256 tiles when there are at least two per CU; otherwise
-        // 128 x 128 tiles, two blocks per CU.
+        // 256 x 256 tiles (one block per CU) when there are at least four per
+        // CU; otherwise 128 x 128 tiles, two blocks per CU, whose second
+        // wavefront per SIMD hides the first one's stalls.
         const int64_t big_tiles = ((N + 255) / 256) * (int64_t)((M + 255) / 256);
-        if (big_tiles >= 512)
+        if (big_tiles >= 1024)
             launch_k_gemm_ring<256, 256>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
         else
             launch_k_gemm_ring<128, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
