@@ -81,8 +81,10 @@ CASES = [
     (130, 1024, 257, torch.bfloat16, sq.SQ_PER_TOKEN, 0.6, 1000),
     (520, 512, 130, torch.float32, sq.SQ_PER_TENSOR, 0.5, 64),
     (96, 12288, 200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 300),
-    # enough output tiles for the 256 x 256 GEMM path, ragged in M and N
-    (2100, 256, 16400, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 512),
+    # 128 x 128 GEMM path, ragged M and N, three stages
+    (2100, 384, 3000, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 512),
+    # enough output tiles for the 256 x 256 GEMM path, ragged in M and N, three stages
+    (4100, 384, 16400, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # K a multiple of 16 but not of 128: register-staged GEMM path with a K tail
     (300, 1040, 520, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 300),
 ]
