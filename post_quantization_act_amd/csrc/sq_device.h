@@ -33,9 +33,17 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 // 16-byte global load (one global_load_dwordx4).
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte streaming load: the nontemporal hint marks data read once, which
+// keeps it from displacing reused lines and lifts HBM read throughput.
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+    const v4u_t t = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // Widen the 8 consecutive elements at p (16-byte aligned) to fp32.
 __device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
-    uint4 q = ld16(p);
+    uint4 q = ld16_stream(p);
     v[0] = bf16_lo(q.x); v[1] = bf16_hi(q.x);
     v[2] = bf16_lo(q.y); v[3] = bf16_hi(q.y);
     v[4] = bf16_lo(q.z); v[5] = bf16_hi(q.z);
@@ -43,7 +51,7 @@ __device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
 }
 
 __device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
-    uint4 a = ld16(p), b = ld16(p + 4);
+    uint4 a = ld16_stream(p), b = ld16_stream(p + 4);
     v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
     v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
     v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
