@@ -41,6 +41,15 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Streaming stores (nontemporal hint) for outputs written once.
+__device__ __forceinline__ void st16_stream(void* p, uint4 v) {
+    __builtin_nontemporal_store(v4u_t{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u_t*>(p));
+}
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st8_stream(void* p, uint2 v) {
+    __builtin_nontemporal_store(v2u_t{v.x, v.y}, reinterpret_cast<v2u_t*>(p));
+}
+
 // Widen the 8 consecutive elements at p (16-byte aligned) to fp32.
 __device__ __forceinline__ void load8(const bf16_t* p, float (&v)[8]) {
     uint4 q = ld16_stream(p);
@@ -105,6 +114,13 @@ __device__ __forceinline__ int code8(float v, float r) {
     t = (t == t) ? t : 0.0f;
     t = fminf(fmaxf(t, -127.0f), 127.0f);
     return static_cast<int>(t);
+}
+
+// Same code when r is finite (then v * r is finite and no NaN can arise):
+// one v_med3_f32 clamps.
+__device__ __forceinline__ int code8_finite(float v, float r) {
+    const float t = __builtin_rintf(v * r);
+    return static_cast<int>(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f));
 }
 
 // Pack four codes (low byte first) into one dword.

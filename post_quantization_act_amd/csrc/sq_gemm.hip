@@ -21,6 +21,7 @@
 //    after it the next stage is complete in LDS and the buffer of this stage
 //    is free, so the copy of stage k+2 is issued during k-step 3.
 //  - k_gemm_generic: any K % 16 == 0; register-staged double buffer.
+//  - k_gemm_decode (M <= 16): weight-streaming kernel, see below.
 // Blocks are dealt round-robin to the 8 XCDs; tiles are renumbered so each
 // XCD walks a contiguous run of a grouped (m-major within groups of 8 tile
 // rows) raster and concurrent blocks on one XCD share operand panels in its L2.
@@ -400,6 +401,128 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__
                                  acc_out);
 }
 
+// ---- decode kernel: few tokens, the weight stream is the cost ---------------------
+//
+// For M <= 16 the product is bound by reading Wq once from HBM.  Each block
+// owns 32 output channels; its 4 wavefronts split K into quarters and stream
+// their part of the 32 weight rows straight into MFMA operand registers
+// (v_mfma_i32_16x16x64_i8: A = 16 weight rows x 64 k, B = the 16 token rows x
+// 64 k, read from L2 where the small Xq stays resident).  The four int32
+// partial tiles are summed through LDS, then one wavefront dequantizes.
+// 16x16 accumulator layout: lane l holds D[4*(l/16) + i][l % 16], i = 0..3,
+// i.e. four consecutive output channels n of token m = l % 16.
+template <int kOut, bool kAcc>
+__global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
+                                                     int xs_step, const int8_t* __restrict__ wq,
+                                                     const float* __restrict__ w_scale, int M, int N, int K,
+                                                     void* __restrict__ y, int32_t* __restrict__ acc_out) {
+    constexpr int U = 4;  // k-steps of 64 in flight per wavefront
+    __shared__ v4i part[4][2][kWave];
+    const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const int n0 = blockIdx.x * 32;
+    const int r16 = lane % 16, kc = (lane / 16) * 16;  // operand row and 16-byte k chunk of this lane
+    const int8_t* a0 = wq + (int64_t)min(n0 + r16, N - 1) * K + kc;
+    const int8_t* a1 = wq + (int64_t)min(n0 + 16 + r16, N - 1) * K + kc;
+    const int8_t* bx = xq + (int64_t)min(r16, M - 1) * K + kc;
+    // K split into 4 contiguous ranges of whole 64-byte steps (the last may be partial)
+    const int steps = (K + 63) / 64;
+    const int per = (steps + 3) / 4;
+    const int s0 = wave * per, s1 = min(steps, s0 + per);
+    v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    auto load = [&](const int8_t* p, int k) -> v4i {
+        // chunks at or past K read the row start and are zeroed
+        const bool in = k + kc < K;
+        const uint4 u = in ? ld16_stream(p + k) : make_uint4(0, 0, 0, 0);
+        return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+    };
+    auto loadb = [&](int k) -> v4i {
+        const bool in = k + kc < K;
+        const uint4 u = in ? ld16(bx + k) : make_uint4(0, 0, 0, 0);
+        return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+    };
+    int st = s0;
+    for (; st + U <= s1; st += U) {
+        v4i fa0[U], fa1[U], fb[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int k = (st + u) * 64;
+            fa0[u] = load(a0, k);
+            fa1[u] = load(a1, k);
+            fb[u] = loadb(k);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa0[u], fb[u], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa1[u], fb[u], acc1, 0, 0, 0);
+        }
+    }
+    for (; st < s1; ++st) {
+        const int k = st * 64;
+        const v4i f0 = load(a0, k), f1 = load(a1, k), fb = loadb(k);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(f0, fb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(f1, fb, acc1, 0, 0, 0);
+    }
+    part[wave][0][lane] = acc0;
+    part[wave][1][lane] = acc1;
+    __syncthreads();
+    if (wave != 0) return;
+    const int m = lane % 16;
+    if (m >= M) return;
+    const float xs = x_scale[m * xs_step];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        v4i t = part[0][h][lane];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) t += part[w][h][lane];
+        const int n = n0 + 16 * h + 4 * (lane / 16);
+        if (n >= N) continue;
+        const int64_t off = (int64_t)m * N + n;
+        constexpr int kTy = kOut & 1;
+        if (kOut < 2) {  // N % 4 == 0: four consecutive outputs at once
+            const float4 ws = *reinterpret_cast<const float4*>(w_scale + n);
+            const float y0 = ((float)t[0] * xs) * ws.x, y1 = ((float)t[1] * xs) * ws.y;
+            const float y2 = ((float)t[2] * xs) * ws.z, y3 = ((float)t[3] * xs) * ws.w;
+            if constexpr (kTy == 0)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) =
+                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+            else
+                *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(y0, y1, y2, y3);
+            if constexpr (kAcc) *reinterpret_cast<int4*>(acc_out + off) = make_int4(t[0], t[1], t[2], t[3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (n + e >= N) break;
+                const float v = ((float)t[e] * xs) * w_scale[n + e];
+                if constexpr (kTy == 0)
+                    static_cast<uint16_t*>(y)[off + e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+                else
+                    static_cast<float*>(y)[off + e] = v;
+                if constexpr (kAcc) acc_out[off + e] = t[e];
+            }
+        }
+    }
+}
+
+static void launch_decode(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                          const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
+                          hipStream_t st) {
+    const dim3 grid((unsigned)((N + 31) / 32));
+    const int step = per_tensor ? 0 : 1;
+    const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);
+    auto go = [&](auto out_c, auto acc_c) {
+        hipLaunchKernelGGL((k_gemm_decode<decltype(out_c)::value, decltype(acc_c)::value>), grid, dim3(256), 0, st,
+                           xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    switch (out) {
+        case 0: if (acc_out) go(std::integral_constant<int, 0>{}, T_{}); else go(std::integral_constant<int, 0>{}, F_{}); break;
+        case 1: if (acc_out) go(std::integral_constant<int, 1>{}, T_{}); else go(std::integral_constant<int, 1>{}, F_{}); break;
+        case 2: if (acc_out) go(std::integral_constant<int, 2>{}, T_{}); else go(std::integral_constant<int, 2>{}, F_{}); break;
+        default: if (acc_out) go(std::integral_constant<int, 3>{}, T_{}); else go(std::integral_constant<int, 3>{}, F_{}); break;
+    }
+}
+
 // ---- launchers ---------------------------------------------------------------------
 
 
@@ -435,6 +558,10 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
                             int32_t* acc_out, hipStream_t st) {
     if (M64 <= 0 || N64 <= 0) return hipSuccess;
     const int M = (int)M64, N = (int)N64, K = (int)K64;
+    if (M <= 16 && K > 0) {
+        launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
+        return hipGetLastError();
+    }
     const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
                       (uint64_t)M * (uint64_t)K < (1ull << 32);
     if (ring) {

@@ -69,20 +69,29 @@ __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, i
             }
         }
         float rr_[8];
+        bool finite = true;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) rr_[cc] = r_s[cg * 8 + cc];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int64_t j = j0 + rg * 8 + rr;
-            const float sj = (kScaled && j < K) ? s[j] : 1.0f;
-#pragma unroll
-            for (int cc = 0; cc < 8; ++cc) {
-                const float wp = kScaled ? sj * v[rr][cc] : v[rr][cc];
-                const uint32_t c = uint32_t(code8(wp, rr_[cc])) & 0xFFu;
-                if (rr < 4) lo[cc] |= c << (8 * rr);
-                else hi[cc] |= c << (8 * (rr - 4));
-            }
+        for (int cc = 0; cc < 8; ++cc) {
+            rr_[cc] = r_s[cg * 8 + cc];
+            finite = finite && (rr_[cc] <= 3.402823466e38f);
         }
+        auto code_all = [&](auto fast) {
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const int64_t j = j0 + rg * 8 + rr;
+                const float sj = (kScaled && j < K) ? s[j] : 1.0f;
+#pragma unroll
+                for (int cc = 0; cc < 8; ++cc) {
+                    const float wp = kScaled ? sj * v[rr][cc] : v[rr][cc];
+                    const int code = decltype(fast)::value ? code8_finite(wp, rr_[cc]) : code8(wp, rr_[cc]);
+                    const uint32_t c = uint32_t(code) & 0xFFu;
+                    if (rr < 4) lo[cc] |= c << (8 * rr);
+                    else hi[cc] |= c << (8 * (rr - 4));
+                }
+            }
+        };
+        if (finite) code_all(std::true_type{});
+        else code_all(std::false_type{});
     }
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) {
@@ -185,16 +194,20 @@ __global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int6
         x_scale[0] = scale;
     }
     if (!valid) return;
+    auto code_row = [&](auto fast) {
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-        const int64_t g = t + (int64_t)q * (WPR * kWave);
-        if (g < groups) {
-            uint2 word;
-            word.x = pack4(code8(v[q][0], r), code8(v[q][1], r), code8(v[q][2], r), code8(v[q][3], r));
-            word.y = pack4(code8(v[q][4], r), code8(v[q][5], r), code8(v[q][6], r), code8(v[q][7], r));
-            *reinterpret_cast<uint2*>(xq + row * K + g * 8) = word;
+        for (int q = 0; q < NV; ++q) {
+            const int64_t g = t + (int64_t)q * (WPR * kWave);
+            if (g < groups) {
+                int c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
+                st8_stream(xq + row * K + g * 8, make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+            }
         }
-    }
+    };
+    if (r <= 3.402823466e38f) code_row(std::true_type{});
+    else code_row(std::false_type{});
 }
 
 // Rows longer than the register-resident variants hold (K > 16384): four

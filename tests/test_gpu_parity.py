@@ -85,6 +85,9 @@ CASES = [
     (2100, 384, 3000, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 512),
     # enough output tiles for the 256 x 256 GEMM path, ragged in M and N, three stages
     (4100, 384, 16400, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
+    # decode path (M <= 16): ragged N, K not a multiple of 64, per-tensor scale
+    (16, 1040, 100, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
+    (9, 4096, 4100, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 64),
     # K a multiple of 16 but not of 128: register-staged GEMM path with a K tail
     (300, 1040, 520, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 300),
 ]
