@@ -4,20 +4,32 @@
 One step = the whole path once, on one batch of synthetic input already in
 HBM: calibration absmax over the calibration tokens, smoothing factors,
 smoothed per-output-channel INT8 weights, smoothed per-token INT8
-activations, INT8 GEMM with the dequant epilogue to bf16.  Inputs rotate over
-a pool of independent sets larger than the 256 MB Infinity Cache, so reads
-come from HBM.
+activations, INT8 GEMM with the dequant epilogue to bf16.  The step runs on
+the attention-projection workload (M=2048 tokens, K=4096, N=4096, 8192
+calibration tokens, alpha=0.5, per-token); inputs rotate over a pool of
+independent sets larger than the 256 MB Infinity Cache, so reads come from
+HBM.
 
-Prints ONE JSON line with the whole-step throughput, a per-kernel breakdown,
-the roofline of the dominant kernel (the GEMM) measured with HIP events on the
-stream the library launches on, and a CPU baseline (the oracle timed on a
-bounded sample on the host cores).
+The JSON line carries, besides the whole-step throughput:
+  roofline      the GEMM of the step (its dominant kernel) against the INT8
+                MFMA peak, timed with HIP events on the library's stream;
+  kernels       every stage of the step (HIP events around each call);
+  large         the HBM-bound kernels at the large workload's sizes
+                (M=8192, K=12288, N=49152, 262144 calibration tokens), the
+                GEMM at the MLP (4096x4096x14336) and large shapes, and the
+                decode GEMM's weight-stream rate (16x8192x28672);
+  alpha_sweep   relative Frobenius error of the smoothed and unsmoothed W8A8
+                output (fp32) against X W (fp64) for the large workload's
+                alphas, on a 256-token sample;
+  cpu_baseline  the CPU oracle as it stands, on the host cores, over the same
+                step workload (the GEMM on a row sample when needed).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 2] [--no-cpu]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-large]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +42,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0    # MI355X dense INT8 MFMA, TOPS (5.0 POP/s)
 METRIC = "W8A8 GEMM TOPS (% INT8 MFMA peak); quant-kernel HBM GB/s (% peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_attn_proj_2048x4096x4096_traffic.json")
+GEMM_SOURCES = [os.path.join(ROOT, "post_quantization_act_amd", "csrc", f) for f in ("sq_gemm.hip", "sq_device.h")]
 
 
 def _parse():
@@ -37,18 +51,51 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2, help="workload: 2 = attention projection 2048x4096x4096")
+    p.add_argument("--config", type=int, default=2, help="workload of the step: 2 = attention projection")
     p.add_argument("--pool-gb", type=float, default=1.0, help="rotate inputs over at least this many GB")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-large", action="store_true", help="skip the large-shape kernel table and alpha sweep")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-probe-mb", type=int, default=0,
+                   help="after timing, run one device copy of this size (for counter calibration)")
     return p.parse_args()
 
 
-def _cpu_baseline(cfg, target_s: float):
-    """Time the oracle (as it stands) on the host cores over a bounded sample
-    of the same workload, scaled to whole-step TOPS."""
-    import numpy as np
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
+
+def _traffic():
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when it is missing or was taken on a different GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_baseline(cfg, target_s: float):
+    """The oracle (as it stands) on the host cores over the step workload,
+    scaled to whole-step TOPS; the GEMM runs on a row sample if the full one
+    would exceed the time budget."""
     import oracle
     import synth
 
@@ -70,7 +117,6 @@ def _cpu_baseline(cfg, target_s: float):
     t0 = time.perf_counter()
     xq, xs = oracle.quant_act(x, inv_s, oracle.PER_TOKEN)
     t["quant_act"] = time.perf_counter() - t0
-    # GEMM: a probe on a few rows sizes the sample so it takes ~target_s.
     probe = max(1, min(M, 8))
     t0 = time.perf_counter()
     oracle.gemm_i8(xq[:probe], wq, nthreads=min(cores, probe))
@@ -90,21 +136,125 @@ def _cpu_baseline(cfg, target_s: float):
     return {
         "value": ops / total / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
         "sample": (f"all five oracle steps on the full {M}x{K}x{N} workload ({cfg.calib_tokens} calibration "
-                   f"tokens), except the GEMM + dequant, timed on {rows} of {M} token rows and scaled by "
-                   f"{M / rows:.2f}; GEMM on {cores} threads, other steps single-threaded"),
+                   f"tokens); the GEMM + dequant timed on {rows} of {M} token rows and scaled by {M / rows:.2f}; "
+                   f"GEMM on {cores} threads, other steps single-threaded"),
         "seconds_per_step": total, "stage_seconds": {k: round(v, 4) for k, v in t.items()},
         "cpu_model": _cpu_model(),
     }
 
 
-def _cpu_model():
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
+class _Timer:
+    """Average duration of a call, from HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, reps=5, warm=1):
+        torch = self.torch
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for i, (a, b) in enumerate(evs):
+            a.record(s)
+            fn(warm + i)
+            b.record(s)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3  # us
+
+
+def _large(torch, sq, synth, pipeline, dev):
+    """HBM-bound kernels at the large workload's sizes, GEMMs at the MLP and
+    large shapes, the decode weight stream, and the alpha sweep."""
+    tm = _Timer(torch)
+    out = {}
+    cfg = synth.CONFIGS[5]
+    M, K, N, T = cfg.M, cfg.K, cfg.N, cfg.calib_tokens
+    print(f"# large: drawing {cfg.name} ({T} calibration tokens)", file=sys.stderr, flush=True)
+    inp = synth.make(cfg, device=dev)
+    b = pipeline.W8A8Buffers.allocate(M, N, K, sq.SQ_PER_TOKEN, dev)
+    torch.cuda.synchronize()
+
+    def rate(us, byts):
+        gbs = byts / (us * 1e-6) / 1e9
+        return {"us": round(us, 1), "alg_bytes": int(byts), "GB_s": round(gbs, 1),
+                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+
+    def calib(i):
+        b.amax_x.zero_()
+        sq.sq_calib_absmax(inp.calib, b.amax_x)
+
+    us_zero = tm(lambda i: b.amax_x.zero_(), reps=5)
+    us = tm(calib, reps=3) - us_zero
+    out["calib_absmax"] = rate(us, 2 * T * K + 8 * K)
+    out["smooth_factors"] = rate(tm(lambda i: sq.sq_smooth_factors(b.amax_x, inp.w, 0.5, b.s, b.inv_s, b.amax_w),
+                                    reps=3), 2 * K * N + 12 * K)
+    out["quant_weight_call"] = rate(tm(lambda i: sq.sq_quant_weight(inp.w, b.s, b.wq, b.w_scale, b.ws_w), reps=3),
+                                    3 * K * N + 4 * N + 4 * K)
+    out["quant_weight_call"]["note"] = ("algorithmic 3 B/element; the call moves 5 (column-max pass reads W, the "
+                                        "coding pass reads W and writes the codes)")
+    out["quant_act"] = rate(tm(lambda i: sq.sq_quant_act(inp.x, b.inv_s, sq.SQ_PER_TOKEN, b.xq, b.x_scale), reps=5),
+                            3 * M * K + 4 * M + 4 * K)
+    us = tm(lambda i: sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y), reps=3)
+    ops = 2.0 * M * N * K
+    out["gemm_8192x12288x49152"] = {"us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
+                                    "pct_int8_peak": round(100 * ops / us / 1e6 / INT8_PEAK_TOPS, 1)}
+
+    # alpha sweep on a 256-token sample, fp32 output, error against fp64 X W
+    rows = torch.arange(0, M, M // 256, device=dev)[:256]
+    xs_ = inp.x[rows].contiguous()
+    y_ref = xs_.double() @ inp.w.double()
+    ref_norm = float(torch.linalg.norm(y_ref))
+    bs = pipeline.W8A8Buffers.allocate(256, N, K, sq.SQ_PER_TOKEN, dev, y_dtype=torch.float32)
+    bs.amax_x.copy_(b.amax_x)
+    sweep = {}
+    for a in cfg.alphas:
+        sq.sq_smooth_factors(bs.amax_x, None, a, bs.s, bs.inv_s, b.amax_w)
+        sq.sq_quant_weight(inp.w, bs.s, bs.wq, bs.w_scale, bs.ws_w)
+        pipeline.forward(xs_, sq.SQ_PER_TOKEN, bs, smoothed=True)
+        err = float(torch.linalg.norm(bs.y.double() - y_ref)) / ref_norm
+        sweep[str(a)] = round(err, 6)
+    sq.sq_quant_weight(inp.w, None, bs.wq, bs.w_scale, bs.ws_w)
+    pipeline.forward(xs_, sq.SQ_PER_TOKEN, bs, smoothed=False)
+    base_tok = float(torch.linalg.norm(bs.y.double() - y_ref)) / ref_norm
+    bt = pipeline.W8A8Buffers.allocate(256, N, K, sq.SQ_PER_TENSOR, dev, y_dtype=torch.float32)
+    sq.sq_quant_weight(inp.w, None, bt.wq, bt.w_scale, bt.ws_w)
+    pipeline.forward(xs_, sq.SQ_PER_TENSOR, bt, smoothed=False)
+    base_ten = float(torch.linalg.norm(bt.y.double() - y_ref)) / ref_norm
+    out_sweep = {"workload": cfg.name, "sample_tokens": 256, "output": "fp32", "reference": "X W in fp64",
+                 "metric": "relative Frobenius error", "smoothed_per_token": sweep,
+                 "unsmoothed_per_token": round(base_tok, 6), "unsmoothed_per_tensor": round(base_ten, 6)}
+    del inp, b, bs, bt, y_ref
+    torch.cuda.empty_cache()
+
+    # MLP shape GEMM (operands rotate over 3 sets: 3 x 75 MB)
+    M3, K3, N3 = 4096, 4096, 14336
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    xq3 = [torch.randint(-127, 128, (M3, K3), dtype=torch.int8, device=dev, generator=g) for _ in range(3)]
+    wq3 = [torch.randint(-127, 128, (N3, K3), dtype=torch.int8, device=dev, generator=g) for _ in range(3)]
+    xs3 = torch.rand(M3, device=dev, generator=g) * 0.01
+    ws3 = torch.rand(N3, device=dev, generator=g) * 0.01
+    y3 = torch.empty(M3, N3, dtype=torch.bfloat16, device=dev)
+    us = tm(lambda i: sq.sq_gemm_w8a8(xq3[i % 3], xs3, sq.SQ_PER_TOKEN, wq3[i % 3], ws3, y3), reps=6)
+    ops = 2.0 * M3 * N3 * K3
+    out["gemm_4096x4096x14336"] = {"us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
+                                   "pct_int8_peak": round(100 * ops / us / 1e6 / INT8_PEAK_TOPS, 1)}
+    del xq3, wq3, y3
+    # decode GEMM: the weight stream (235 MB) rotates over 2 copies (> MALL)
+    M4, K4, N4 = 16, 8192, 28672
+    xq4 = torch.randint(-127, 128, (M4, K4), dtype=torch.int8, device=dev, generator=g)
+    wq4 = [torch.randint(-127, 128, (N4, K4), dtype=torch.int8, device=dev, generator=g) for _ in range(2)]
+    xs4 = torch.rand(M4, device=dev, generator=g) * 0.01
+    ws4 = torch.rand(N4, device=dev, generator=g) * 0.01
+    y4 = torch.empty(M4, N4, dtype=torch.bfloat16, device=dev)
+    us = tm(lambda i: sq.sq_gemm_w8a8(xq4, xs4, sq.SQ_PER_TOKEN, wq4[i % 2], ws4, y4), reps=10)
+    out["gemm_decode_16x8192x28672"] = rate(us, N4 * K4 + M4 * K4 + 2 * M4 * N4 + 4 * (M4 + N4))
+    out["gemm_decode_16x8192x28672"]["note"] = "weight-stream bound: 235 MB of int8 weights per launch"
+    del xq4, wq4, y4
+    torch.cuda.empty_cache()
+    return out, out_sweep
 
 
 def main():
@@ -175,6 +325,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
 
     per = {name: [] for name in stages}
     for ev in events:
@@ -199,8 +350,25 @@ def main():
     gemm_tops = ops / (avg_us["gemm_w8a8"] * 1e-6) / 1e12
     kernels["gemm_w8a8"].update({"ops": ops, "TOPS": round(gemm_tops, 1),
                                  "pct_int8_peak": round(100 * gemm_tops / INT8_PEAK_TOPS, 1)})
+    kernels["note"] = ("HIP-event intervals per call: calib_absmax includes zeroing the running max; "
+                       "quant_weight is three launches (clear, column max, coding)")
+
+    if args.copy_probe_mb > 0:
+        # a plain copy of known size whose source is not cache resident: 1 GiB
+        # is written between filling the source and copying it
+        nb = args.copy_probe_mb << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src.fill_(1)
+        flush.fill_(2)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst, flush
 
     value = ops / (ms_per_step * 1e-3) / 1e12
+    traffic = _traffic()
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -209,13 +377,18 @@ def main():
                    "act_granularity": cfg.gran, "weight_granularity": "per_output_channel",
                    "input_dtype": cfg.x_dtype, "output_dtype": "bf16", "input_pool_sets": pool,
                    "value_definition": "2*M*N*K of the GEMM / wall time of one whole five-step pass"},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_w8a8", "achieved": round(gemm_tops, 1),
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_ring<128,128>", "achieved": round(gemm_tops, 1),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": None, "launch_us": round(avg_us["gemm_w8a8"], 2),
-                     "alg_ops_per_launch": ops},
+                     "traffic": traffic, "launch_us": round(avg_us["gemm_w8a8"], 2), "alg_ops_per_launch": ops,
+                     "gemm_source_sha256_16": gemm_source_hash()},
         "kernels": kernels,
     }
+    if not args.no_large:
+        del sets
+        torch.cuda.empty_cache()
+        out["large"], out["alpha_sweep"] = _large(torch, sq, synth, pipeline, dev)
     if not args.no_cpu:
+        print("# CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = _cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
