@@ -199,7 +199,8 @@ def _large(torch, sq, synth, pipeline, dev):
     us = tm(lambda i: sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y), reps=3)
     ops = 2.0 * M * N * K
     out["gemm_8192x12288x49152"] = {"us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
-                                    "pct_int8_peak": round(100 * ops / us / 1e6 / INT8_PEAK_TOPS, 1)}
+                                    "pct_int8_peak": round(100 * ops / us / 1e6 / INT8_PEAK_TOPS, 1),
+                                    "kernel": sq.sq_gemm_kernel_name(M, N, K)}
 
     # alpha sweep on a 256-token sample, fp32 output, error against fp64 X W
     rows = torch.arange(0, M, M // 256, device=dev)[:256]
@@ -240,7 +241,8 @@ def _large(torch, sq, synth, pipeline, dev):
     us = tm(lambda i: sq.sq_gemm_w8a8(xq3[i % 3], xs3, sq.SQ_PER_TOKEN, wq3[i % 3], ws3, y3), reps=6)
     ops = 2.0 * M3 * N3 * K3
     out["gemm_4096x4096x14336"] = {"us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
-                                   "pct_int8_peak": round(100 * ops / us / 1e6 / INT8_PEAK_TOPS, 1)}
+                                   "pct_int8_peak": round(100 * ops / us / 1e6 / INT8_PEAK_TOPS, 1),
+                                   "kernel": sq.sq_gemm_kernel_name(M3, N3, K3)}
     del xq3, wq3, y3
     # decode GEMM: the weight stream (235 MB) rotates over 2 copies (> MALL)
     M4, K4, N4 = 16, 8192, 28672
@@ -252,6 +254,7 @@ def _large(torch, sq, synth, pipeline, dev):
     us = tm(lambda i: sq.sq_gemm_w8a8(xq4, xs4, sq.SQ_PER_TOKEN, wq4[i % 2], ws4, y4), reps=10)
     out["gemm_decode_16x8192x28672"] = rate(us, N4 * K4 + M4 * K4 + 2 * M4 * N4 + 4 * (M4 + N4))
     out["gemm_decode_16x8192x28672"]["note"] = "weight-stream bound: 235 MB of int8 weights per launch"
+    out["gemm_decode_16x8192x28672"]["kernel"] = sq.sq_gemm_kernel_name(M4, N4, K4)
     del xq4, wq4, y4
     torch.cuda.empty_cache()
     return out, out_sweep
@@ -377,7 +380,7 @@ def main():
                    "act_granularity": cfg.gran, "weight_granularity": "per_output_channel",
                    "input_dtype": cfg.x_dtype, "output_dtype": "bf16", "input_pool_sets": pool,
                    "value_definition": "2*M*N*K of the GEMM / wall time of one whole five-step pass"},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_ring<128,128>", "achieved": round(gemm_tops, 1),
+        "roofline": {"bound": "mfma", "kernel": sq.sq_gemm_kernel_name(M, N, K), "achieved": round(gemm_tops, 1),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
                      "traffic": traffic, "launch_us": round(avg_us["gemm_w8a8"], 2), "alg_ops_per_launch": ops,
                      "gemm_source_sha256_16": gemm_source_hash()},

@@ -20,7 +20,7 @@ __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
     "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
-    "sq_gemm_w8a8", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "EXPORTED_SYMBOLS",
+    "sq_gemm_w8a8", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,7 @@ SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, S
 
 EXPORTED_SYMBOLS = (
     "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
-    "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version",
+    "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
 )
 
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
     L.sq_last_error.restype = ctypes.c_char_p
     L.sq_version.argtypes = []
     L.sq_version.restype = ctypes.c_char_p
+    L.sq_gemm_kernel_name.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    L.sq_gemm_kernel_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -88,6 +90,11 @@ def sq_last_error() -> str:
 
 def sq_version() -> str:
     return lib().sq_version().decode()
+
+
+def sq_gemm_kernel_name(M: int, N: int, K: int) -> str:
+    """Which GEMM kernel sq_gemm_w8a8 launches for an M x N x K product."""
+    return lib().sq_gemm_kernel_name(int(M), int(N), int(K)).decode()
 
 
 def sq_workspace_size(op: int, M: int, N: int, K: int, gran: int = SQ_PER_TOKEN) -> int:

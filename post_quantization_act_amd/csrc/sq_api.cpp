@@ -95,6 +95,8 @@ extern "C" {
 
 const char* sq_version(void) { return "0.1.0"; }
 
+const char* sq_gemm_kernel_name(int64_t M, int64_t N, int64_t K) { return sqk::gemm_kernel_name(M, N, K); }
+
 const char* sq_last_error(void) { return g_last_error.c_str(); }
 
 const char* sq_status_str(sq_status s) {

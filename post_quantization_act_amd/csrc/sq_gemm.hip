@@ -11,8 +11,10 @@
 //
 // Two kernels:
 //  - k_gemm_ring (K % 128 == 0, operands below 4 GiB): block tile BN x BM,
-//    4 wavefronts in a 2 x 2 grid, each owning (BN/2) x (BM/2) of 32 x 32 MFMA
-//    blocks.  Operand tiles of 128 bytes of k per row ("stages") are copied
+//    8 wavefronts in a WGN x WGM grid (two per SIMD, so one wavefront's
+//    LDS and barrier waits are covered by the other's MFMAs), each owning
+//    (BN/WGN) x (BM/WGM) of 32 x 32 MFMA blocks with its accumulators in
+//    VGPRs.  Operand tiles of 128 bytes of k per row ("stages") are copied
 //    from global memory straight into a two-buffer LDS ring with
 //    global_load_lds_dwordx4, so no registers stage them and each row request
 //    is one full 128-byte line.  Each stage is four k-steps of 32; fragments
@@ -139,39 +141,40 @@ __device__ __forceinline__ void copy16_to_lds(const int8_t* base, uint32_t voff,
 
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
 
-template <int BN, int BM, int kOut, bool kAcc>
-__global__ __launch_bounds__(256) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
+template <int BN, int BM, int WGN, int WGM, int kOut, bool kAcc>
+__global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
                                                    int xs_step, const int8_t* __restrict__ wq,
                                                    const float* __restrict__ w_scale, int M, int N, int K,
                                                    void* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
                                                    int tiles_m, int group_m) {
-    constexpr int WN = BN / 2, WM = BM / 2, TN = WN / 32, TM = WM / 32;
+    constexpr int NW = WGN * WGM;             // wavefronts per block
+    constexpr int WN = BN / WGN, WM = BM / WGM, TN = WN / 32, TM = WM / 32;
     constexpr int ROWS = BN + BM;             // rows of a stage: Wq tile rows, then Xq tile rows
     constexpr int STAGE = ROWS * 8;           // 16-byte slots per stage
     constexpr int COPIES = ROWS / 8;          // 1-KB copies per stage (8 rows each)
-    constexpr int L = COPIES / 4;             // copies per wavefront per stage
+    constexpr int L = COPIES / NW;            // copies per wavefront per stage
     constexpr int NMF = TN * TM;              // MFMAs per k-step
     constexpr int NRD = TN + TM;              // fragment reads per k-step
     constexpr int DR = (NRD + NMF - 1) / NMF, DD = (L + NMF - 1) / NMF;
-    static_assert(COPIES % 4 == 0 && BN % 8 == 0, "tile");
+    static_assert(COPIES % NW == 0 && BN % 8 == 0 && WN % 32 == 0 && WM % 32 == 0, "tile");
     static_assert(2 * STAGE * 16 <= 160 * 1024, "LDS");
     __shared__ uint4 lds[2 * STAGE];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int wn = wave % 2, wm = wave / 2;
+    const int wn = wave % WGN, wm = wave / WGN;
     int tn, tm;
     tile_of_block(tiles_n, tiles_m, group_m, tn, tm);
     const int n0 = tn * BN, m0 = tm * BM;
 
-    // Copy j of this wavefront (global copy index i = wave + 4j) fills rows
+    // Copy j of this wavefront (global copy index i = wave + NW j) fills rows
     // 8i .. 8i+7 of a stage: lane -> row 8i + lane/8 and LDS chunk lane%8,
     // which holds logical chunk (lane%8) ^ ((row >> 1) & 7).  Rows past the
     // matrix edge are clamped to the last row (read, never stored).
     uint32_t off[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        const int i = wave + 4 * j;
+        const int i = wave + NW * j;
         const int r = 8 * i + lane / 8;
         const int c = (lane % 8) ^ ((r >> 1) & 7);
         if (r < BN) off[j] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c * 16;
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(256) void k_gemm_ring(const int8_t* __restrict__ xq
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
     auto copy = [&](int kt, int j) {
-        const int i = wave + 4 * j;
+        const int i = wave + NW * j;
         const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + ((kt & 1) * STAGE + i * 64) * 16);
         copy16_to_lds(8 * i < BN ? wq : xq, off[j] + (uint32_t)kt * kBK, la);
     };
@@ -550,31 +553,77 @@ static void launch_decode(const int8_t* xq, const float* x_scale, bool per_tenso
         }                                                                                                          \
     }
 
-SQ_DEFINE_LAUNCH(k_gemm_ring)
 SQ_DEFINE_LAUNCH(k_gemm_generic)
+
+template <int BN, int BM, int WGN, int WGM>
+static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                        const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
+                        int group_m, hipStream_t st) {
+    const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+    const dim3 grid((unsigned)(tiles_n * tiles_m));
+    const int step = per_tensor ? 0 : 1;
+    const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);
+    auto go = [&](auto out_c, auto acc_c) {
+        hipLaunchKernelGGL((k_gemm_ring<BN, BM, WGN, WGM, decltype(out_c)::value, decltype(acc_c)::value>), grid,
+                           dim3(64 * WGN * WGM), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n,
+                           tiles_m, group_m);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    switch (out) {
+        case 0: if (acc_out) go(std::integral_constant<int, 0>{}, T_{}); else go(std::integral_constant<int, 0>{}, F_{}); break;
+        case 1: if (acc_out) go(std::integral_constant<int, 1>{}, T_{}); else go(std::integral_constant<int, 1>{}, F_{}); break;
+        case 2: if (acc_out) go(std::integral_constant<int, 2>{}, T_{}); else go(std::integral_constant<int, 2>{}, F_{}); break;
+        default: if (acc_out) go(std::integral_constant<int, 3>{}, T_{}); else go(std::integral_constant<int, 3>{}, F_{}); break;
+    }
+}
+
+// Which kernel a product of this shape runs (the one rule both the launcher
+// and gemm_kernel_name use).
+enum class GemmPath { kNone, kDecode, kRing256, kRing128, kGeneric };
+
+static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
+    if (M <= 0 || N <= 0) return GemmPath::kNone;
+    if (M <= 16 && K > 0) return GemmPath::kDecode;
+    const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
+                      (uint64_t)M * (uint64_t)K < (1ull << 32);
+    if (!ring) return GemmPath::kGeneric;
+    // 256 x 256 tiles (one block per CU, 128 KB LDS ring) when there are at
+    // least two per CU; otherwise 128 x 128 tiles (two blocks per CU), whose
+    // shorter per-block latency chain wins on smaller problems.
+    const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
+    return t256 >= 512 ? GemmPath::kRing256 : GemmPath::kRing128;
+}
+
+const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
+    switch (gemm_path(M, N, K)) {
+        case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
+        case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2> (256x256 tile, 8 wavefronts of 64x128)";
+        case GemmPath::kRing128: return "k_gemm_ring<128,128,2,4> (128x128 tile, 8 wavefronts of 64x32)";
+        case GemmPath::kGeneric: return "k_gemm_generic<256,128> (register-staged, any K % 16 == 0)";
+        default: return "none (empty product)";
+    }
+}
 
 hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
                             const float* w_scale, int64_t M64, int64_t N64, int64_t K64, void* y, bool y_bf16,
                             int32_t* acc_out, hipStream_t st) {
-    if (M64 <= 0 || N64 <= 0) return hipSuccess;
     const int M = (int)M64, N = (int)N64, K = (int)K64;
-    if (M <= 16 && K > 0) {
-        launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
-        return hipGetLastError();
-    }
-    const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
-                      (uint64_t)M * (uint64_t)K < (1ull << 32);
-    if (ring) {
-        // 256 x 256 tiles (one block per CU) when there are at least four per
-        // CU; otherwise 128 x 128 tiles, two blocks per CU, whose second
-        // wavefront per SIMD hides the first one's stalls.
-        const int64_t big_tiles = ((N + 255) / 256) * (int64_t)((M + 255) / 256);
-        if (big_tiles >= 1024)
-            launch_k_gemm_ring<256, 256>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
-        else
-            launch_k_gemm_ring<128, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
-    } else {
-        launch_k_gemm_generic<256, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+    switch (gemm_path(M64, N64, K64)) {
+        case GemmPath::kNone: return hipSuccess;
+        case GemmPath::kDecode:
+            launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
+            break;
+        case GemmPath::kRing256:
+            launch_ring<256, 256, 4, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 4, st);
+            break;
+        case GemmPath::kRing128:
+            launch_ring<128, 128, 2, 4>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+            break;
+        case GemmPath::kGeneric:
+            launch_k_gemm_generic<256, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8,
+                                            st);
+            break;
     }
     return hipGetLastError();
 }

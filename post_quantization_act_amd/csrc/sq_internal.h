@@ -37,4 +37,7 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
                             const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16,
                             int32_t* acc_out, hipStream_t st);
 
+// Static description of the GEMM kernel launch_gemm_w8a8 runs for this shape.
+const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K);
+
 }  // namespace sqk

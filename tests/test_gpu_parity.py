@@ -83,8 +83,10 @@ CASES = [
     (96, 12288, 200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 300),
     # 128 x 128 GEMM path, ragged M and N, three stages
     (2100, 384, 3000, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 512),
-    # enough output tiles for the 256 x 256 GEMM path, ragged in M and N, three stages
-    (4100, 384, 16400, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
+    # 128 x 128 GEMM path, ragged M, N % 4 != 0 (element-wise output stores), three stages
+    (2000, 384, 3998, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
+    # enough output tiles for the 256 x 256 GEMM path, ragged M, N % 4 != 0, three stages
+    (4100, 384, 16398, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # decode path (M <= 16): ragged N, K not a multiple of 64, per-tensor scale
     (16, 1040, 100, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     (9, 4096, 4100, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 64),
