@@ -198,7 +198,8 @@ const char *sq_version(void);
 
 /* Static description of the kernel sq_gemm_w8a8 launches for an M x N x K
  * product (tile shape and wavefront layout), for profiling and reports.
- * Pure host function: touches no device and never fails. */
+ * Host function: enqueues nothing; it may query the current device's compute
+ * unit count (the decode kernel's grid depends on it).  Never fails. */
 const char *sq_gemm_kernel_name(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

@@ -27,6 +27,7 @@
 // Blocks are dealt round-robin to the 8 XCDs; tiles are renumbered so each
 // XCD walks a contiguous run of a grouped (m-major within groups of 8 tile
 // rows) raster and concurrent blocks on one XCD share operand panels in its L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "sq_device.h"
@@ -506,6 +507,213 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
     }
 }
 
+// ---- decode kernel, LDS-ring variant (K % 2048 == 0, K <= 16384) ------------------
+//
+// Same product as k_gemm_decode, streamed so that every load instruction reads
+// whole 128-byte lines: one block of 16 wavefronts per CU; wavefront w owns the
+// k-bytes [w K/16, (w+1) K/16), i.e. SPW stages of 128 bytes, and keeps the
+// token operand of that range in registers for the whole kernel.  Work items
+// are groups of 16 output channels, dealt round-robin to the blocks.  A stage
+// is 16 weight rows x 128 bytes, copied by two global_load_lds_dwordx4 (8 rows
+// x 128 bytes each, nontemporal: the stream is read once) into the
+// wavefront's own three-stage LDS ring; chunk c of row r sits at slot
+// 8 r + (c ^ ((r >> 1) & 7)), so the MFMA fragment reads are conflict-free.
+// No workgroup barrier guards the rings (each is private to a wavefront);
+// only explicit vmcnt waits do, and no other vector-memory instruction runs
+// during the stream: scales are staged in LDS first, the 16 partial tiles of
+// a group are summed through LDS and kept there as int32, and the epilogue
+// and all stores run after the last stage.
+constexpr int kDrWaves = 16, kDrStages = 3, kDrStageBytes = 128, kDrMaxGroups = 24;
+
+__device__ __forceinline__ void copy16_to_lds_nt(const int8_t* base, uint32_t voff, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                 :
+                 : "s"(lds_off), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+// vmcnt wait and LDS-only barrier as asm with a memory clobber, so that no LDS
+// read of copied data is moved above them.
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int SPW>
+__global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
+    const int8_t* __restrict__ xq, const float* __restrict__ x_scale, int xs_step, const int8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int M, int N, int K, void* __restrict__ y, bool y_bf16,
+    int32_t* __restrict__ acc_out) {
+    constexpr int NW = kDrWaves, NST = kDrStages, SB = kDrStageBytes;
+    constexpr int CPR = SB / 16;     // 16-byte chunks per row per stage (8)
+    constexpr int SLOTS = 16 * CPR;  // 16-byte slots per stage
+    constexpr int NCP = SB / 64;     // copies per stage (2), 8 rows each
+    constexpr int RPC = 1024 / SB;   // rows per copy
+    constexpr int KS = SB / 64;      // MFMA k-steps per stage
+    __shared__ uint4 ring_all[NW * NST * SLOTS];
+    __shared__ v4i part[NW * 64];
+    __shared__ v4i sums[kDrMaxGroups * 64];
+    __shared__ __align__(16) float wsl[kDrMaxGroups * 16];
+    __shared__ float xsl[16];
+    auto h = [](int r) { return (r >> 1) & 7; };
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int G = (N + 15) / 16;
+    const int ngroups = (G - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int kw = wave * (K / NW);
+
+    // token operand: lane l holds token l % 16, 16-byte chunk l / 16 of each 64-byte k-step
+    v4i xb[SPW][KS];
+    {
+        const int8_t* xr = xq + (int64_t)min(lane % 16, M - 1) * K + kw + 16 * (lane / 16);
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint4 u = ld16(xr + sp * SB + s * 64);
+                xb[sp][s] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+            }
+        // consume them here so the compiler's own waits for these loads come
+        // before the stream and never inside it
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(xb[sp][s]));
+    }
+    for (int i = threadIdx.x; i < ngroups * 16; i += 64 * NW) {
+        const int g = (int)blockIdx.x + (i / 16) * (int)gridDim.x;
+        wsl[i] = w_scale[min(16 * g + i % 16, N - 1)];
+    }
+    if (threadIdx.x < 16) xsl[threadIdx.x] = x_scale[min((int)threadIdx.x, M - 1) * xs_step];
+
+    const uint32_t ring = (uint32_t)(uintptr_t)(lds_char*)(ring_all + wave * NST * SLOTS);
+    const int rr = lane / CPR, cl = lane % CPR;
+    const int T = ngroups * SPW;  // stages of this wavefront
+    auto issue = [&](int t) {
+        const int gi = t / SPW, sp = t % SPW;
+        const int g = (int)blockIdx.x + gi * (int)gridDim.x;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(ring + (uint32_t)((t % NST) * SLOTS * 16));
+#pragma unroll
+        for (int i = 0; i < NCP; ++i) {
+            const int r = RPC * i + rr;
+            const int n = min(16 * g + r, N - 1);
+            const uint32_t off = (uint32_t)n * (uint32_t)K + (uint32_t)(kw + sp * SB + 16 * (cl ^ h(r)));
+            copy16_to_lds_nt(wq, off, la + i * 1024);
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NST - 1; ++t)
+        if (t < T) issue(t);
+    wait_vmcnt<0>();
+
+    v4i acc = {0, 0, 0, 0};
+    const int fr = lane % 16, fc = lane / 16;
+    for (int gi = 0; gi < ngroups; ++gi) {
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp) {
+            const int t = gi * SPW + sp;
+            if (t + NST - 1 < T) {
+                issue(t + NST - 1);
+                wait_vmcnt<NCP*(NST - 1)>();  // stage t has landed; the later ones stay in flight
+            } else {
+                wait_vmcnt<0>();
+            }
+            const uint4* st = ring_all + wave * NST * SLOTS + (t % NST) * SLOTS;
+            v4i fa[KS];
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint4 u = st[CPR * fr + ((4 * s + fc) ^ h(fr))];
+                fa[s] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+            }
+#pragma unroll
+            for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[s], xb[sp][s], acc, 0, 0, 0);
+        }
+        // group done: the 16 partial tiles are summed by one wavefront
+        part[wave * 64 + lane] = acc;
+        acc = v4i{0, 0, 0, 0};
+        lds_barrier();
+        if (wave == (gi % NW)) {
+            v4i sum = part[lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) sum += part[w * 64 + lane];
+            sums[gi * 64 + lane] = sum;
+        }
+        lds_barrier();  // part is reused by the next group
+    }
+
+    // epilogue: 16x16 accumulator layout, lane l holds channels 4 (l / 16) + e of token l % 16
+    for (int idx = threadIdx.x; idx < ngroups * 64; idx += 64 * NW) {
+        const int gi = idx / 64, l = idx % 64;
+        const int g = (int)blockIdx.x + gi * (int)gridDim.x;
+        const int m = l % 16, n = 16 * g + 4 * (l / 16);
+        if (m >= M || n >= N) continue;
+        const v4i sum = sums[idx];
+        const float xs = xsl[m];
+        const float* ws = wsl + gi * 16 + 4 * (l / 16);
+        const int64_t off = (int64_t)m * N + n;
+        if (n + 3 < N && N % 4 == 0) {
+            const float y0 = ((float)sum[0] * xs) * ws[0], y1 = ((float)sum[1] * xs) * ws[1];
+            const float y2 = ((float)sum[2] * xs) * ws[2], y3 = ((float)sum[3] * xs) * ws[3];
+            if (y_bf16)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) =
+                    make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+            else
+                *reinterpret_cast<float4*>(static_cast<float*>(y) + off) = make_float4(y0, y1, y2, y3);
+            if (acc_out) *reinterpret_cast<int4*>(acc_out + off) = make_int4(sum[0], sum[1], sum[2], sum[3]);
+        } else {
+            for (int e = 0; e < 4 && n + e < N; ++e) {
+                const float v = ((float)sum[e] * xs) * ws[e];
+                if (y_bf16)
+                    static_cast<uint16_t*>(y)[off + e] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
+                else
+                    static_cast<float*>(y)[off + e] = v;
+                if (acc_out) acc_out[off + e] = sum[e];
+            }
+        }
+    }
+}
+
+static int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+static bool decode_ring_fits(int64_t M, int64_t N, int64_t K) {
+    if (M > 16 || K < 2048 || K % 2048 != 0 || K > 16384 || (uint64_t)N * (uint64_t)K >= (1ull << 32)) return false;
+    const int64_t G = (N + 15) / 16;
+    const int64_t grid = std::min<int64_t>(device_cu_count(), G);
+    return (G + grid - 1) / grid <= kDrMaxGroups;
+}
+
+static void launch_decode_ring(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                               const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
+                               hipStream_t st) {
+    const int G = (N + 15) / 16;
+    const dim3 grid((unsigned)std::min(device_cu_count(), G));
+    const int step = per_tensor ? 0 : 1;
+#define SQ_DR(S)                                                                                                   \
+    hipLaunchKernelGGL((k_gemm_decode_ring<S>), grid, dim3(64 * kDrWaves), 0, st, xq, x_scale, step, wq, w_scale, M, \
+                       N, K, y, y_bf16, acc_out)
+    switch (K / 2048) {
+        case 1: SQ_DR(1); break;
+        case 2: SQ_DR(2); break;
+        case 3: SQ_DR(3); break;
+        case 4: SQ_DR(4); break;
+        case 5: SQ_DR(5); break;
+        case 6: SQ_DR(6); break;
+        case 7: SQ_DR(7); break;
+        default: SQ_DR(8); break;
+    }
+#undef SQ_DR
+}
+
 static void launch_decode(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
                           const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
                           hipStream_t st) {
@@ -580,11 +788,11 @@ static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor,
 
 // Which kernel a product of this shape runs (the one rule both the launcher
 // and gemm_kernel_name use).
-enum class GemmPath { kNone, kDecode, kRing256, kRing128, kGeneric };
+enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing128, kGeneric };
 
 static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0) return GemmPath::kNone;
-    if (M <= 16 && K > 0) return GemmPath::kDecode;
+    if (M <= 16 && K > 0) return decode_ring_fits(M, N, K) ? GemmPath::kDecodeRing : GemmPath::kDecode;
     const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
                       (uint64_t)M * (uint64_t)K < (1ull << 32);
     if (!ring) return GemmPath::kGeneric;
@@ -597,6 +805,8 @@ static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
 
 const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
     switch (gemm_path(M, N, K)) {
+        case GemmPath::kDecodeRing:
+            return "k_gemm_decode_ring (one block of 16 wavefronts per CU, per-wavefront LDS rings of 128-byte stages)";
         case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
         case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2> (256x256 tile, 8 wavefronts of 64x128)";
         case GemmPath::kRing128: return "k_gemm_ring<128,128,2,4> (128x128 tile, 8 wavefronts of 64x32)";
@@ -611,6 +821,9 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
     const int M = (int)M64, N = (int)N64, K = (int)K64;
     switch (gemm_path(M64, N64, K64)) {
         case GemmPath::kNone: return hipSuccess;
+        case GemmPath::kDecodeRing:
+            launch_decode_ring(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
+            break;
         case GemmPath::kDecode:
             launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
             break;

@@ -45,7 +45,8 @@ def test_gemm_kernel_choice():
     """The shape rule of the GEMM dispatch: decode kernel for M <= 16, the LDS
     ring kernel for K % 128 == 0 (256 x 256 tiles once there are 512 of them),
     the register-staged kernel otherwise."""
-    assert sq.sq_gemm_kernel_name(16, 28672, 8192).startswith("k_gemm_decode")
+    assert sq.sq_gemm_kernel_name(16, 28672, 8192).startswith("k_gemm_decode_ring")
+    assert sq.sq_gemm_kernel_name(16, 100, 1040).startswith("k_gemm_decode (")
     assert sq.sq_gemm_kernel_name(2048, 4096, 4096).startswith("k_gemm_ring<128,128")
     assert sq.sq_gemm_kernel_name(4096, 14336, 4096).startswith("k_gemm_ring<256,256")
     assert sq.sq_gemm_kernel_name(8192, 49152, 12288).startswith("k_gemm_ring<256,256")

@@ -89,7 +89,14 @@ CASES = [
     (4100, 384, 16398, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # decode path (M <= 16): ragged N, K not a multiple of 64, per-tensor scale
     (16, 1040, 100, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
+    # LDS-ring decode path (K % 2048 == 0): 257 channel groups over 256 blocks, per-tensor
     (9, 4096, 4100, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 64),
+    # ring decode: N % 4 != 0 (element-wise stores), 63 groups
+    (16, 2048, 1001, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
+    # ring decode: one token, K = 16384 (eight stages per wavefront), per-tensor
+    (1, 16384, 300, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 16),
+    # ring decode: 513 groups, so one block takes three; K = 6144
+    (12, 6144, 8200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     # K a multiple of 16 but not of 128: register-staged GEMM path with a K tail
     (300, 1040, 520, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 300),
 ]
