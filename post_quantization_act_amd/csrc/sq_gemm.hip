@@ -140,9 +140,17 @@ __device__ __forceinline__ void copy16_to_lds(const int8_t* base, uint32_t voff,
                  : "memory", "m0");
 }
 
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8)); }
+// vmcnt wait and LDS-only barrier as asm with a memory clobber, so that no LDS
+// read of copied data is moved above them.  The copies are the only vector
+// memory loads in flight in the kernels that use them, and loads complete in
+// order, so vmcnt(n) means "all but the n most recent copies have landed".
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int BN, int BM, int WGN, int WGM, int kOut, bool kAcc>
+template <int BN, int BM, int WGN, int WGM, int NS, int kOut, bool kAcc>
 __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
                                                    int xs_step, const int8_t* __restrict__ wq,
                                                    const float* __restrict__ w_scale, int M, int N, int K,
@@ -158,8 +166,8 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
     constexpr int NRD = TN + TM;              // fragment reads per k-step
     constexpr int DR = (NRD + NMF - 1) / NMF, DD = (L + NMF - 1) / NMF;
     static_assert(COPIES % NW == 0 && BN % 8 == 0 && WN % 32 == 0 && WM % 32 == 0, "tile");
-    static_assert(2 * STAGE * 16 <= 160 * 1024, "LDS");
-    __shared__ uint4 lds[2 * STAGE];
+    static_assert(NS >= 2 && NS * STAGE * 16 <= 160 * 1024, "LDS");
+    __shared__ uint4 lds[NS * STAGE];
 
     const int lane = threadIdx.x % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -184,7 +192,7 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
     auto copy = [&](int kt, int j) {
         const int i = wave + NW * j;
-        const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + ((kt & 1) * STAGE + i * 64) * 16);
+        const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + ((kt % NS) * STAGE + i * 64) * 16);
         copy16_to_lds(8 * i < BN ? wq : xq, off[j] + (uint32_t)kt * kBK, la);
     };
 
@@ -227,45 +235,50 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
         }
     };
 
+    // Prologue: stages 0 .. NS-1 in flight, wait for stage 0.
     const int nk = K / kBK;
-    if (nk > 0) {
 #pragma unroll
-        for (int j = 0; j < L; ++j) copy(0, j);
-    }
-    if (nk > 1) {
+    for (int s = 0; s < NS; ++s)
+        if (s < nk) {
 #pragma unroll
-        for (int j = 0; j < L; ++j) copy(1, j);
-    }
-    wait_vmcnt0();
-    __syncthreads();
+            for (int j = 0; j < L; ++j) copy(s, j);
+        }
+    if (nk >= NS)
+        wait_vmcnt<L*(NS - 1)>();
+    else
+        wait_vmcnt<0>();
+    lds_barrier();
     if (nk > 0) {
 #pragma unroll
         for (int q = 0; q < NRD; ++q) read_frag(0, 0, q, 0);
     }
-    // Steady state (every iteration reads stage kt+1 and copies stage kt+2),
-    // then the last two iterations with those steps switched off.
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) {
-        const int buf = kt & 1;
+    // Steady state: iteration kt reads stage kt+1 from LDS and copies stage
+    // kt+NS into the buffer of stage kt; the last NS iterations copy nothing.
+    int kt = 0, buf = 0;
+    for (; kt + NS < nk; ++kt) {
+        const int nbuf = buf + 1 == NS ? 0 : buf + 1;
         __builtin_amdgcn_sched_barrier(0);
         kstep(0, true, buf, 1, 1, false, 0);
         kstep(1, true, buf, 2, 0, false, 0);
         kstep(0, true, buf, 3, 1, false, 0);
-        // Every read of this stage is issued (and completes before the
-        // barrier); this wavefront's copies of stage kt+1 have landed.
-        wait_vmcnt0();
-        __syncthreads();
-        kstep(1, true, buf ^ 1, 0, 0, true, kt + 2);
+        // This wavefront's copies of stage kt+1 have landed (those of stages
+        // kt+2 .. kt+NS-1 may stay in flight); after the barrier every
+        // wavefront's have, and every read of this stage's buffer is done.
+        wait_vmcnt<L*(NS - 2)>();
+        lds_barrier();
+        kstep(1, true, nbuf, 0, 0, true, kt + NS);
+        buf = nbuf;
     }
     for (; kt < nk; ++kt) {
-        const int buf = kt & 1;
+        const int nbuf = buf + 1 == NS ? 0 : buf + 1;
         __builtin_amdgcn_sched_barrier(0);
         kstep(0, true, buf, 1, 1, false, 0);
         kstep(1, true, buf, 2, 0, false, 0);
         kstep(0, true, buf, 3, 1, false, 0);
-        wait_vmcnt0();
-        __syncthreads();
-        kstep(1, kt + 1 < nk, buf ^ 1, 0, 0, false, 0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        kstep(1, kt + 1 < nk, nbuf, 0, 0, false, 0);
+        buf = nbuf;
     }
     epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
                                  acc_out);
@@ -531,13 +544,6 @@ __device__ __forceinline__ void copy16_to_lds_nt(const int8_t* base, uint32_t vo
                  : "s"(lds_off), "v"(voff), "s"(base)
                  : "memory", "m0");
 }
-// vmcnt wait and LDS-only barrier as asm with a memory clobber, so that no LDS
-// read of copied data is moved above them.
-template <int kN>
-__device__ __forceinline__ void wait_vmcnt() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
-}
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int SPW>
 __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
@@ -763,7 +769,7 @@ static void launch_decode(const int8_t* xq, const float* x_scale, bool per_tenso
 
 SQ_DEFINE_LAUNCH(k_gemm_generic)
 
-template <int BN, int BM, int WGN, int WGM>
+template <int BN, int BM, int WGN, int WGM, int NS>
 static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
                         const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
                         int group_m, hipStream_t st) {
@@ -772,7 +778,7 @@ static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor,
     const int step = per_tensor ? 0 : 1;
     const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);
     auto go = [&](auto out_c, auto acc_c) {
-        hipLaunchKernelGGL((k_gemm_ring<BN, BM, WGN, WGM, decltype(out_c)::value, decltype(acc_c)::value>), grid,
+        hipLaunchKernelGGL((k_gemm_ring<BN, BM, WGN, WGM, NS, decltype(out_c)::value, decltype(acc_c)::value>), grid,
                            dim3(64 * WGN * WGM), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n,
                            tiles_m, group_m);
     };
@@ -788,7 +794,7 @@ static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor,
 
 // Which kernel a product of this shape runs (the one rule both the launcher
 // and gemm_kernel_name use).
-enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing128, kGeneric };
+enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing256x128, kRing128, kGeneric };
 
 static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
     if (M <= 0 || N <= 0) return GemmPath::kNone;
@@ -796,11 +802,17 @@ static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
     const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
                       (uint64_t)M * (uint64_t)K < (1ull << 32);
     if (!ring) return GemmPath::kGeneric;
-    // 256 x 256 tiles (one block per CU, 128 KB LDS ring) when there are at
-    // least two per CU; otherwise 128 x 128 tiles (two blocks per CU), whose
-    // shorter per-block latency chain wins on smaller problems.
+    // 256 x 256 tiles (one block per CU, two-stage 128 KB ring) when there are
+    // at least two per CU.  Otherwise 256 x 128 tiles (one block per CU,
+    // three-stage 144 KB ring) if they need no more rounds over the CUs than
+    // 128 x 128 tiles (two blocks per CU) would; else 128 x 128.
     const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
-    return t256 >= 512 ? GemmPath::kRing256 : GemmPath::kRing128;
+    if (t256 >= 512) return GemmPath::kRing256;
+    const int64_t cus = device_cu_count();
+    const int64_t t_wide = ((N + 255) / 256) * ((M + 127) / 128);
+    const int64_t t128 = ((N + 127) / 128) * ((M + 127) / 128);
+    if ((t_wide + cus - 1) / cus <= (t128 + 2 * cus - 1) / (2 * cus)) return GemmPath::kRing256x128;
+    return GemmPath::kRing128;
 }
 
 const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
@@ -808,8 +820,10 @@ const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
         case GemmPath::kDecodeRing:
             return "k_gemm_decode_ring (one block of 16 wavefronts per CU, per-wavefront LDS rings of 128-byte stages)";
         case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
-        case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2> (256x256 tile, 8 wavefronts of 64x128)";
-        case GemmPath::kRing128: return "k_gemm_ring<128,128,2,4> (128x128 tile, 8 wavefronts of 64x32)";
+        case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2,2> (256x256 tile, 8 wavefronts of 64x128, 2 stages)";
+        case GemmPath::kRing256x128:
+            return "k_gemm_ring<256,128,2,4,3> (256x128 tile, 8 wavefronts of 128x32, 3 stages)";
+        case GemmPath::kRing128: return "k_gemm_ring<128,128,2,4,2> (128x128 tile, 8 wavefronts of 64x32, 2 stages)";
         case GemmPath::kGeneric: return "k_gemm_generic<256,128> (register-staged, any K % 16 == 0)";
         default: return "none (empty product)";
     }
@@ -828,10 +842,13 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
             launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
             break;
         case GemmPath::kRing256:
-            launch_ring<256, 256, 4, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 4, st);
+            launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 4, st);
+            break;
+        case GemmPath::kRing256x128:
+            launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
             break;
         case GemmPath::kRing128:
-            launch_ring<128, 128, 2, 4>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+            launch_ring<128, 128, 2, 4, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
             break;
         case GemmPath::kGeneric:
             launch_k_gemm_generic<256, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8,

@@ -81,10 +81,12 @@ CASES = [
     (130, 1024, 257, torch.bfloat16, sq.SQ_PER_TOKEN, 0.6, 1000),
     (520, 512, 130, torch.float32, sq.SQ_PER_TENSOR, 0.5, 64),
     (96, 12288, 200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 300),
-    # 128 x 128 GEMM path, ragged M and N, three stages
+    # 256 x 128 GEMM path (three-stage ring), ragged M and N, three stages (prologue only)
     (2100, 384, 3000, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 512),
-    # 128 x 128 GEMM path, ragged M, N % 4 != 0 (element-wise output stores), three stages
-    (2000, 384, 3998, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
+    # 256 x 128 path, ragged M, N % 4 != 0 (element-wise output stores), eight stages
+    (2000, 1024, 3998, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
+    # 128 x 128 path (258 tiles of 256 x 128 would need two rounds over 256 CUs), N < 128
+    (33000, 384, 100, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # enough output tiles for the 256 x 256 GEMM path, ragged M, N % 4 != 0, three stages
     (4100, 384, 16398, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # decode path (M <= 16): ragged N, K not a multiple of 64, per-tensor scale
