@@ -197,6 +197,12 @@ def _large(torch, sq, synth, pipeline, dev):
                                     3 * K * N + 4 * N + 4 * K)
     out["quant_weight_call"]["note"] = ("algorithmic 3 B/element; the call moves 5 (column-max pass reads W, the "
                                         "coding pass reads W and writes the codes)")
+    out["prepare_weights_call"] = rate(tm(lambda i: sq.sq_prepare_weights(b.amax_x, inp.w, 0.5, b.s, b.inv_s,
+                                                                          b.amax_w, b.wq, b.w_scale, b.ws_p),
+                                          reps=3), 5 * K * N + 4 * N + 16 * K)
+    out["prepare_weights_call"]["note"] = ("steps 2 + 3 in one call: algorithmic 2 + 3 B/element (row maxima; "
+                                           "codes), realised as one read of W for the row and column maxima and "
+                                           "one read + write for the codes")
     out["quant_act"] = rate(tm(lambda i: sq.sq_quant_act(inp.x, b.inv_s, sq.SQ_PER_TOKEN, b.xq, b.x_scale), reps=5),
                             3 * M * K + 4 * M + 4 * K)
     us = tm(lambda i: sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y), reps=3)
@@ -297,7 +303,7 @@ def main():
     b = pipeline.W8A8Buffers.allocate(M, N, K, gran, dev)
     stream = torch.cuda.current_stream(dev)
 
-    stages = ["calib_absmax", "smooth_factors", "quant_weight", "quant_act", "gemm_w8a8"]
+    stages = ["calib_absmax", "prepare_weights", "quant_act", "gemm_w8a8"]
 
     def step(i, ev=None):
         s = sets[i % pool]
@@ -306,18 +312,15 @@ def main():
         pipeline.calibrate(s.calib, b.amax_x)
         if ev is not None:
             ev[1].record(stream)
-        sq.sq_smooth_factors(b.amax_x, s.w, alpha, b.s, b.inv_s, b.amax_w)
+        sq.sq_prepare_weights(b.amax_x, s.w, alpha, b.s, b.inv_s, b.amax_w, b.wq, b.w_scale, b.ws_p)
         if ev is not None:
             ev[2].record(stream)
-        sq.sq_quant_weight(s.w, b.s, b.wq, b.w_scale, b.ws_w)
-        if ev is not None:
-            ev[3].record(stream)
         sq.sq_quant_act(s.x, b.inv_s, gran, b.xq, b.x_scale, b.ws_a)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
         sq.sq_gemm_w8a8(b.xq, b.x_scale, gran, b.wq, b.w_scale, b.y)
         if ev is not None:
-            ev[5].record(stream)
+            ev[4].record(stream)
 
     if args.launch == "graph":
         graphs = [pipeline.CapturedPass(st.x, st.w, st.calib, alpha, gran, b) for st in sets]
@@ -342,7 +345,7 @@ def main():
 
     # per-call breakdown: separate eager passes with HIP events between the calls
     # (not part of the timed region above)
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
@@ -355,8 +358,7 @@ def main():
     ops = 2.0 * M * N * K
     bytes_alg = {
         "calib_absmax": T * K * esz + 8 * K,
-        "smooth_factors": K * N * esz + 12 * K,
-        "quant_weight": K * N * esz + N * K + 4 * N + 4 * K,
+        "prepare_weights": 2 * K * N * esz + N * K + 4 * N + 16 * K,
         "quant_act": M * K * esz + M * K + 4 * M + 4 * K,
         "gemm_w8a8": M * K + N * K + 2 * M * N + 4 * (M + N),
     }
@@ -370,7 +372,8 @@ def main():
     kernels["gemm_w8a8"].update({"ops": ops, "TOPS": round(gemm_tops, 1),
                                  "pct_int8_peak": round(100 * gemm_tops / INT8_PEAK_TOPS, 1)})
     kernels["note"] = ("HIP-event intervals per call from separate eager passes (not the timed ones): calib_absmax "
-                       "includes zeroing the running max; quant_weight is three launches (clear, column max, coding)")
+                       "includes zeroing the running max; prepare_weights is steps 2 + 3 (one read of W for row and "
+                       "column maxima, a reduction of per-block maxima, one read + write for the codes)")
 
     if args.copy_probe_mb > 0:
         # a plain copy of known size whose source is not cache resident: 1 GiB

@@ -90,7 +90,8 @@ typedef enum {
     SQ_OP_SMOOTH_FACTORS = 1,
     SQ_OP_QUANT_WEIGHT = 2,
     SQ_OP_QUANT_ACT = 3,
-    SQ_OP_GEMM_W8A8 = 4
+    SQ_OP_GEMM_W8A8 = 4,
+    SQ_OP_PREPARE_WEIGHTS = 5
 } sq_op;
 
 /*
@@ -143,6 +144,31 @@ sq_status sq_smooth_factors(const float *amax_x, const void *w, sq_dtype wt, int
 sq_status sq_quant_weight(const void *w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
                           const float *s, int8_t *wq, float *w_scale, void *ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * Steps 2 and 3 in one call -- the offline weight preparation (page "4.2 W8A8
+ * 量化与 SmoothQuant" section 7.1: factors from the calibration statistics,
+ * then the smoothed weights quantized statically per channel).
+ *
+ * Computes exactly what sq_smooth_factors(amax_x, w, ..., alpha, s, inv_s,
+ * amax_w) followed by sq_quant_weight(w, ..., s, wq, w_scale, ...) compute,
+ * with the same arguments and results.  For a large bf16 W (K N >= 2^27
+ * elements, 16-byte aligned rows, N % 8 == 0, N <= 49152 when alpha is 0,
+ * 1/2 or 1 and N <= 32768 otherwise) it reads W once less: one pass over W
+ * yields the row maxima, the factors and the column maxima of diag(s) W, and
+ * a second pass writes the codes.  Other inputs take the two-call sequence
+ * internally.
+ *
+ *   amax_x, w, wt, K, N, ldw, alpha, s, inv_s, amax_w   as sq_smooth_factors
+ *                   (w is required; amax_w is an optional output);
+ *   wq, w_scale     as sq_quant_weight;
+ *   ws              workspace of sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, 0, N,
+ *                   K, 0) bytes, 16-byte aligned (column maxima and per-block
+ *                   partial maxima, about 1 KB per output channel).
+ */
+sq_status sq_prepare_weights(const float *amax_x, const void *w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
+                             float alpha, float *s, float *inv_s, float *amax_w, int8_t *wq, float *w_scale,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Step 4 -- fused smoothing and activation quantization (page "大模型训练、适配

@@ -20,7 +20,8 @@ __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
     "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
-    "sq_gemm_w8a8", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
+    "sq_gemm_w8a8", "sq_prepare_weights", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version",
+    "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -28,10 +29,10 @@ _LIB_PATH = os.path.join(_HERE, "libsq.so")
 
 SQ_F32, SQ_BF16 = 0, 1
 SQ_PER_TOKEN, SQ_PER_TENSOR = 0, 1
-SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, SQ_OP_GEMM_W8A8 = range(5)
+SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, SQ_OP_GEMM_W8A8, SQ_OP_PREPARE_WEIGHTS = range(6)
 
 EXPORTED_SYMBOLS = (
-    "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
+    "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights",
     "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
 )
 
@@ -64,7 +65,9 @@ def lib() -> ctypes.CDLL:
     L.sq_quant_weight.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     L.sq_quant_act.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.sq_gemm_w8a8.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
-    for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8"):
+    L.sq_prepare_weights.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
+              "sq_prepare_weights"):
         getattr(L, f).restype = ctypes.c_int
     L.sq_workspace_size.argtypes = [i32, i64, i64, i64, i32]
     L.sq_workspace_size.restype = sz
@@ -199,6 +202,25 @@ def sq_quant_weight(w: torch.Tensor, s: torch.Tensor | None, wq: torch.Tensor, w
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sq_quant_weight(_ptr(w), _dtype(w), K, N, ld, _ptr(s), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
                                  _stream(_dev(w), stream)))
+
+
+def sq_prepare_weights(amax_x: torch.Tensor, w: torch.Tensor, alpha: float, s: torch.Tensor, inv_s: torch.Tensor,
+                       amax_w: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor, ws: torch.Tensor | None,
+                       stream=None) -> None:
+    """Steps 2 and 3 in one call: s, inv_s [K] (and amax_w) from amax_x and W [K, N], then wq [N, K] and
+    w_scale [N] of diag(s) W."""
+    K, N, ld = _rows(w)
+    _dense(amax_x, "amax_x", (K,), torch.float32)
+    _dense(s, "s", (K,), torch.float32)
+    _dense(inv_s, "inv_s", (K,), torch.float32)
+    if amax_w is not None:
+        _dense(amax_w, "amax_w", (K,), torch.float32)
+    _dense(wq, "wq", (N, K), torch.int8)
+    _dense(w_scale, "w_scale", (N,), torch.float32)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sq_prepare_weights(_ptr(amax_x), _ptr(w), _dtype(w), K, N, ld, ctypes.c_float(alpha), _ptr(s),
+                                    _ptr(inv_s), _ptr(amax_w), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
+                                    _stream(_dev(w, amax_x), stream)))
 
 
 def sq_quant_act(x: torch.Tensor, inv_s: torch.Tensor | None, gran: int, xq: torch.Tensor,

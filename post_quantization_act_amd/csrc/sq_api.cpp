@@ -115,6 +115,10 @@ size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran 
     (void)K;
     switch (op) {
         case SQ_OP_QUANT_WEIGHT: return N > 0 ? round256((size_t)N * sizeof(uint32_t)) : 0;
+        case SQ_OP_PREPARE_WEIGHTS:
+            return N > 0 && K > 0 ? round256((size_t)N * sizeof(uint32_t)) +
+                                        round256((size_t)sqk::prep_blocks(K) * (size_t)N * sizeof(float))
+                                  : 0;
         case SQ_OP_QUANT_ACT: return g == SQ_PER_TENSOR ? 256 : 0;
         default: return 0;
     }
@@ -177,6 +181,50 @@ sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t K, int64_t N, int6
     hipError_t e = sqk::launch_fill_u32(colmax, N, 0u, stream);
     if (e == hipSuccess) e = sqk::launch_col_absmax(w, wt == SQ_BF16, K, N, ldw, s, colmax, stream);
     if (e == hipSuccess) e = sqk::launch_quant_weight(w, wt == SQ_BF16, K, N, ldw, s, colmax, wq, w_scale, stream);
+    return hip_result(e, fn);
+}
+
+sq_status sq_prepare_weights(const float* amax_x, const void* w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
+                             float alpha, float* s, float* inv_s, float* amax_w, int8_t* wq, float* w_scale, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "sq_prepare_weights";
+    SQ_TRY(check_k(fn, K));
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(SQ_ERR_INVALID_ARG, "%s: alpha = %g is not in [0, 1]", fn, alpha);
+    if (N > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld too large", fn, (long long)N);
+    if (K > 0 && N <= 0) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld must be positive", fn, (long long)N);
+    SQ_TRY(check_vec(fn, "amax_x", amax_x, K));
+    SQ_TRY(check_vec(fn, "s", s, K));
+    SQ_TRY(check_vec(fn, "inv_s", inv_s, K));
+    if (amax_w) SQ_TRY(check_vec(fn, "amax_w", amax_w, K));
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
+    SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
+    if (K > 0 && N > 0) {
+        if (!wq) return fail(SQ_ERR_INVALID_ARG, "%s: wq is NULL", fn);
+        if (!aligned16(wq)) return fail(SQ_ERR_INVALID_ARG, "%s: wq is not 16-byte aligned", fn);
+    }
+    const size_t need = sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, 0, N, K, SQ_PER_TOKEN);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    ws ? ws_bytes : (size_t)0);
+    if (N == 0) return ok();
+    if (K == 0)  // no input channels: every column max is 0, so every scale is 0
+        return hip_result(sqk::launch_fill_u32(reinterpret_cast<uint32_t*>(w_scale), N, 0u, stream), fn);
+    const bool bf16 = wt == SQ_BF16;
+    uint32_t* colmax = static_cast<uint32_t*>(ws);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)N * sizeof(uint32_t)));
+    hipError_t e;
+    // The one-read pass streams each block's rows one (or a few) at a time; it
+    // wins once W is large enough for the saved read of W to dominate (at
+    // 4096 x 4096 the more parallel separate passes are faster).
+    const bool big = (uint64_t)K * (uint64_t)N >= (128ull << 20);
+    if (big && sqk::prep_fused_supported(w, bf16, N, ldw, alpha)) {
+        e = sqk::launch_prepare_weights(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, partial, colmax, stream);
+    } else {
+        e = sqk::launch_row_absmax_factors(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, stream);
+        if (e == hipSuccess) e = sqk::launch_fill_u32(colmax, N, 0u, stream);
+        if (e == hipSuccess) e = sqk::launch_col_absmax(w, bf16, K, N, ldw, s, colmax, stream);
+    }
+    if (e == hipSuccess) e = sqk::launch_quant_weight(w, bf16, K, N, ldw, s, colmax, wq, w_scale, stream);
     return hip_result(e, fn);
 }
 

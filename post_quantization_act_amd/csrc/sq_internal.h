@@ -18,6 +18,17 @@ hipError_t launch_row_absmax_factors(const void* w, bool bf16, int64_t K, int64_
                                      const float* amax_x, float alpha, float* s, float* inv_s, float* amax_w,
                                      hipStream_t st);
 
+// Steps 2 + 3a in one read of W (bf16, 16-byte aligned rows, N % 8 == 0,
+// N <= 49152 for alpha in {0, 1/2, 1}, N <= 32768 otherwise): amax_w (optional), s, inv_s and the column maxima of diag(s) W
+// into colmax (fp32 bits), through per-block partial maxima
+// partial[prep_blocks(K)][N].  hipErrorNotSupported (nothing enqueued) when
+// prep_fused_supported() is false.
+int prep_blocks(int64_t K);
+bool prep_fused_supported(const void* w, bool bf16, int64_t N, int64_t ld, float alpha);
+hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* amax_x,
+                                  float alpha, float* s, float* inv_s, float* amax_w, float* partial,
+                                  uint32_t* colmax, hipStream_t st);
+
 hipError_t launch_factors(const float* amax_x, const float* amax_w, int64_t K, float alpha, float* s,
                           float* inv_s, hipStream_t st);
 

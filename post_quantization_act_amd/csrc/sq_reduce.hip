@@ -86,22 +86,24 @@ __global__ __launch_bounds__(256) void k_col_absmax(const T* __restrict__ x, int
 }
 
 // x^e in fp64 with the exact forms for e = 0, 1/2, 1.
+template <bool kGeneral = true>
 __device__ __forceinline__ double pow_cases(double x, double e) {
     if (e == 0.0) return 1.0;
     if (e == 1.0) return x;
-    if (e == 0.5) return sqrt(x);
+    if (e == 0.5 || !kGeneral) return sqrt(x);  // !kGeneral: the caller guarantees e is 0, 1/2 or 1
     return pow(x, e);
 }
 
 // s = a^alpha / b^(1-alpha) with both maxima floored at 1e-5f, in fp64 and
 // rounded once; inv_s = correctly rounded fp32 reciprocal.
+template <bool kGeneral = true>
 __device__ __forceinline__ void smooth_factor(float ax, float aw, float alpha, float& s, float& inv_s) {
     const float fl = 1e-5f;
     const float a = ax > fl ? ax : fl;
     const float b = aw > fl ? aw : fl;
     const double ea = (double)alpha;
     const double eb = 1.0 - ea;
-    s = (float)(pow_cases((double)a, ea) / pow_cases((double)b, eb));
+    s = (float)(pow_cases<kGeneral>((double)a, ea) / pow_cases<kGeneral>((double)b, eb));
     inv_s = 1.0f / s;
 }
 
@@ -146,6 +148,174 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
         inv_s[j] = ij;
         if (amax_w) amax_w[j] = m;
     }
+}
+
+// ---- steps 2 + 3a fused: one read of W gives amax_w, s, inv_s and the
+// column maxima of diag(s) W ------------------------------------------------
+//
+// A block of 512 threads streams the rows [r0, r1) of W (bf16, 16-byte
+// aligned rows, N % 8 == 0).  Each iteration takes RB rows: row slot
+// t / TPR (TPR = 512 / RB threads per row); thread t % TPR of a slot owns
+// the 8-column groups q = t % TPR + TPR i, i < GPT, and keeps their running
+// column maxima in registers.  Per row: max |w| over the slot (shuffles, then
+// LDS across its wavefronts behind one barrier), s_j by the same fp64 rule
+// as k_row_absmax_factors, then the running maxima take |fl(s_j w)|.  The
+// next row's loads are issued once s_j is known (the fp64 factor then runs
+// with one row buffer live) and stay in flight through the update and the
+// next reduction; the barrier waits on LDS only, and nothing else touches
+// global memory in
+// the loop: amax_x is staged in LDS before, the per-row results are written
+// after it.  The block's column maxima (its RB slots combined through LDS)
+// leave as plain stores to partial[blockIdx.x][N]; k_colmax_reduce takes the
+// maximum over blocks.
+constexpr int kPrepThreads = 512;
+constexpr int kPrepMaxRows = 256;  // rows per block (LDS staging of per-row values)
+
+__device__ __forceinline__ void lds_only_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int RB, int GR, int GL, bool kGeneral>
+__global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __restrict__ w, int64_t K, int64_t N,
+                                                            int64_t ld, const float* __restrict__ amax_x,
+                                                            float alpha, float* __restrict__ s,
+                                                            float* __restrict__ inv_s, float* __restrict__ amax_w,
+                                                            float* __restrict__ partial, int rows_per_block) {
+    // GR groups keep their running maxima in registers, GL more in LDS
+    // (thread-major, so each access is conflict-free)
+    constexpr int GPT = GR + GL;
+    constexpr int TPR = kPrepThreads / RB, WPR = TPR / kWave;
+    static_assert(RB == 1 || GL == 0, "LDS-held maxima only with one row per iteration");
+    __shared__ float red[2][kPrepThreads / kWave];
+    __shared__ float axl[kPrepMaxRows], srow[kPrepMaxRows], irow[kPrepMaxRows], arow[kPrepMaxRows];
+    __shared__ float comb[RB > 1 ? (RB - 1) * TPR * 8 * GPT : 1];
+    __shared__ float cml[GL > 0 ? GL * 8 * kPrepThreads : 1];
+    const int t = threadIdx.x, slot = t / TPR, ts = t % TPR, wave = t / kWave, lane = t % kWave;
+    const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+    const int nrows = (int)min((int64_t)rows_per_block, K - r0);
+    for (int i = t; i < nrows; i += kPrepThreads) axl[i] = amax_x[r0 + i];
+#pragma unroll
+    for (int i = 0; i < GL * 8; ++i) cml[i * kPrepThreads + t] = 0.0f;
+    const int iters = (nrows + RB - 1) / RB;
+
+    float cm[GR][8];
+#pragma unroll
+    for (int i = 0; i < GR; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cm[i][e] = 0.0f;
+    uint4 cur[GPT], nxt[GPT];
+    auto load_rows = [&](int it, uint4 (&dst)[GPT]) {
+        const int rl = it * RB + slot;
+        const bf16_t* row = w + (r0 + rl) * ld;
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int64_t q = ts + (int64_t)TPR * i;
+            dst[i] = (rl < nrows && 8 * q < N) ? ld16_stream(row + 8 * q) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    if (iters > 0) load_rows(0, cur);
+    for (int it = 0; it < iters; ++it) {
+        const int rl = it * RB + slot;
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const uint32_t u[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) m = fmaxf(m, fmaxf(fabsf(bf16_lo(u[h])), fabsf(bf16_hi(u[h]))));
+        }
+        m = wave_max(m);
+        if (lane == 0) red[it & 1][wave] = m;
+        lds_only_barrier();
+        // the row stays packed across the barrier and the factor: unpack it
+        // again below instead of keeping 8 floats per group alive
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            asm volatile("" : "+v"(cur[i].x), "+v"(cur[i].y), "+v"(cur[i].z), "+v"(cur[i].w));
+        if (rl < nrows) {  // uniform over the slot's wavefronts
+            float rm = 0.0f;
+#pragma unroll
+            for (int v = 0; v < WPR; ++v) rm = fmaxf(rm, red[it & 1][slot * WPR + v]);
+            float sj = 0.0f, ij = 0.0f;
+            if (lane == 0) smooth_factor<kGeneral>(axl[rl], rm, alpha, sj, ij);
+            sj = __shfl(sj, 0);
+            if (ts == 0) {
+                srow[rl] = sj;
+                irow[rl] = ij;
+                arow[rl] = rm;
+            }
+            if (it + 1 < iters) load_rows(it + 1, nxt);
+#pragma unroll
+            for (int i = 0; i < GPT; ++i) {
+                const uint32_t u[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float a0 = fabsf(sj * bf16_lo(u[h])), a1 = fabsf(sj * bf16_hi(u[h]));
+                    if (i < GR) {
+                        cm[i < GR ? i : 0][2 * h] = fmaxf(cm[i < GR ? i : 0][2 * h], a0);
+                        cm[i < GR ? i : 0][2 * h + 1] = fmaxf(cm[i < GR ? i : 0][2 * h + 1], a1);
+                    } else {
+                        float* c = cml + ((i - GR) * 8 + 2 * h) * kPrepThreads + t;
+                        c[0] = fmaxf(c[0], a0);
+                        c[kPrepThreads] = fmaxf(c[kPrepThreads], a1);
+                    }
+                }
+            }
+        } else if (it + 1 < iters) {
+            load_rows(it + 1, nxt);
+        }
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) cur[i] = nxt[i];
+    }
+    if constexpr (RB > 1) {
+        if (slot > 0) {
+#pragma unroll
+            for (int i = 0; i < GPT; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) comb[(((slot - 1) * GPT + i) * TPR + ts) * 8 + e] = cm[i][e];
+        }
+    }
+    lds_only_barrier();
+    if (slot == 0) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) {
+            const int64_t q = ts + (int64_t)TPR * i;
+            if (8 * q >= N) continue;
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                o[e] = i < GR ? cm[i < GR ? i : 0][e] : cml[((i - GR) * 8 + e) * kPrepThreads + t];
+            if constexpr (RB > 1) {
+                for (int sl = 1; sl < RB; ++sl)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) o[e] = fmaxf(o[e], comb[(((sl - 1) * GPT + i) * TPR + ts) * 8 + e]);
+            }
+            float* dst = partial + (int64_t)blockIdx.x * N + 8 * q;
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+    }
+    for (int i = t; i < nrows; i += kPrepThreads) {
+        s[r0 + i] = srow[i];
+        inv_s[r0 + i] = irow[i];
+        if (amax_w) amax_w[r0 + i] = arow[i];
+    }
+}
+
+// colmax[k] = max over blocks b of partial[b][k], as fp32 bit patterns.
+__global__ __launch_bounds__(256) void k_colmax_reduce(const float* __restrict__ partial, int nb, int64_t N,
+                                                       uint32_t* __restrict__ colmax) {
+    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (k >= N) return;
+    float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
+    int b = 0;
+    for (; b + 3 < nb; b += 4) {
+        m0 = fmaxf(m0, partial[(int64_t)b * N + k]);
+        m1 = fmaxf(m1, partial[(int64_t)(b + 1) * N + k]);
+        m2 = fmaxf(m2, partial[(int64_t)(b + 2) * N + k]);
+        m3 = fmaxf(m3, partial[(int64_t)(b + 3) * N + k]);
+    }
+    for (; b < nb; ++b) m0 = fmaxf(m0, partial[(int64_t)b * N + k]);
+    colmax[k] = __float_as_uint(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
 }
 
 // s and inv_s from both maxima already known (reuse of amax_w across alphas).
@@ -222,6 +392,60 @@ hipError_t launch_row_absmax_factors(const void* w, bool bf16, int64_t K, int64_
     };
     if (bf16) { if (vec) go(bf16_t{}, std::true_type{}); else go(bf16_t{}, std::false_type{}); }
     else { if (vec) go(float{}, std::true_type{}); else go(float{}, std::false_type{}); }
+    return hipGetLastError();
+}
+
+
+// About 256 blocks (one per CU), at most kPrepMaxRows rows each, none empty.
+int prep_blocks(int64_t K) {
+    if (K <= 0) return 0;
+    int64_t rpb = (K + 255) / 256;
+    if (rpb > kPrepMaxRows) rpb = kPrepMaxRows;
+    return (int)((K + rpb - 1) / rpb);
+}
+
+bool prep_fused_supported(const void* w, bool bf16, int64_t N, int64_t ld, float alpha) {
+    const bool exact = alpha == 0.0f || alpha == 0.5f || alpha == 1.0f;
+    const int64_t max_groups = (int64_t)kPrepThreads * (exact ? 12 : 8);
+    return bf16 && N > 0 && N % 8 == 0 && N / 8 <= max_groups && rows_aligned16(w, ld, 2);
+}
+
+hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* amax_x,
+                                  float alpha, float* s, float* inv_s, float* amax_w, float* partial,
+                                  uint32_t* colmax, hipStream_t st) {
+    if (K <= 0 || N <= 0) return hipSuccess;
+    if (!prep_fused_supported(w, bf16, N, ld, alpha)) return hipErrorNotSupported;
+    const int nb = prep_blocks(K);
+    const int rpb = (int)((K + nb - 1) / nb);
+    const int64_t groups = N / 8;
+    const bf16_t* wb = static_cast<const bf16_t*>(w);
+#define SQ_PREP(RB, GR, GL, G)                                                                                    \
+    hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G>), dim3((unsigned)nb), dim3(kPrepThreads), 0, st, wb, K, N, ld,    \
+                       amax_x, alpha, s, inv_s, amax_w, partial, rpb)
+    // alpha in {0, 1/2, 1} needs no fp64 pow: fewer registers, wider rows
+    const bool general = !(alpha == 0.0f || alpha == 0.5f || alpha == 1.0f);
+    if (general) {
+        if (groups <= 128) SQ_PREP(4, 1, 0, true);
+        else if (groups <= 256) SQ_PREP(2, 1, 0, true);
+        else if (groups <= 512) SQ_PREP(1, 1, 0, true);
+        else if (groups <= 1024) SQ_PREP(1, 2, 0, true);
+        else if (groups <= 2048) SQ_PREP(1, 4, 0, true);
+        else if (groups <= 3072) SQ_PREP(1, 6, 0, true);
+        else SQ_PREP(1, 8, 0, true);
+    } else {
+        if (groups <= 128) SQ_PREP(4, 1, 0, false);
+        else if (groups <= 256) SQ_PREP(2, 1, 0, false);
+        else if (groups <= 512) SQ_PREP(1, 1, 0, false);
+        else if (groups <= 1024) SQ_PREP(1, 2, 0, false);
+        else if (groups <= 2048) SQ_PREP(1, 4, 0, false);
+        else if (groups <= 3072) SQ_PREP(1, 6, 0, false);
+        else if (groups <= 4096) SQ_PREP(1, 8, 0, false);
+        else SQ_PREP(1, 4, 8, false);
+    }
+#undef SQ_PREP
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, partial, nb, N, colmax);
     return hipGetLastError();
 }
 

@@ -9,8 +9,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR, sq_calib_absmax, sq_gemm_w8a8, sq_quant_act,
-               sq_quant_weight, sq_smooth_factors, sq_workspace_size)
+from . import (SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR, sq_calib_absmax,
+               sq_gemm_w8a8, sq_prepare_weights, sq_quant_act, sq_quant_weight, sq_smooth_factors,
+               sq_workspace_size)
 
 
 @dataclass
@@ -27,6 +28,7 @@ class W8A8Buffers:
     acc: torch.Tensor | None
     ws_w: torch.Tensor | None
     ws_a: torch.Tensor | None
+    ws_p: torch.Tensor | None
 
     @classmethod
     def allocate(cls, M: int, N: int, K: int, gran: int, device, y_dtype=torch.bfloat16, with_acc=False):
@@ -44,6 +46,7 @@ class W8A8Buffers:
             acc=torch.empty(M, N, dtype=torch.int32, device=device) if with_acc else None,
             ws_w=ws(sq_workspace_size(SQ_OP_QUANT_WEIGHT, M, N, K, gran)),
             ws_a=ws(sq_workspace_size(SQ_OP_QUANT_ACT, M, N, K, gran)),
+            ws_p=ws(sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, M, N, K, gran)),
         )
 
 
@@ -56,10 +59,14 @@ def calibrate(calib, amax_x: torch.Tensor, reset: bool = True, stream=None) -> N
         sq_calib_absmax(c, amax_x, stream=stream)
 
 
-def prepare_weights(w: torch.Tensor, alpha: float | None, b: W8A8Buffers, stream=None) -> None:
-    """Steps 2-3 (alpha=None: unsmoothed weights)."""
+def prepare_weights(w: torch.Tensor, alpha: float | None, b: W8A8Buffers, stream=None, fused: bool = True) -> None:
+    """Steps 2-3 (alpha=None: unsmoothed weights).  fused: one sq_prepare_weights call; otherwise
+    sq_smooth_factors then sq_quant_weight (same results)."""
     if alpha is None:
         sq_quant_weight(w, None, b.wq, b.w_scale, b.ws_w, stream=stream)
+        return
+    if fused:
+        sq_prepare_weights(b.amax_x, w, alpha, b.s, b.inv_s, b.amax_w, b.wq, b.w_scale, b.ws_p, stream=stream)
         return
     sq_smooth_factors(b.amax_x, w, alpha, b.s, b.inv_s, b.amax_w, stream=stream)
     sq_quant_weight(w, b.s, b.wq, b.w_scale, b.ws_w, stream=stream)
@@ -72,11 +79,12 @@ def forward(x: torch.Tensor, gran: int, b: W8A8Buffers, smoothed: bool = True, s
     return b.y
 
 
-def smoothquant_w8a8(x, w, calib, alpha: float | None, gran: int, b: W8A8Buffers, stream=None) -> torch.Tensor:
+def smoothquant_w8a8(x, w, calib, alpha: float | None, gran: int, b: W8A8Buffers, stream=None,
+                     fused: bool = True) -> torch.Tensor:
     """All five steps.  alpha=None runs the unsmoothed W8A8 baseline (no calibration)."""
     if alpha is not None:
         calibrate(calib, b.amax_x, stream=stream)
-    prepare_weights(w, alpha, b, stream=stream)
+    prepare_weights(w, alpha, b, stream=stream, fused=fused)
     return forward(x, gran, b, smoothed=alpha is not None, stream=stream)
 
 

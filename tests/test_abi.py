@@ -63,6 +63,11 @@ def test_workspace_sizes():
     assert sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, 2048, 0, 4096, sq.SQ_PER_TOKEN) == 0
     assert sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, 2048, 0, 4096, sq.SQ_PER_TENSOR) >= 4
     assert sq.sq_workspace_size(sq.SQ_OP_CALIB_ABSMAX, 1, 1, 16) == 0
+    # prepare_weights: column maxima + one partial row of N maxima per block (<= 256 blocks)
+    assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 4096) >= 4096 * 4 + 256 * 4096 * 4
+    assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 100) >= 4096 * 4 + 100 * 4096 * 4
+    assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 300) < 4096 * 4 + 256 * 4096 * 4  # 150 blocks
+    assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 0, 4096) == 0
 
 
 FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
@@ -151,3 +156,18 @@ def test_binding_rejects_host_tensors():
     amax = torch.zeros(32)
     with pytest.raises(ValueError, match="device tensors"):
         sq.sq_calib_absmax(x, amax)
+
+
+def test_prepare_weights_rejects():
+    L = _L()
+    f = ctypes.c_float
+    args = lambda **kw: [kw.get("amax_x", FAKE), kw.get("w", FAKE), sq.SQ_BF16, kw.get("K", 32), kw.get("N", 64),
+                         kw.get("ld", 64), f(kw.get("alpha", 0.5)), kw.get("s", FAKE), FAKE, None,
+                         kw.get("wq", FAKE), FAKE, kw.get("ws", FAKE), kw.get("wsb", 1 << 20), None]
+    _expect(L.sq_prepare_weights(*args(alpha=1.5)), -1, "alpha")
+    _expect(L.sq_prepare_weights(*args(N=0)), -1, "N = 0")
+    _expect(L.sq_prepare_weights(*args(s=None)), -1, "s is NULL")
+    _expect(L.sq_prepare_weights(*args(wq=MISALIGNED)), -1, "wq")
+    _expect(L.sq_prepare_weights(*args(K=33)), -1, "K = 33")
+    _expect(L.sq_prepare_weights(*args(ws=None, wsb=0)), -3, "workspace")
+    _expect(L.sq_prepare_weights(*args(wsb=64)), -3, "workspace")

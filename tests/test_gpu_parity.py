@@ -271,3 +271,93 @@ def test_determinism_repeat_runs():
     b2 = _run_gpu(xd, wd, cd, 0.5, sq.SQ_PER_TOKEN)
     for name in ("amax_x", "s", "wq", "w_scale", "xq", "x_scale", "acc", "y"):
         assert torch.equal(getattr(b1, name), getattr(b2, name)), name
+
+
+PREP_CASES = [
+    # K, N, alpha, dtype.  W of at least 2^27 elements takes the one-read pass: every
+    # row layout of it, both factor kinds (alpha in {0, 1/2, 1} without pow, others
+    # with it), ragged rows per block and ragged column groups.
+    (131072, 1024, 0.5, torch.bfloat16),  # 4 rows per iteration, 512 blocks of 256 rows
+    (65536, 2048, 0.75, torch.bfloat16),  # 2 rows per iteration, general alpha
+    (32768, 4096, 0.5, torch.bfloat16),   # one group per thread
+    (16384, 8192, 0.4, torch.bfloat16),   # two groups, general alpha
+    (8192, 16384, 0.0, torch.bfloat16),   # four groups, alpha = 0
+    (5472, 24576, 1.0, torch.bfloat16),   # six groups, alpha = 1, 22 rows per block, last block 16
+    (5472, 24600, 0.5, torch.bfloat16),   # 3075 groups: eight per thread, the last ones partly masked
+    (4096, 32768, 0.6, torch.bfloat16),   # eight groups, general alpha
+    (2736, 49152, 0.5, torch.bfloat16),   # twelve groups: 4 in registers, 8 in LDS
+    # the two-call sequence: small W, general alpha beyond 32768 columns, N % 8 != 0, fp32
+    (304, 1000, 0.5, torch.bfloat16),
+    (2736, 49152, 0.75, torch.bfloat16),
+    (112, 1001, 0.5, torch.bfloat16),
+    (208, 512, 0.5, torch.float32),
+]
+
+
+@pytest.mark.parametrize("K,N,alpha,dtype", PREP_CASES)
+def test_prepare_weights_matches_two_calls(K, N, alpha, dtype):
+    """sq_prepare_weights == sq_smooth_factors + sq_quant_weight, bit for bit, and
+    both equal the oracle (factors in full, codes on sampled channels)."""
+    _say(f"prepare_weights K={K} N={N} alpha={alpha} {dtype}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(K * 31 + N)
+    n_out = max(1, K // 100)
+    idx = torch.randperm(K, generator=g, device=DEV)[:n_out]
+    wd = synth.weights(K, N, 0.02, dtype, g, DEV)
+    wd[idx[: max(1, n_out // 2)]] *= 8.0  # a few heavy weight rows (exact in bf16)
+    ad = (torch.rand(K, generator=g, device=DEV) * 3 + 0.01).float()
+    ad[idx] *= 100.0
+    f32 = dict(dtype=torch.float32, device=DEV)
+    res = []
+    for fused in (True, False):
+        s_, i_, aw = torch.empty(K, **f32), torch.empty(K, **f32), torch.empty(K, **f32)
+        wq = torch.empty(N, K, dtype=torch.int8, device=DEV)
+        wsc = torch.empty(N, **f32)
+        if fused:
+            ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, N, K), dtype=torch.uint8, device=DEV)
+            sq.sq_prepare_weights(ad, wd, alpha, s_, i_, aw, wq, wsc, ws)
+        else:
+            ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, N, K), dtype=torch.uint8, device=DEV)
+            sq.sq_smooth_factors(ad, wd, alpha, s_, i_, aw)
+            sq.sq_quant_weight(wd, s_, wq, wsc, ws)
+        torch.cuda.synchronize()
+        res.append((s_, i_, aw, wq, wsc))
+        del ws
+    for a, b, name in zip(res[0], res[1], ("s", "inv_s", "amax_w", "wq", "w_scale")):
+        assert torch.equal(a, b), name
+    w = _np(wd)
+    aw_o = oracle.weight_rowmax(w)
+    s_o, i_o = oracle.smooth_factors(_np(ad), aw_o, alpha)
+    np.testing.assert_array_equal(_np(res[0][2]), aw_o)
+    np.testing.assert_array_equal(_np(res[0][0]), s_o)
+    np.testing.assert_array_equal(_np(res[0][1]), i_o)
+    cols = np.unique(np.linspace(0, N - 1, 24).astype(int))
+    wq_o, ws_o = oracle.quant_weight(np.ascontiguousarray(w[:, cols]), s_o)
+    np.testing.assert_array_equal(_np(res[0][4])[cols], ws_o)
+    np.testing.assert_array_equal(_np(res[0][3])[cols], wq_o)
+
+
+def test_prepare_weights_without_amax_w_and_empty():
+    K, N = 256, 768
+    g = torch.Generator(device="cpu")
+    g.manual_seed(9)
+    w = synth.weights(K, N, 0.02, torch.bfloat16, g, "cpu").to(DEV)
+    ax = (torch.rand(K, generator=g) + 0.1).float().to(DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    s1, i1, s2, i2 = (torch.empty(K, **f32) for _ in range(4))
+    wq1, wq2 = (torch.empty(N, K, dtype=torch.int8, device=DEV) for _ in range(2))
+    w1, w2 = torch.empty(N, **f32), torch.empty(N, **f32)
+    ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, N, K), dtype=torch.uint8, device=DEV)
+    sq.sq_prepare_weights(ax, w, 0.5, s1, i1, None, wq1, w1, ws)
+    ws2 = torch.empty(sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, N, K), dtype=torch.uint8, device=DEV)
+    sq.sq_smooth_factors(ax, w, 0.5, s2, i2, None)
+    sq.sq_quant_weight(w, s2, wq2, w2, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(wq1, wq2) and torch.equal(w1, w2)
+    # K = 0: every scale is 0
+    w0 = torch.empty(0, 8, dtype=torch.bfloat16, device=DEV)
+    e = torch.empty(0, **f32)
+    wsc = torch.full((8,), 7.0, **f32)
+    sq.sq_prepare_weights(e, w0, 0.5, e, e, None, torch.empty(8, 0, dtype=torch.int8, device=DEV), wsc, None)
+    torch.cuda.synchronize()
+    assert torch.equal(wsc, torch.zeros(8, **f32))
