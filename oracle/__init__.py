@@ -59,6 +59,9 @@ def lib():
         L.sqo_smooth_factors.argtypes = [f32p, f32p, i64, ctypes.c_float, f32p, f32p]
         L.sqo_quant_weight.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, i64, f32p]
         L.sqo_quant_act.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, vp, i64, f32p]
+        L.sqo_static_act_max.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp]
+        L.sqo_static_act_max.restype = ctypes.c_float
+        L.sqo_quant_act_static.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_float, vp, i64, f32p]
         L.sqo_gemm_i8.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i64, ctypes.c_int]
         L.sqo_dequant.argtypes = [vp, i64, f32p, ctypes.c_int, f32p, i64, i64, vp, vp, i64]
         L.sqo_quant_sym.argtypes = [f32p, i64, ctypes.c_int, vp, f32p]
@@ -158,6 +161,26 @@ def quant_act(x: np.ndarray, inv_s: np.ndarray | None, gran: int = PER_TOKEN):
     xs = np.empty(1 if gran == PER_TENSOR else M, np.float32)
     _check(lib().sqo_quant_act(_p(x), _dtype_code(x), M, K, K, _p(ip), gran, _p(xq), K, _p(xs)),
            "quant_act")
+    return xq, xs
+
+
+def static_act_max(calib: np.ndarray, inv_s: np.ndarray | None) -> np.float32:
+    """Calibrated per-tensor maximum: max over the calibration tokens of |X'| (fp32)."""
+    calib = np.ascontiguousarray(calib)
+    T, K = calib.shape
+    ip = None if inv_s is None else np.ascontiguousarray(inv_s, dtype=np.float32)
+    return np.float32(lib().sqo_static_act_max(_p(calib), _dtype_code(calib), T, K, K, _p(ip)))
+
+
+def quant_act_static(x: np.ndarray, inv_s: np.ndarray | None, a: float):
+    """Per-tensor codes of X' with the fixed (calibrated) maximum a: (xq[M, K], x_scale[1])."""
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    ip = None if inv_s is None else np.ascontiguousarray(inv_s, dtype=np.float32)
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(1, np.float32)
+    _check(lib().sqo_quant_act_static(_p(x), _dtype_code(x), M, K, K, _p(ip), ctypes.c_float(float(a)), _p(xq),
+                                      K, _p(xs)), "quant_act_static")
     return xq, xs
 
 

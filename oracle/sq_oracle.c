@@ -298,6 +298,44 @@ int sqo_quant_act(const void *x, int dtype, int64_t M, int64_t K, int64_t ldx,
     return 0;
 }
 
+/* ---- static per-tensor activation scale ([P3] 7.1 export step) ---------- */
+
+/* The calibrated maximum of the smoothed activations: the largest |X'| =
+ * |fl(x * inv_s_j)| over all calibration tokens t and channels j ([P3] 7.1:
+ * activation scales may come from calibration statistics instead of being
+ * computed at run time).  inv_s == NULL takes X itself. */
+float sqo_static_act_max(const void *x, int dtype, int64_t T, int64_t K, int64_t ldx, const float *inv_s)
+{
+    float a = 0.0f;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < K; ++j) {
+            float v = load_elem(x, dtype, t * ldx + j);
+            float m = fabsf(inv_s ? v * inv_s[j] : v);
+            if (m > a)
+                a = m;
+        }
+    return a;
+}
+
+/* Per-tensor codes with that fixed maximum a: x_scale[0] = fl(a / 127) and
+ * r = fl(127 / a) (0 if a = 0) as for a dynamic per-tensor scale, but a does
+ * not depend on x, so run-time values beyond the calibrated range saturate
+ * at +-127. */
+int sqo_quant_act_static(const void *x, int dtype, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
+                         float a, int8_t *xq, int64_t ldq, float *x_scale)
+{
+    if (M < 0 || K < 0 || ldx < K || ldq < K || !(a >= 0.0f))
+        return -1;
+    float r;
+    sym_scale(a, 127.0f, x_scale, &r);
+    for (int64_t i = 0; i < M; ++i)
+        for (int64_t j = 0; j < K; ++j) {
+            float v = load_elem(x, dtype, i * ldx + j);
+            xq[i * ldq + j] = (int8_t)sym_code(inv_s ? v * inv_s[j] : v, r, 127.0f);
+        }
+    return 0;
+}
+
 /* ---- step 5: INT8 x INT8 -> int32 GEMM and dequantization --------------- */
 
 /* acc[i, k] = sum_j Xq[i, j] * Wq[k, j] in int32.  |acc| <= K * 127^2, which

@@ -368,3 +368,77 @@ def test_tiny_group_where_multiplier_overflows():
     assert xq[0, :4].tolist() == [127, -127, 0, 127]
     assert not xq[0, 4:].any()
     assert xs[0] == np.float32(np.float32(1e-38) / np.float32(127.0))
+
+
+# ---- static per-tensor activation scale (page "4.2 W8A8 量化与 SmoothQuant" 7.1) ----
+
+def _static_w8a8(X, W, alpha, calib):
+    """The W8A8 path with the per-tensor activation scale fixed by calibration."""
+    s = inv_s = None
+    if alpha is not None:
+        s, inv_s = oracle.smooth_factors(oracle.calib_absmax(calib), oracle.weight_rowmax(W), alpha)
+    a = oracle.static_act_max(calib, inv_s)
+    wq, ws = oracle.quant_weight(W, s)
+    xq, xs = oracle.quant_act_static(X, inv_s, a)
+    y32, _ = oracle.dequant(oracle.gemm_i8(xq, wq), xs, oracle.PER_TENSOR, ws)
+    return a, xq, xs, y32
+
+
+def test_static_scale_worked_example_errors(worked):
+    """Calibrating on X itself (as the worked example does), the static
+    per-tensor scale is the example's per-tensor scale: its two printed errors
+    (1.95 % unsmoothed, 0.15 % smoothed) and its steps 0.378 -> 0.0244 come out."""
+    g, X, W = worked
+    e = g["relative_error_percent"]["per_tensor_act_per_channel_w"]
+    st = g["per_tensor_step"]
+    Y = oracle.matmul_f64(X, W)
+    a0, _, xs0, y0 = _static_w8a8(X, W, None, X)
+    a1, xq1, xs1, y1 = _static_w8a8(X, W, g["alpha"], X)
+    assert a0 == np.float32(48.0)
+    assert round(float(xs0[0]), st["before_decimals"]) == st["before"]
+    assert round(float(xs1[0]), st["after_decimals"]) == st["after"]
+    assert xq1[:, 0].tolist() == g["channel1_codes"]["after"]
+    assert round(100 * oracle.rel_fro(y0, Y), e["before_decimals"]) == e["before"]
+    assert round(100 * oracle.rel_fro(y1, Y), e["after_decimals"]) == e["after"]
+
+
+def test_static_scale_clips_beyond_calibrated_range():
+    """Run-time values beyond the calibrated maximum saturate at +-127; the
+    scale does not move; values inside the range code as with a dynamic
+    per-tensor scale whose maximum is the calibrated one."""
+    rng = np.random.default_rng(11)
+    K = 64
+    calib = rng.standard_normal((32, K)).astype(np.float32)
+    inv_s = (0.5 + rng.random(K)).astype(np.float32)
+    a = oracle.static_act_max(calib, inv_s)
+    assert a == np.float32(np.abs(calib * inv_s[None, :]).max())
+    x = rng.standard_normal((4, K)).astype(np.float32)
+    x[1, 3] = 3.0 * a / inv_s[3]      # three times the calibrated range
+    x[2, 7] = -5.0 * a / inv_s[7]
+    xq, xs = oracle.quant_act_static(x, inv_s, a)
+    assert xs[0] == np.float32(a / np.float32(127.0))
+    assert xq[1, 3] == 127 and xq[2, 7] == -127
+    # inside the range: the same codes as a per-tensor quantization whose maximum is a
+    r = np.float32(127.0) / a
+    xp = (x * inv_s[None, :]).astype(np.float32)
+    inside = np.abs(xp) <= a
+    ref = np.clip(np.rint((xp * r).astype(np.float32)), -127, 127).astype(np.int8)
+    np.testing.assert_array_equal(xq[inside], ref[inside])
+
+
+def test_static_scale_equals_dynamic_on_its_own_calibration():
+    """Quantizing the calibration tensor itself with its static scale gives the
+    dynamic per-tensor result bit for bit."""
+    rng = np.random.default_rng(12)
+    calib = (rng.standard_normal((48, 96)) * np.where(rng.random(96) < 0.05, 80.0, 1.0)).astype(np.float32)
+    inv_s = (1.0 / (0.3 + rng.random(96))).astype(np.float32)
+    a = oracle.static_act_max(calib, inv_s)
+    xq_s, xs_s = oracle.quant_act_static(calib, inv_s, a)
+    xq_d, xs_d = oracle.quant_act(calib, inv_s, oracle.PER_TENSOR)
+    np.testing.assert_array_equal(xq_s, xq_d)
+    np.testing.assert_array_equal(xs_s, xs_d)
+
+
+def test_static_scale_zero():
+    xq, xs = oracle.quant_act_static(np.ones((2, 16), np.float32), None, 0.0)
+    assert xs[0] == 0.0 and not xq.any()
