@@ -205,6 +205,17 @@ def _large(torch, sq, synth, pipeline, dev):
                                            "one read + write for the codes")
     out["quant_act"] = rate(tm(lambda i: sq.sq_quant_act(inp.x, b.inv_s, sq.SQ_PER_TOKEN, b.xq, b.x_scale), reps=5),
                             3 * M * K + 4 * M + 4 * K)
+    # per-tensor activation scales: dynamic (a max pass, then codes) and static (calibrated max, one pass)
+    xs1 = torch.empty(1, dtype=torch.float32, device=dev)
+    ws_t = torch.empty(sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, M, N, K, sq.SQ_PER_TENSOR), dtype=torch.uint8,
+                       device=dev)
+    a_st = torch.empty(1, dtype=torch.float32, device=dev)
+    sq.sq_static_act_max(b.amax_x, b.inv_s, a_st)
+    out["quant_act_per_tensor_dynamic"] = rate(tm(lambda i: sq.sq_quant_act(inp.x, b.inv_s, sq.SQ_PER_TENSOR, b.xq,
+                                                                            xs1, ws_t), reps=5),
+                                               3 * M * K + 4 * K)
+    out["quant_act_per_tensor_static"] = rate(tm(lambda i: sq.sq_quant_act_static(inp.x, b.inv_s, a_st, b.xq, xs1),
+                                                 reps=5), 3 * M * K + 4 * K)
     us = tm(lambda i: sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y), reps=3)
     ops = 2.0 * M * N * K
     out["gemm_8192x12288x49152"] = {"us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),

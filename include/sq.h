@@ -189,6 +189,26 @@ sq_status sq_quant_act(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t
                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Static per-tensor activation scale (page "4.2 W8A8 量化与 SmoothQuant"
+ * section 7.1, export step: activation scales may come from the calibration
+ * statistics instead of being computed at run time).
+ *
+ * sq_static_act_max: a_static[0] = max_j fl(amax_x[j] * inv_s[j]), the
+ *   largest |X'| over the calibration tokens (amax_x from step 1, inv_s from
+ *   step 2, or NULL for unsmoothed activations).  K may be 0 (a = 0).
+ * sq_quant_act_static: step 4 with that fixed maximum: x_scale[0] =
+ *   fl(a/127), codes clamp(rne(fl(fl(x * inv_s_j) * fl(127/a))), -127, 127).
+ *   Run-time values beyond the calibrated range saturate at +-127; no
+ *   reduction over X runs, so the call is one pass and needs no workspace.
+ *   x, inv_s, xq as sq_quant_act; a_static is a device pointer to one float
+ *   (a >= 0).  The GEMM then takes x_scale with SQ_PER_TENSOR.
+ */
+sq_status sq_static_act_max(const float *amax_x, const float *inv_s, int64_t K, float *a_static,
+                            hipStream_t stream);
+sq_status sq_quant_act_static(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const float *inv_s,
+                              const float *a_static, int8_t *xq, float *x_scale, hipStream_t stream);
+
+/*
  * Step 5 -- INT8 GEMM with int32 accumulation and the dequantization epilogue
  * (page "4.2 W8A8 量化与 SmoothQuant" section 6: the runtime kernel is a plain
  * INT8 GEMM; page "量化：只压权重..." SmoothQuant W8A8: the activation scale

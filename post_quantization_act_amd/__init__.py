@@ -20,8 +20,8 @@ __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
     "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
-    "sq_gemm_w8a8", "sq_prepare_weights", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version",
-    "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
+    "sq_gemm_w8a8", "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_workspace_size",
+    "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -33,7 +33,7 @@ SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, S
 
 EXPORTED_SYMBOLS = (
     "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights",
-    "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
+    "sq_static_act_max", "sq_quant_act_static", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
 )
 
 
@@ -66,8 +66,10 @@ def lib() -> ctypes.CDLL:
     L.sq_quant_act.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.sq_gemm_w8a8.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
     L.sq_prepare_weights.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sq_static_act_max.argtypes = [vp, vp, i64, vp, vp]
+    L.sq_quant_act_static.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
-              "sq_prepare_weights"):
+              "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static"):
         getattr(L, f).restype = ctypes.c_int
     L.sq_workspace_size.argtypes = [i32, i64, i64, i64, i32]
     L.sq_workspace_size.restype = sz
@@ -221,6 +223,30 @@ def sq_prepare_weights(amax_x: torch.Tensor, w: torch.Tensor, alpha: float, s: t
     _check(lib().sq_prepare_weights(_ptr(amax_x), _ptr(w), _dtype(w), K, N, ld, ctypes.c_float(alpha), _ptr(s),
                                     _ptr(inv_s), _ptr(amax_w), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
                                     _stream(_dev(w, amax_x), stream)))
+
+
+def sq_static_act_max(amax_x: torch.Tensor, inv_s: torch.Tensor | None, a_static: torch.Tensor,
+                      stream=None) -> None:
+    """a_static[0] = max_j fl(amax_x[j] * inv_s[j]): the calibrated per-tensor maximum of X'."""
+    K = amax_x.shape[0]
+    _dense(amax_x, "amax_x", (K,), torch.float32)
+    if inv_s is not None:
+        _dense(inv_s, "inv_s", (K,), torch.float32)
+    _dense(a_static, "a_static", (1,), torch.float32)
+    _check(lib().sq_static_act_max(_ptr(amax_x), _ptr(inv_s), K, _ptr(a_static), _stream(_dev(amax_x), stream)))
+
+
+def sq_quant_act_static(x: torch.Tensor, inv_s: torch.Tensor | None, a_static: torch.Tensor, xq: torch.Tensor,
+                        x_scale: torch.Tensor, stream=None) -> None:
+    """Step 4 with the fixed per-tensor maximum a_static[0] (values beyond it saturate)."""
+    M, K, ld = _rows(x)
+    _dense(xq, "xq", (M, K), torch.int8)
+    _dense(x_scale, "x_scale", (1,), torch.float32)
+    _dense(a_static, "a_static", (1,), torch.float32)
+    if inv_s is not None:
+        _dense(inv_s, "inv_s", (K,), torch.float32)
+    _check(lib().sq_quant_act_static(_ptr(x), _dtype(x), M, K, ld, _ptr(inv_s), _ptr(a_static), _ptr(xq),
+                                     _ptr(x_scale), _stream(_dev(x), stream)))
 
 
 def sq_quant_act(x: torch.Tensor, inv_s: torch.Tensor | None, gran: int, xq: torch.Tensor,

@@ -256,6 +256,34 @@ sq_status sq_quant_act(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t
     return hip_result(e, fn);
 }
 
+sq_status sq_static_act_max(const float* amax_x, const float* inv_s, int64_t K, float* a_static, hipStream_t stream) {
+    const char* fn = "sq_static_act_max";
+    SQ_TRY(check_k(fn, K));
+    SQ_TRY(check_vec(fn, "amax_x", amax_x, K));
+    if (inv_s) SQ_TRY(check_vec(fn, "inv_s", inv_s, K));
+    SQ_TRY(check_vec(fn, "a_static", a_static, 1));
+    return hip_result(sqk::launch_static_max(amax_x, inv_s, K, a_static, stream), fn);
+}
+
+sq_status sq_quant_act_static(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const float* inv_s,
+                              const float* a_static, int8_t* xq, float* x_scale, hipStream_t stream) {
+    const char* fn = "sq_quant_act_static";
+    SQ_TRY(check_k(fn, K));
+    if (M > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
+    SQ_TRY(check_matrix(fn, "x", x, xt, M, K, ldx));
+    if (inv_s) SQ_TRY(check_vec(fn, "inv_s", inv_s, K, true));
+    SQ_TRY(check_vec(fn, "a_static", a_static, 1));
+    SQ_TRY(check_vec(fn, "x_scale", x_scale, M > 0 ? 1 : 0));
+    if (M > 0 && K > 0) {
+        if (!xq) return fail(SQ_ERR_INVALID_ARG, "%s: xq is NULL", fn);
+        if (!aligned16(xq)) return fail(SQ_ERR_INVALID_ARG, "%s: xq is not 16-byte aligned", fn);
+    }
+    if (M == 0) return ok();
+    // mode 2 of the activation kernels: codes from a given tensor maximum (read only)
+    uint32_t* a_bits = const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(a_static));
+    return hip_result(sqk::launch_quant_act(x, xt == SQ_BF16, M, K, ldx, inv_s, 2, xq, x_scale, a_bits, stream), fn);
+}
+
 sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_gran g, const int8_t* wq, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, void* y, sq_dtype yt, int32_t* acc_out, void* ws,
                        size_t ws_bytes, hipStream_t stream) {

@@ -29,6 +29,9 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
                                   float alpha, float* s, float* inv_s, float* amax_w, float* partial,
                                   uint32_t* colmax, hipStream_t st);
 
+// out[0] = max_j fl(amax_x[j] * inv_s[j]) (inv_s may be NULL).
+hipError_t launch_static_max(const float* amax_x, const float* inv_s, int64_t K, float* out, hipStream_t st);
+
 hipError_t launch_factors(const float* amax_x, const float* amax_w, int64_t K, float alpha, float* s,
                           float* inv_s, hipStream_t st);
 

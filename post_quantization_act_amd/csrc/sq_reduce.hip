@@ -318,6 +318,26 @@ __global__ __launch_bounds__(256) void k_colmax_reduce(const float* __restrict__
     colmax[k] = __float_as_uint(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
 }
 
+// Static per-tensor activation maximum from the calibration statistics:
+// a = max_j fl(amax_x[j] * inv_s[j]) (inv_s NULL: max_j amax_x[j]).  Rounding
+// is monotonic, so this is the largest |fl(x * inv_s_j)| of the calibration
+// tokens.  One block; out[0] is written, not accumulated.
+__global__ __launch_bounds__(1024) void k_static_max(const float* __restrict__ amax_x,
+                                                     const float* __restrict__ inv_s, int64_t K,
+                                                     float* __restrict__ out) {
+    __shared__ float red[16];
+    float m = 0.0f;
+    for (int64_t j = threadIdx.x; j < K; j += 1024) m = fmaxf(m, inv_s ? amax_x[j] * inv_s[j] : amax_x[j]);
+    m = wave_max(m);
+    if (threadIdx.x % kWave == 0) red[threadIdx.x / kWave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float r = red[0];
+        for (int i = 1; i < 16; ++i) r = fmaxf(r, red[i]);
+        out[0] = r;
+    }
+}
+
 // s and inv_s from both maxima already known (reuse of amax_w across alphas).
 __global__ __launch_bounds__(256) void k_factors(const float* __restrict__ amax_x,
                                                  const float* __restrict__ amax_w, int64_t K, float alpha,
@@ -446,6 +466,11 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, partial, nb, N, colmax);
+    return hipGetLastError();
+}
+
+hipError_t launch_static_max(const float* amax_x, const float* inv_s, int64_t K, float* out, hipStream_t st) {
+    hipLaunchKernelGGL(k_static_max, dim3(1), dim3(1024), 0, st, amax_x, inv_s, K, out);
     return hipGetLastError();
 }
 

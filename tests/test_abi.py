@@ -171,3 +171,11 @@ def test_prepare_weights_rejects():
     _expect(L.sq_prepare_weights(*args(K=33)), -1, "K = 33")
     _expect(L.sq_prepare_weights(*args(ws=None, wsb=0)), -3, "workspace")
     _expect(L.sq_prepare_weights(*args(wsb=64)), -3, "workspace")
+
+
+def test_static_scale_rejects():
+    L = _L()
+    _expect(L.sq_static_act_max(FAKE, None, 32, None, None), -1, "a_static is NULL")
+    _expect(L.sq_static_act_max(FAKE, None, 20, FAKE, None), -1, "multiple of 16")
+    _expect(L.sq_quant_act_static(FAKE, sq.SQ_BF16, 4, 32, 32, None, None, FAKE, FAKE, None), -1, "a_static is NULL")
+    _expect(L.sq_quant_act_static(FAKE, sq.SQ_BF16, 4, 32, 32, None, FAKE, MISALIGNED, FAKE, None), -1, "xq")
