@@ -62,6 +62,8 @@ def lib():
         L.sqo_static_act_max.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp]
         L.sqo_static_act_max.restype = ctypes.c_float
         L.sqo_quant_act_static.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_float, vp, i64, f32p]
+        L.sqo_fold_layernorm.argtypes = [vp, vp, vp, i64, vp, vp]
+        L.sqo_layernorm_quant.argtypes = [vp, i64, i64, i64, vp, vp, ctypes.c_float, vp, i64, f32p]
         L.sqo_gemm_i8.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i64, ctypes.c_int]
         L.sqo_dequant.argtypes = [vp, i64, f32p, ctypes.c_int, f32p, i64, i64, vp, vp, i64]
         L.sqo_quant_sym.argtypes = [f32p, i64, ctypes.c_int, vp, f32p]
@@ -181,6 +183,34 @@ def quant_act_static(x: np.ndarray, inv_s: np.ndarray | None, a: float):
     xs = np.empty(1, np.float32)
     _check(lib().sqo_quant_act_static(_p(x), _dtype_code(x), M, K, K, _p(ip), ctypes.c_float(float(a)), _p(xq),
                                       K, _p(xs)), "quant_act_static")
+    return xq, xs
+
+
+def fold_layernorm(gamma: np.ndarray, beta: np.ndarray | None, inv_s: np.ndarray):
+    """(gamma', beta') = (fl(gamma * inv_s), fl(beta * inv_s)); beta' is None without a bias."""
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    b = None if beta is None else np.ascontiguousarray(beta, dtype=np.float32)
+    i = np.ascontiguousarray(inv_s, dtype=np.float32)
+    K = g.size
+    go = np.empty(K, np.float32)
+    bo = None if b is None else np.empty(K, np.float32)
+    _check(lib().sqo_fold_layernorm(_p(g), _p(b), _p(i), K, _p(go), _p(bo)), "fold_layernorm")
+    return go, bo
+
+
+def layernorm_quant(x_bf16: np.ndarray, gamma: np.ndarray, beta: np.ndarray | None, eps: float):
+    """LayerNorm of each bf16 row (fp64 statistics) with gamma/beta, then per-token INT8:
+    (xq[M, K], x_scale[M])."""
+    x = np.ascontiguousarray(x_bf16)
+    if x.dtype != np.uint16:
+        raise TypeError("layernorm_quant takes bf16 bit patterns (uint16)")
+    M, K = x.shape
+    g = np.ascontiguousarray(gamma, dtype=np.float32)
+    b = None if beta is None else np.ascontiguousarray(beta, dtype=np.float32)
+    xq = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    _check(lib().sqo_layernorm_quant(_p(x), M, K, K, _p(g), _p(b), ctypes.c_float(eps), _p(xq), K, _p(xs)),
+           "layernorm_quant")
     return xq, xs
 
 

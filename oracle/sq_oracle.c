@@ -336,6 +336,73 @@ int sqo_quant_act_static(const void *x, int dtype, int64_t M, int64_t K, int64_t
     return 0;
 }
 
+/* ---- LayerNorm fold ([P3] section 6) ------------------------------------ */
+
+/* The smoothing folded into the LayerNorm in front of the linear layer:
+ * LN(x)_j / s_j = (x_j - mu) / sigma * (gamma_j / s_j) + beta_j / s_j, so
+ * gamma'_j = fl(gamma_j * inv_s_j) and beta'_j = fl(beta_j * inv_s_j) (division
+ * by s_j realised as the multiply by inv_s_j, as everywhere else).  beta may
+ * be NULL (no bias): beta_out is then left alone. */
+int sqo_fold_layernorm(const float *gamma, const float *beta, const float *inv_s, int64_t K, float *gamma_out,
+                       float *beta_out)
+{
+    if (K < 0 || !gamma || !inv_s || !gamma_out)
+        return -1;
+    for (int64_t j = 0; j < K; ++j) {
+        gamma_out[j] = gamma[j] * inv_s[j];
+        if (beta)
+            beta_out[j] = beta[j] * inv_s[j];
+    }
+    return 0;
+}
+
+/* LayerNorm of one bf16 token row followed by per-token symmetric INT8 codes
+ * (the runtime half of the fold: the row that reaches the GEMM is
+ * LN(x) diag(s)^-1).  Statistics in fp64: S1 = sum x_j and S2 = sum x_j^2,
+ * mu = S1 / K, var = max(S2 / K - mu^2, 0) (biased, as LayerNorm uses),
+ * rstd = 1 / sqrt(var + eps), each a single correctly rounded fp64
+ * operation.  Element j: n_j = (float)(((double)x_j - mu) * rstd), then
+ * z_j = fl(fl(n_j * gamma_j) + beta_j) in fp32; the row's codes and scale
+ * are those of step 4 per token.  beta NULL: no bias term. */
+int sqo_layernorm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *gamma,
+                        const float *beta, float eps, int8_t *xq, int64_t ldq, float *x_scale)
+{
+    if (M < 0 || K <= 0 || ldx < K || ldq < K || !gamma)
+        return -1;
+    float *z = (float *)malloc((size_t)K * sizeof(float));
+    if (!z)
+        return -2;
+    for (int64_t i = 0; i < M; ++i) {
+        const uint16_t *row = x + i * ldx;
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t j = 0; j < K; ++j) {
+            double v = (double)bf16_bits_to_float(row[j]);
+            s1 += v;
+            s2 += v * v;
+        }
+        double mu = s1 / (double)K;
+        double var = s2 / (double)K - mu * mu;
+        if (var < 0.0)
+            var = 0.0;
+        double rstd = 1.0 / sqrt(var + (double)eps);
+        float m = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            float n = (float)(((double)bf16_bits_to_float(row[j]) - mu) * rstd);
+            float t = n * gamma[j];
+            z[j] = beta ? t + beta[j] : t;
+            float a = fabsf(z[j]);
+            if (a > m)
+                m = a;
+        }
+        float r;
+        sym_scale(m, 127.0f, &x_scale[i], &r);
+        for (int64_t j = 0; j < K; ++j)
+            xq[i * ldq + j] = (int8_t)sym_code(z[j], r, 127.0f);
+    }
+    free(z);
+    return 0;
+}
+
 /* ---- step 5: INT8 x INT8 -> int32 GEMM and dequantization --------------- */
 
 /* acc[i, k] = sum_j Xq[i, j] * Wq[k, j] in int32.  |acc| <= K * 127^2, which

@@ -442,3 +442,105 @@ def test_static_scale_equals_dynamic_on_its_own_calibration():
 def test_static_scale_zero():
     xq, xs = oracle.quant_act_static(np.ones((2, 16), np.float32), None, 0.0)
     assert xs[0] == 0.0 and not xq.any()
+
+
+# ---- LayerNorm fold (page "4.2 W8A8 量化与 SmoothQuant" section 6) -------------
+
+def _bf16(a):
+    return oracle.f32_to_bf16(np.asarray(a, np.float32))
+
+
+def test_layernorm_quant_closed_form():
+    """x = [1, 2, 3, 4], gamma = 1, beta = 0, eps = 0: mu = 2.5, var = 1.25, so
+    LN(x) = (x - 2.5) / sqrt(1.25) = [-1.342, -0.447, 0.447, 1.342]; per-token
+    codes 127 * LN / max|LN| = [-127, -42, 42, 127] (-42.33 rounds to -42)."""
+    x = _bf16([[1, 2, 3, 4]])
+    xq, xs = oracle.layernorm_quant(x, np.ones(4, np.float32), None, 0.0)
+    assert xq.tolist() == [[-127, -42, 42, 127]]
+    assert abs(float(xs[0]) - 1.5 / np.sqrt(1.25) / 127) < 1e-7
+
+
+def _ln_ref(xf, gamma, beta, eps):
+    mu = xf.mean(axis=1, keepdims=True)
+    var = ((xf - mu) ** 2).mean(axis=1, keepdims=True)
+    return (xf - mu) / np.sqrt(var + eps) * gamma[None, :] + (0 if beta is None else beta[None, :])
+
+
+@pytest.mark.parametrize("eps", [1e-5, 1e-3])
+def test_layernorm_quant_matches_fp64_layernorm(eps):
+    """Against numpy's fp64 LayerNorm (biased variance, eps inside the root,
+    gamma then beta): scales agree to fp32 rounding, codes agree except for
+    rare ties broken the other way (by at most 1)."""
+    rng = np.random.default_rng(21)
+    M, K = 64, 512
+    xf = (rng.standard_normal((M, K)) * np.where(rng.random(K) < 0.02, 30.0, 1.0) + 0.3).astype(np.float32)
+    x = _bf16(xf)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    gamma = (0.5 + rng.random(K)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(K)).astype(np.float32)
+    xq, xs = oracle.layernorm_quant(x, gamma, beta, eps)
+    z = _ln_ref(xf, gamma.astype(np.float64), beta.astype(np.float64), eps)
+    m = np.abs(z).max(axis=1)
+    np.testing.assert_allclose(xs, m / 127, rtol=3e-7)
+    ref = np.clip(np.rint(z * (127 / m)[:, None]), -127, 127)
+    d = np.abs(xq.astype(np.int64) - ref)
+    assert d.max() <= 1 and (d > 0).mean() < 1e-3
+
+
+def test_layernorm_quant_constant_row_is_beta():
+    """A constant row has zero variance: LN(x) = beta exactly, whatever eps."""
+    K = 32
+    beta = np.linspace(-1.0, 1.0, K).astype(np.float32)
+    x = _bf16(np.full((1, K), 3.25))
+    xq, xs = oracle.layernorm_quant(x, np.ones(K, np.float32), beta, 1e-5)
+    q, s = oracle.quant_act(beta[None, :], None, oracle.PER_TOKEN)
+    np.testing.assert_array_equal(xq, q)
+    np.testing.assert_array_equal(xs, s)
+
+
+def test_fold_is_layernorm_times_inverse_factor():
+    """LN with (gamma / s, beta / s) is LN(x) diag(s)^-1: against the fp64
+    LayerNorm divided by s, codes agree within 1 and scales to fp32 rounding."""
+    rng = np.random.default_rng(22)
+    M, K = 32, 256
+    x = _bf16(rng.standard_normal((M, K)) * 2.0)
+    gamma = (0.5 + rng.random(K)).astype(np.float32)
+    beta = (0.2 * rng.standard_normal(K)).astype(np.float32)
+    s = np.exp(rng.standard_normal(K)).astype(np.float32)
+    inv_s = (np.float32(1.0) / s).astype(np.float32)
+    g2, b2 = oracle.fold_layernorm(gamma, beta, inv_s)
+    np.testing.assert_array_equal(g2, (gamma * inv_s).astype(np.float32))
+    xq, xs = oracle.layernorm_quant(x, g2, b2, 1e-5)
+    z = _ln_ref(oracle.bf16_to_f32(x).astype(np.float64), gamma.astype(np.float64), beta.astype(np.float64),
+                1e-5) / s.astype(np.float64)[None, :]
+    m = np.abs(z).max(axis=1)
+    np.testing.assert_allclose(xs, m / 127, rtol=1e-6)
+    ref = np.clip(np.rint(z * (127 / m)[:, None]), -127, 127)
+    assert np.abs(xq.astype(np.int64) - ref).max() <= 1
+
+
+def test_folded_w8a8_error_matches_smoothed_path():
+    """The folded runtime (LN with gamma', beta' -> per-token codes -> GEMM with
+    diag(s) W codes) reaches about the error of quantizing LN(x) diag(s)^-1
+    directly, far below the unsmoothed error on outlier channels."""
+    rng = np.random.default_rng(23)
+    M, K, N = 96, 512, 128
+    x = _bf16(rng.standard_normal((M, K)))
+    out = rng.choice(K, 6, replace=False)
+    gamma = np.ones(K, np.float32)
+    gamma[out] = 60.0  # outlier channels come from the LayerNorm weight
+    beta = (0.05 * rng.standard_normal(K)).astype(np.float32)
+    w = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    ln = _ln_ref(oracle.bf16_to_f32(x).astype(np.float64), gamma.astype(np.float64), beta.astype(np.float64),
+                 1e-5).astype(np.float32)
+    Y = oracle.matmul_f64(ln, w)
+    s, inv_s = oracle.smooth_factors(oracle.calib_absmax(ln), oracle.weight_rowmax(w), 0.5)
+    g2, b2 = oracle.fold_layernorm(gamma, beta, inv_s)
+    xq, xs = oracle.layernorm_quant(x, g2, b2, 1e-5)
+    wq, ws = oracle.quant_weight(w, s)
+    y_fold, _ = oracle.dequant(oracle.gemm_i8(xq, wq), xs, oracle.PER_TOKEN, ws)
+    e_fold = oracle.rel_fro(y_fold, Y)
+    e_direct = oracle.rel_fro(oracle.w8a8_linear(ln, w, 0.5, oracle.PER_TOKEN)["y32"], Y)
+    e_plain = oracle.rel_fro(oracle.w8a8_linear(ln, w, None, oracle.PER_TOKEN)["y32"], Y)
+    assert abs(e_fold - e_direct) < 0.1 * e_direct
+    assert e_fold < 0.5 * e_plain
