@@ -358,32 +358,49 @@ int sqo_fold_layernorm(const float *gamma, const float *beta, const float *inv_s
 
 /* LayerNorm of one bf16 token row followed by per-token symmetric INT8 codes
  * (the runtime half of the fold: the row that reaches the GEMM is
- * LN(x) diag(s)^-1).  Statistics in fp64: S1 = sum x_j and S2 = sum x_j^2,
- * mu = S1 / K, var = max(S2 / K - mu^2, 0) (biased, as LayerNorm uses),
- * rstd = 1 / sqrt(var + eps), each a single correctly rounded fp64
- * operation.  Element j: n_j = (float)(((double)x_j - mu) * rstd), then
- * z_j = fl(fl(n_j * gamma_j) + beta_j) in fp32; the row's codes and scale
- * are those of step 4 per token.  beta NULL: no bias term. */
+ * LN(x) diag(s)^-1).  The pages give the LayerNorm formula but not its
+ * arithmetic; the statistics are taken on a fixed-point grid so that they do
+ * not depend on the order of summation: with 2^E the power of two just above
+ * the row's largest magnitude (frexp), each x_j is truncated toward zero to a
+ * multiple of 2^(E - 40) and each x_j^2 to a multiple of 2^(2E - 40), and the
+ * integers are summed exactly (|sum| < K 2^40 <= 2^54 for K <= 16384):
+ *   mu = S1 2^(E-40) / K,  var = max(S2 2^(2E-40) / K - mu^2, 0)  (biased),
+ *   rstd = 1 / sqrt(var + eps), all in fp64 with single roundings.
+ * Element j: n_j = (float)((x_j - mu) * rstd) (fp64 product rounded once to
+ * fp32), z_j = fl(fl(n_j * gamma_j) + beta_j).  The row's codes and scale are
+ * those of step 4 per token.  beta NULL: no bias term. */
 int sqo_layernorm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *gamma,
                         const float *beta, float eps, int8_t *xq, int64_t ldq, float *x_scale)
 {
-    if (M < 0 || K <= 0 || ldx < K || ldq < K || !gamma)
+    if (M < 0 || K <= 0 || K > 16384 || ldx < K || ldq < K || !gamma)
         return -1;
     float *z = (float *)malloc((size_t)K * sizeof(float));
     if (!z)
         return -2;
     for (int64_t i = 0; i < M; ++i) {
         const uint16_t *row = x + i * ldx;
-        double s1 = 0.0, s2 = 0.0;
+        float xmax = 0.0f;
         for (int64_t j = 0; j < K; ++j) {
-            double v = (double)bf16_bits_to_float(row[j]);
-            s1 += v;
-            s2 += v * v;
+            float a = fabsf(bf16_bits_to_float(row[j]));
+            if (a > xmax)
+                xmax = a;
         }
-        double mu = s1 / (double)K;
-        double var = s2 / (double)K - mu * mu;
-        if (var < 0.0)
-            var = 0.0;
+        double mu = 0.0, var = 0.0;
+        if (xmax > 0.0f) {
+            int E;
+            frexpf(xmax, &E);
+            const double c1 = ldexp(1.0, 40 - E), c2 = ldexp(1.0, 40 - 2 * E);
+            int64_t s1 = 0, s2 = 0;
+            for (int64_t j = 0; j < K; ++j) {
+                double v = (double)bf16_bits_to_float(row[j]);
+                s1 += (int64_t)(v * c1);
+                s2 += (int64_t)(v * v * c2);
+            }
+            mu = ldexp((double)s1, E - 40) / (double)K;
+            var = ldexp((double)s2, 2 * E - 40) / (double)K - mu * mu;
+            if (var < 0.0)
+                var = 0.0;
+        }
         double rstd = 1.0 / sqrt(var + (double)eps);
         float m = 0.0f;
         for (int64_t j = 0; j < K; ++j) {
