@@ -216,6 +216,12 @@ def _large(torch, sq, synth, pipeline, dev):
                                                3 * M * K + 4 * K)
     out["quant_act_per_tensor_static"] = rate(tm(lambda i: sq.sq_quant_act_static(inp.x, b.inv_s, a_st, b.xq, xs1),
                                                  reps=5), 3 * M * K + 4 * K)
+    # LayerNorm fold: the runtime LayerNorm + per-token codes with 1/s folded into gamma and beta
+    gam = torch.ones(K, dtype=torch.float32, device=dev)
+    bet = torch.zeros(K, dtype=torch.float32, device=dev)
+    sq.sq_fold_layernorm(gam, bet, b.inv_s, gam, bet)
+    out["layernorm_quant"] = rate(tm(lambda i: sq.sq_layernorm_quant(inp.x, gam, bet, 1e-5, b.xq, b.x_scale),
+                                     reps=5), 3 * M * K + 4 * M + 8 * K)
     us = tm(lambda i: sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y), reps=3)
     ops = 2.0 * M * N * K
     out["gemm_8192x12288x49152"] = {"us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),

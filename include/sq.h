@@ -189,6 +189,33 @@ sq_status sq_quant_act(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t
                        size_t ws_bytes, hipStream_t stream);
 
 /*
+ * LayerNorm fold (page "4.2 W8A8 量化与 SmoothQuant" section 6: the factor
+ * 1/s_j folds into the LayerNorm in front of the layer,
+ * LN(x)_j / s_j = (x_j - mu) / sigma * gamma_j / s_j + beta_j / s_j, so the
+ * runtime needs no separate smoothing multiply).
+ *
+ * sq_fold_layernorm: offline, gamma_out[j] = fl(gamma[j] * inv_s[j]) and
+ *   beta_out[j] = fl(beta[j] * inv_s[j]) (beta may be NULL: no bias, beta_out
+ *   unused).  All [K] fp32 device vectors; outputs may alias the inputs.
+ * sq_layernorm_quant: at run time, LayerNorm of each bf16 token row of
+ *   x [M, K] with the folded gamma/beta, then per-token INT8 codes (step 4
+ *   with the smoothing already inside gamma/beta):
+ *     S1 = sum_j x_j, S2 = sum_j x_j^2 in fp64; mu = S1 / K;
+ *     var = max(S2 / K - mu^2, 0); rstd = 1 / sqrt(var + eps) (fp64);
+ *     z_j = fl(fl((float)((x_j - mu) * rstd) * gamma_j) + beta_j);
+ *     x_scale[i] = fl(m_i / 127), codes clamp(rne(fl(z_j * fl(127 / m_i)))).
+ *   The fp64 sums are exact (so the result does not depend on the order of
+ *   summation) when a row's magnitudes span less than 2^29; results are
+ *   specified under that condition.  x: bf16 only (SQ_ERR_UNSUPPORTED
+ *   otherwise), 16-byte aligned rows; K <= 16384; gamma (and beta) 16-byte
+ *   aligned; xq [M, K] and x_scale [M] as sq_quant_act per token.
+ */
+sq_status sq_fold_layernorm(const float *gamma, const float *beta, const float *inv_s, int64_t K, float *gamma_out,
+                            float *beta_out, hipStream_t stream);
+sq_status sq_layernorm_quant(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const float *gamma,
+                             const float *beta, float eps, int8_t *xq, float *x_scale, hipStream_t stream);
+
+/*
  * Static per-tensor activation scale (page "4.2 W8A8 量化与 SmoothQuant"
  * section 7.1, export step: activation scales may come from the calibration
  * statistics instead of being computed at run time).

@@ -20,7 +20,8 @@ __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
     "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
-    "sq_gemm_w8a8", "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_workspace_size",
+    "sq_gemm_w8a8", "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
+    "sq_layernorm_quant", "sq_workspace_size",
     "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +34,7 @@ SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, S
 
 EXPORTED_SYMBOLS = (
     "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights",
-    "sq_static_act_max", "sq_quant_act_static", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
+    "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
 )
 
 
@@ -68,8 +69,11 @@ def lib() -> ctypes.CDLL:
     L.sq_prepare_weights.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.sq_static_act_max.argtypes = [vp, vp, i64, vp, vp]
     L.sq_quant_act_static.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.sq_fold_layernorm.argtypes = [vp, vp, vp, i64, vp, vp, vp]
+    L.sq_layernorm_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, f32, vp, vp, vp]
     for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
-              "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static"):
+              "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
+              "sq_layernorm_quant"):
         getattr(L, f).restype = ctypes.c_int
     L.sq_workspace_size.argtypes = [i32, i64, i64, i64, i32]
     L.sq_workspace_size.restype = sz
@@ -223,6 +227,32 @@ def sq_prepare_weights(amax_x: torch.Tensor, w: torch.Tensor, alpha: float, s: t
     _check(lib().sq_prepare_weights(_ptr(amax_x), _ptr(w), _dtype(w), K, N, ld, ctypes.c_float(alpha), _ptr(s),
                                     _ptr(inv_s), _ptr(amax_w), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
                                     _stream(_dev(w, amax_x), stream)))
+
+
+def sq_fold_layernorm(gamma: torch.Tensor, beta: torch.Tensor | None, inv_s: torch.Tensor, gamma_out: torch.Tensor,
+                      beta_out: torch.Tensor | None = None, stream=None) -> None:
+    """gamma_out = gamma * inv_s, beta_out = beta * inv_s (fp32, [K]): the smoothing folded into a LayerNorm."""
+    K = gamma.shape[0]
+    for t, n in ((gamma, "gamma"), (inv_s, "inv_s"), (gamma_out, "gamma_out")):
+        _dense(t, n, (K,), torch.float32)
+    if beta is not None:
+        _dense(beta, "beta", (K,), torch.float32)
+        _dense(beta_out, "beta_out", (K,), torch.float32)
+    _check(lib().sq_fold_layernorm(_ptr(gamma), _ptr(beta), _ptr(inv_s), K, _ptr(gamma_out), _ptr(beta_out),
+                                   _stream(_dev(gamma), stream)))
+
+
+def sq_layernorm_quant(x: torch.Tensor, gamma: torch.Tensor, beta: torch.Tensor | None, eps: float,
+                       xq: torch.Tensor, x_scale: torch.Tensor, stream=None) -> None:
+    """LayerNorm of bf16 rows x [M, K] with (folded) gamma/beta, then per-token INT8 codes and scales."""
+    M, K, ld = _rows(x)
+    _dense(gamma, "gamma", (K,), torch.float32)
+    if beta is not None:
+        _dense(beta, "beta", (K,), torch.float32)
+    _dense(xq, "xq", (M, K), torch.int8)
+    _dense(x_scale, "x_scale", (M,), torch.float32)
+    _check(lib().sq_layernorm_quant(_ptr(x), _dtype(x), M, K, ld, _ptr(gamma), _ptr(beta), ctypes.c_float(eps),
+                                    _ptr(xq), _ptr(x_scale), _stream(_dev(x), stream)))
 
 
 def sq_static_act_max(amax_x: torch.Tensor, inv_s: torch.Tensor | None, a_static: torch.Tensor,

@@ -256,6 +256,38 @@ sq_status sq_quant_act(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t
     return hip_result(e, fn);
 }
 
+sq_status sq_fold_layernorm(const float* gamma, const float* beta, const float* inv_s, int64_t K, float* gamma_out,
+                            float* beta_out, hipStream_t stream) {
+    const char* fn = "sq_fold_layernorm";
+    if (K < 0) return fail(SQ_ERR_INVALID_ARG, "%s: K = %lld is negative", fn, (long long)K);
+    SQ_TRY(check_vec(fn, "gamma", gamma, K));
+    SQ_TRY(check_vec(fn, "inv_s", inv_s, K));
+    SQ_TRY(check_vec(fn, "gamma_out", gamma_out, K));
+    if (beta) SQ_TRY(check_vec(fn, "beta_out", beta_out, K));
+    return hip_result(sqk::launch_fold_ln(gamma, beta, inv_s, K, gamma_out, beta_out, stream), fn);
+}
+
+sq_status sq_layernorm_quant(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const float* gamma,
+                             const float* beta, float eps, int8_t* xq, float* x_scale, hipStream_t stream) {
+    const char* fn = "sq_layernorm_quant";
+    SQ_TRY(check_k(fn, K));
+    if (xt != SQ_BF16) return fail(SQ_ERR_UNSUPPORTED, "%s: only bf16 rows are supported", fn);
+    if (K > 16384) return fail(SQ_ERR_UNSUPPORTED, "%s: K = %lld above 16384", fn, (long long)K);
+    if (M > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
+    if (!(eps >= 0.0f)) return fail(SQ_ERR_INVALID_ARG, "%s: eps = %g must be >= 0", fn, eps);
+    SQ_TRY(check_matrix(fn, "x", x, xt, M, K, ldx));
+    SQ_TRY(check_vec(fn, "gamma", gamma, K, true));
+    if (beta) SQ_TRY(check_vec(fn, "beta", beta, K, true));
+    SQ_TRY(check_vec(fn, "x_scale", x_scale, M));
+    if (M > 0 && K > 0) {
+        if (!xq) return fail(SQ_ERR_INVALID_ARG, "%s: xq is NULL", fn);
+        if (!aligned16(xq)) return fail(SQ_ERR_INVALID_ARG, "%s: xq is not 16-byte aligned", fn);
+    }
+    if (M == 0) return ok();
+    if (K == 0) return hip_result(sqk::launch_fill_u32(reinterpret_cast<uint32_t*>(x_scale), M, 0u, stream), fn);
+    return hip_result(sqk::launch_ln_quant(x, M, K, ldx, gamma, beta, eps, xq, x_scale, stream), fn);
+}
+
 sq_status sq_static_act_max(const float* amax_x, const float* inv_s, int64_t K, float* a_static, hipStream_t stream) {
     const char* fn = "sq_static_act_max";
     SQ_TRY(check_k(fn, K));

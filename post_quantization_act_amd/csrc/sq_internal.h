@@ -46,6 +46,14 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, const float* inv_s,
                             int mode, int8_t* xq, float* x_scale, uint32_t* gmax, hipStream_t st);
 
+// LayerNorm fold: gamma_out = fl(gamma * inv_s), beta_out = fl(beta * inv_s) (beta may be NULL).
+hipError_t launch_fold_ln(const float* gamma, const float* beta, const float* inv_s, int64_t K, float* gamma_out,
+                          float* beta_out, hipStream_t st);
+// LayerNorm (fp64 statistics) of bf16 rows with gamma/beta, then per-token codes; K / 8 <= 2048
+// (hipErrorNotSupported beyond).
+hipError_t launch_ln_quant(const void* x, int64_t M, int64_t K, int64_t ld, const float* gamma, const float* beta,
+                           float eps, int8_t* xq, float* x_scale, hipStream_t st);
+
 // INT8 GEMM + dequant epilogue.
 hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
                             const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16,

@@ -285,6 +285,157 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
     return hipGetLastError();
 }
 
+// ---- fused LayerNorm + per-token codes (the runtime half of the LN fold) ----------
+//
+// Same row layout as k_quant_act (WPR wavefronts per bf16 token row, NV groups
+// of 8 channels per thread, the row in registers).  The statistics use a
+// fixed-point grid so no reduction order can change them: with 2^E the power
+// of two just above the row's largest magnitude, x_j is truncated toward zero
+// to a multiple of 2^(E-40) and x_j^2 to a multiple of 2^(2E-40), and those
+// integers are summed exactly in int64 (K <= 16384 keeps |sum| < 2^54).  Then
+// mu = S1 2^(E-40) / K, var = max(S2 2^(2E-40) / K - mu^2, 0),
+// rstd = 1 / sqrt(var + eps) in fp64; element j: n = (float)((x_j - mu) rstd),
+// z = fl(fl(n g_j) + b_j) with the folded LayerNorm weight g and bias b; then
+// the row's max |z|, scale and codes as in step 4.
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+template <int NV, int WPR>
+__global__ __launch_bounds__(256) void k_ln_quant(const bf16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld,
+                                                  const float* __restrict__ gamma, const float* __restrict__ beta,
+                                                  float eps, int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+    constexpr int kRowsPerBlock = 4 / WPR;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int row_in_block = wave / WPR;
+    const int t = (wave % WPR) * kWave + lane;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + row_in_block;
+    const bool valid = row < M;
+    const int64_t groups = K / 8;
+
+    float v[NV][8];
+    float xm = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t g = t + (int64_t)q * (WPR * kWave);
+        if (valid && g < groups) {
+            load8(x + row * ld + g * 8, v[q]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xm = fmaxf(xm, fabsf(v[q][i]));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[q][i] = 0.0f;
+        }
+    }
+    __shared__ float redm[4];
+    __shared__ int64_t red1[4], red2[4];
+    xm = wave_max(xm);
+    if constexpr (WPR > 1) {
+        if (lane == 0) redm[wave] = xm;
+        __syncthreads();
+        const int w0 = row_in_block * WPR;
+        xm = redm[w0];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) xm = fmaxf(xm, redm[w0 + i]);
+        __syncthreads();  // redm is reused below
+    }
+    int E = 0;
+    frexpf(xm, &E);
+    const double c1 = ldexp(1.0, 40 - E), c2 = ldexp(1.0, 40 - 2 * E);
+    int64_t s1 = 0, s2 = 0;
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double d = (double)v[q][i];
+            s1 += (int64_t)(d * c1);
+            s2 += (int64_t)(d * d * c2);
+        }
+    // convert again below rather than keeping 8 doubles per group alive
+#pragma unroll
+    for (int q = 0; q < NV; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[q][i]));
+    s1 = wave_sum_i64(s1);
+    s2 = wave_sum_i64(s2);
+    if constexpr (WPR > 1) {
+        if (lane == 0) {
+            red1[wave] = s1;
+            red2[wave] = s2;
+        }
+        __syncthreads();
+        const int w0 = row_in_block * WPR;
+        s1 = red1[w0];
+        s2 = red2[w0];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) {
+            s1 += red1[w0 + i];
+            s2 += red2[w0 + i];
+        }
+    }
+    double mu = 0.0, var = 0.0;
+    if (xm > 0.0f) {
+        mu = ldexp((double)s1, E - 40) / (double)K;
+        var = ldexp((double)s2, 2 * E - 40) / (double)K - mu * mu;
+        if (var < 0.0) var = 0.0;
+    }
+    const double rstd = 1.0 / sqrt(var + (double)eps);
+
+    float m = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t g = t + (int64_t)q * (WPR * kWave);
+        if (valid && g < groups) {
+            const float4 ga = *reinterpret_cast<const float4*>(gamma + g * 8);
+            const float4 gb = *reinterpret_cast<const float4*>(gamma + g * 8 + 4);
+            const float gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+            float bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (beta) {
+                const float4 ba = *reinterpret_cast<const float4*>(beta + g * 8);
+                const float4 bb = *reinterpret_cast<const float4*>(beta + g * 8 + 4);
+                bw[0] = ba.x; bw[1] = ba.y; bw[2] = ba.z; bw[3] = ba.w;
+                bw[4] = bb.x; bw[5] = bb.y; bw[6] = bb.z; bw[7] = bb.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float n = (float)(((double)v[q][i] - mu) * rstd);
+                const float tt = n * gw[i];
+                v[q][i] = beta ? tt + bw[i] : tt;
+                m = fmaxf(m, fabsf(v[q][i]));
+            }
+        }
+    }
+    m = wave_max(m);
+    if constexpr (WPR > 1) {
+        if (lane == 0) redm[wave] = m;
+        __syncthreads();
+        const int w0 = row_in_block * WPR;
+        m = redm[w0];
+#pragma unroll
+        for (int i = 1; i < WPR; ++i) m = fmaxf(m, redm[w0 + i]);
+    }
+    float scale, r;
+    group_scale(m, scale, r);
+    if (!valid) return;
+    if (t == 0) x_scale[row] = scale;
+    auto code_row = [&](auto fast) {
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int64_t g = t + (int64_t)q * (WPR * kWave);
+            if (g < groups) {
+                int c[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
+                st8_stream(xq + row * K + g * 8, make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+            }
+        }
+    };
+    if (r <= 3.402823466e38f) code_row(std::true_type{});
+    else code_row(std::false_type{});
+}
+
 template <typename T, int NV, int WPR>
 static void launch_act_rows(const T* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode, int8_t* xq,
                             float* x_scale, uint32_t* gmax, hipStream_t st) {
@@ -307,6 +458,49 @@ static void dispatch_act(const T* x, int64_t M, int64_t K, int64_t ld, const flo
     if (groups <= 8 * 4 * kWave) return launch_act_rows<T, 8, 4>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
     hipLaunchKernelGGL((k_quant_act_long<T>), dim3((unsigned)M), dim3(256), 0, st, x, M, K, ld, inv_s, mode, xq,
                        x_scale, gmax);
+}
+
+template <int NV, int WPR>
+static void launch_ln_rows(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* gamma, const float* beta,
+                           float eps, int8_t* xq, float* x_scale, hipStream_t st) {
+    constexpr int rpb = 4 / WPR;
+    const int64_t blocks = (M + rpb - 1) / rpb;
+    hipLaunchKernelGGL((k_ln_quant<NV, WPR>), dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ld, gamma, beta, eps,
+                       xq, x_scale);
+}
+
+hipError_t launch_ln_quant(const void* x, int64_t M, int64_t K, int64_t ld, const float* gamma, const float* beta,
+                           float eps, int8_t* xq, float* x_scale, hipStream_t st) {
+    if (M <= 0) return hipSuccess;
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const int64_t groups = K / 8;
+    if (groups <= 1 * kWave) launch_ln_rows<1, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else if (groups <= 2 * kWave) launch_ln_rows<2, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else if (groups <= 4 * kWave) launch_ln_rows<4, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else if (groups <= 8 * kWave) launch_ln_rows<8, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else if (groups <= 4 * 4 * kWave) launch_ln_rows<4, 4>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else if (groups <= 6 * 4 * kWave) launch_ln_rows<6, 4>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else if (groups <= 8 * 4 * kWave) launch_ln_rows<8, 4>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
+    else return hipErrorNotSupported;
+    return hipGetLastError();
+}
+
+// gamma_out[j] = fl(gamma[j] * inv_s[j]); beta_out likewise when beta is given.
+__global__ __launch_bounds__(256) void k_fold_ln(const float* __restrict__ gamma, const float* __restrict__ beta,
+                                                 const float* __restrict__ inv_s, int64_t K,
+                                                 float* __restrict__ gamma_out, float* __restrict__ beta_out) {
+    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= K) return;
+    gamma_out[j] = gamma[j] * inv_s[j];
+    if (beta) beta_out[j] = beta[j] * inv_s[j];
+}
+
+hipError_t launch_fold_ln(const float* gamma, const float* beta, const float* inv_s, int64_t K, float* gamma_out,
+                          float* beta_out, hipStream_t st) {
+    if (K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_fold_ln, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, st, gamma, beta, inv_s, K,
+                       gamma_out, beta_out);
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, const float* inv_s,

@@ -179,3 +179,16 @@ def test_static_scale_rejects():
     _expect(L.sq_static_act_max(FAKE, None, 20, FAKE, None), -1, "multiple of 16")
     _expect(L.sq_quant_act_static(FAKE, sq.SQ_BF16, 4, 32, 32, None, None, FAKE, FAKE, None), -1, "a_static is NULL")
     _expect(L.sq_quant_act_static(FAKE, sq.SQ_BF16, 4, 32, 32, None, FAKE, MISALIGNED, FAKE, None), -1, "xq")
+
+
+def test_layernorm_rejects():
+    L = _L()
+    f = ctypes.c_float
+    _expect(L.sq_layernorm_quant(FAKE, sq.SQ_F32, 4, 32, 32, FAKE, None, f(1e-5), FAKE, FAKE, None), -2, "bf16")
+    _expect(L.sq_layernorm_quant(FAKE, sq.SQ_BF16, 4, 16400, 16400, FAKE, None, f(1e-5), FAKE, FAKE, None), -2,
+            "16384")
+    _expect(L.sq_layernorm_quant(FAKE, sq.SQ_BF16, 4, 32, 32, None, None, f(1e-5), FAKE, FAKE, None), -1,
+            "gamma is NULL")
+    _expect(L.sq_layernorm_quant(FAKE, sq.SQ_BF16, 4, 32, 32, FAKE, None, f(-1.0), FAKE, FAKE, None), -1, "eps")
+    _expect(L.sq_fold_layernorm(None, None, FAKE, 8, FAKE, None, None), -1, "gamma is NULL")
+    _expect(L.sq_fold_layernorm(FAKE, FAKE, FAKE, 8, FAKE, None, None), -1, "beta_out is NULL")
