@@ -249,7 +249,15 @@ def _large(torch, sq, synth, pipeline, dev):
     sq.sq_quant_weight(inp.w, None, bt.wq, bt.w_scale, bt.ws_w)
     pipeline.forward(xs_, sq.SQ_PER_TENSOR, bt, smoothed=False)
     base_ten = float(torch.linalg.norm(bt.y.double() - y_ref)) / ref_norm
+    grid = [round(0.05 * i, 2) for i in range(21)]
+    t0 = time.perf_counter()
+    best, errs = pipeline.search_alpha(xs_, inp.w, b.amax_x, grid)
+    torch.cuda.synchronize()
+    search = {"grid": "0.00 .. 1.00 step 0.05", "best_alpha": best, "best_error": round(errs[best], 6),
+              "seconds": round(time.perf_counter() - t0, 3),
+              "errors": {f"{a:.2f}": round(e, 6) for a, e in errs.items()}}
     out_sweep = {"workload": cfg.name, "sample_tokens": 256, "output": "fp32", "reference": "X W in fp64",
+                 "search": search,
                  "metric": "relative Frobenius error", "smoothed_per_token": sweep,
                  "unsmoothed_per_token": round(base_tok, 6), "unsmoothed_per_tensor": round(base_ten, 6)}
     del inp, b, bs, bt, y_ref

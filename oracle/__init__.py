@@ -275,6 +275,20 @@ def w8a8_linear(x, w, alpha: float | None, gran: int = PER_TOKEN, calib=None, nt
     return out
 
 
+def search_alpha(x, w, calib, alphas, gran: int = PER_TOKEN, nthreads: int = 8):
+    """Offline migration-strength search (page "4.2 W8A8 量化与 SmoothQuant" 5.2: a
+    grid search over alpha on calibration data): for each alpha the W8A8 output
+    (fp32, before the bf16 rounding) of the sample x against X W in fp64, by
+    relative Frobenius error.  Returns (best alpha, {alpha: error}); ties go to
+    the first alpha of the grid."""
+    y = matmul_f64(x, w)
+    errs = {}
+    for a in alphas:
+        errs[float(a)] = rel_fro(w8a8_linear(x, w, float(a), gran, calib=calib, nthreads=nthreads)["y32"], y)
+    best = min(errs, key=lambda a: (errs[a], list(errs).index(a)))
+    return best, errs
+
+
 # ---- fp64 ideal path -----------------------------------------------------------
 
 def matmul_f64(x, w) -> np.ndarray:

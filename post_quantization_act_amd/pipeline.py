@@ -112,3 +112,33 @@ class CapturedPass:
     def replay(self) -> torch.Tensor:
         self.graph.replay()
         return self.b.y
+
+
+def search_alpha(x_sample: torch.Tensor, w: torch.Tensor, amax_x: torch.Tensor, alphas, gran: int = 0):
+    """Offline migration-strength search: for each alpha of the grid, quantize W
+    and the token sample x_sample with the library and compare the W8A8 output
+    (fp32, before the bf16 rounding) with X W in fp64, by relative Frobenius
+    error.  amax_x: the calibration maxima (step 1).  Returns (best alpha,
+    {alpha: error}); ties go to the first alpha of the grid.
+
+    The quantization and the INT8 GEMM are the library's kernels; the fp64
+    reference product and the two norms are torch plumbing of this offline
+    helper (they are not part of the runtime path)."""
+    M, K = x_sample.shape
+    N = w.shape[1]
+    dev = x_sample.device
+    b = W8A8Buffers.allocate(M, N, K, gran, dev, y_dtype=torch.float32)
+    b.amax_x.copy_(amax_x)
+    y_ref = x_sample.double() @ w.double()
+    ref = float(torch.linalg.norm(y_ref))
+    errs = {}
+    for i, a in enumerate(alphas):
+        if i == 0:
+            sq_smooth_factors(b.amax_x, w, float(a), b.s, b.inv_s, b.amax_w)  # row maxima of W once
+        else:
+            sq_smooth_factors(b.amax_x, None, float(a), b.s, b.inv_s, b.amax_w)
+        sq_quant_weight(w, b.s, b.wq, b.w_scale, b.ws_w)
+        forward(x_sample, gran, b, smoothed=True)
+        errs[float(a)] = float(torch.linalg.norm(b.y.double() - y_ref)) / ref
+    best = min(errs, key=lambda a: (errs[a], list(errs).index(a)))
+    return best, errs

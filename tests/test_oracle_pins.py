@@ -544,3 +544,25 @@ def test_folded_w8a8_error_matches_smoothed_path():
     e_plain = oracle.rel_fro(oracle.w8a8_linear(ln, w, None, oracle.PER_TOKEN)["y32"], Y)
     assert abs(e_fold - e_direct) < 0.1 * e_direct
     assert e_fold < 0.5 * e_plain
+
+
+# ---- alpha grid search (page "4.2 W8A8 量化与 SmoothQuant" sections 5.1, 5.2) ----
+
+def test_alpha_search_has_an_interior_optimum():
+    """Section 5.1: alpha too small leaves the activation error dominant, too
+    large makes the weights the problem; the optimum lies inside, and on data
+    with 100x outlier channels the page's effective range 0.4-0.6 contains it."""
+    rng = np.random.default_rng(31)
+    M, K, N = 64, 512, 192
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    out = rng.choice(K, 6, replace=False)
+    x[:, out] *= 100.0
+    calib = rng.standard_normal((256, K)).astype(np.float32)
+    calib[:, out] *= 100.0
+    w = (0.02 * rng.standard_normal((K, N))).astype(np.float32)
+    grid = [round(0.1 * i, 1) for i in range(11)]
+    best, errs = oracle.search_alpha(x, w, calib, grid)
+    assert errs[0.0] > errs[best] and errs[1.0] > errs[best]
+    assert 0.4 <= best <= 0.6
+    # the curve falls towards the optimum from both ends
+    assert errs[0.0] > errs[0.2] > errs[best] and errs[1.0] > errs[0.8] > errs[best]
