@@ -362,9 +362,10 @@ int sqo_fold_layernorm(const float *gamma, const float *beta, const float *inv_s
  * arithmetic; the statistics are taken on a fixed-point grid so that they do
  * not depend on the order of summation: with 2^E the power of two just above
  * the row's largest magnitude (frexp), each x_j is truncated toward zero to a
- * multiple of 2^(E - 40) and each x_j^2 to a multiple of 2^(2E - 40), and the
- * integers are summed exactly (|sum| < K 2^40 <= 2^54 for K <= 16384):
- *   mu = S1 2^(E-40) / K,  var = max(S2 2^(2E-40) / K - mu^2, 0)  (biased),
+ * multiple of 2^(E - 39) and each x_j^2 to a multiple of 2^(2E - 39), and the
+ * integers are summed exactly (|sum| < K 2^39 <= 2^53 for K <= 16384, so the
+ * sums are exact even in fp64):
+ *   mu = S1 2^(E-39) / K,  var = max(S2 2^(2E-39) / K - mu^2, 0)  (biased),
  *   rstd = 1 / sqrt(var + eps), all in fp64 with single roundings.
  * Element j: n_j = (float)((x_j - mu) * rstd) (fp64 product rounded once to
  * fp32), z_j = fl(fl(n_j * gamma_j) + beta_j).  The row's codes and scale are
@@ -389,15 +390,15 @@ int sqo_layernorm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, co
         if (xmax > 0.0f) {
             int E;
             frexpf(xmax, &E);
-            const double c1 = ldexp(1.0, 40 - E), c2 = ldexp(1.0, 40 - 2 * E);
+            const double c1 = ldexp(1.0, 39 - E), c2 = ldexp(1.0, 39 - 2 * E);
             int64_t s1 = 0, s2 = 0;
             for (int64_t j = 0; j < K; ++j) {
                 double v = (double)bf16_bits_to_float(row[j]);
                 s1 += (int64_t)(v * c1);
                 s2 += (int64_t)(v * v * c2);
             }
-            mu = ldexp((double)s1, E - 40) / (double)K;
-            var = ldexp((double)s2, 2 * E - 40) / (double)K - mu * mu;
+            mu = ldexp((double)s1, E - 39) / (double)K;
+            var = ldexp((double)s2, 2 * E - 39) / (double)K - mu * mu;
             if (var < 0.0)
                 var = 0.0;
         }
