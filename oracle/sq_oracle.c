@@ -366,10 +366,11 @@ int sqo_fold_layernorm(const float *gamma, const float *beta, const float *inv_s
  * integers are summed exactly (|sum| < K 2^39 <= 2^53 for K <= 16384, so the
  * sums are exact even in fp64):
  *   mu = S1 2^(E-39) / K,  var = max(S2 2^(2E-39) / K - mu^2, 0)  (biased),
- *   rstd = 1 / sqrt(var + eps), all in fp64 with single roundings.
- * Element j: n_j = (float)((x_j - mu) * rstd) (fp64 product rounded once to
- * fp32), z_j = fl(fl(n_j * gamma_j) + beta_j).  The row's codes and scale are
- * those of step 4 per token.  beta NULL: no bias term. */
+ *   rstd = 1 / sqrt(var + eps), all in fp64 with single roundings; then
+ * mu32 = (float)mu and rstd32 = (float)rstd.  Element j, in fp32 as a fp32
+ * LayerNorm computes it: n_j = fl(fl(x_j - mu32) * rstd32),
+ * z_j = fl(fl(n_j * gamma_j) + beta_j).  The row's codes and scale are those
+ * of step 4 per token.  beta NULL: no bias term. */
 int sqo_layernorm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, const float *gamma,
                         const float *beta, float eps, int8_t *xq, int64_t ldq, float *x_scale)
 {
@@ -402,10 +403,10 @@ int sqo_layernorm_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, co
             if (var < 0.0)
                 var = 0.0;
         }
-        double rstd = 1.0 / sqrt(var + (double)eps);
+        const float mu32 = (float)mu, rstd32 = (float)(1.0 / sqrt(var + (double)eps));
         float m = 0.0f;
         for (int64_t j = 0; j < K; ++j) {
-            float n = (float)(((double)bf16_bits_to_float(row[j]) - mu) * rstd);
+            float n = (bf16_bits_to_float(row[j]) - mu32) * rstd32;
             float t = n * gamma[j];
             z[j] = beta ? t + beta[j] : t;
             float a = fabsf(z[j]);
