@@ -166,7 +166,11 @@ __global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int6
         __syncthreads();
         if (threadIdx.x == 0) {
             const float bm = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-            if (bm > 0.0f) atomicMax(gmax, __float_as_uint(bm));
+            // the running maximum only grows: when it already reaches bm the
+            // atomic would change nothing (and thousands of blocks would queue
+            // on one address)
+            if (bm > 0.0f && __uint_as_float(__atomic_load_n(gmax, __ATOMIC_RELAXED)) < bm)
+                atomicMax(gmax, __float_as_uint(bm));
         }
         return;
     }
@@ -236,7 +240,8 @@ __global__ __launch_bounds__(256) void k_quant_act_long(const T* __restrict__ x,
         __syncthreads();
         m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         if (mode == 1) {
-            if (threadIdx.x == 0 && m > 0.0f) atomicMax(gmax, __float_as_uint(m));
+            if (threadIdx.x == 0 && m > 0.0f && __uint_as_float(__atomic_load_n(gmax, __ATOMIC_RELAXED)) < m)
+                atomicMax(gmax, __float_as_uint(m));
             return;
         }
     }
@@ -291,13 +296,17 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
 // of 8 channels per thread, the row in registers).  The statistics use a
 // fixed-point grid so no reduction order can change them: with 2^E the power
 // of two just above the row's largest magnitude, x_j is truncated toward zero
-// to a multiple of 2^(E-40) and x_j^2 to a multiple of 2^(2E-40), and those
-// integers are summed exactly in int64 (K <= 16384 keeps |sum| < 2^54).  Then
-// mu = S1 2^(E-40) / K, var = max(S2 2^(2E-40) / K - mu^2, 0),
-// rstd = 1 / sqrt(var + eps) in fp64; element j: n = (float)((x_j - mu) rstd),
-// z = fl(fl(n g_j) + b_j) with the folded LayerNorm weight g and bias b; then
-// the row's max |z|, scale and codes as in step 4.
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+// to a multiple of 2^(E-39) and x_j^2 to a multiple of 2^(2E-39); the
+// truncated values are integers in units of the grid, and with K <= 16384 every
+// partial sum stays below 2^53, so fp64 adds them exactly in any order.  Then
+// mu = S1 2^(E-39) / K, var = max(S2 2^(2E-39) / K - mu^2, 0),
+// rstd = 1 / sqrt(var + eps) in fp64, each rounded once to fp32; element j in
+// fp32: n = fl(fl(x_j - mu) rstd), z = fl(fl(n g_j) + b_j) with the folded
+// LayerNorm weight g and bias b; then the row's max |z|, scale and codes as
+// in step 4.  The grid terms are formed in fp32 (for bf16 x, x 2^(39-E) and
+// (x 2^-E)^2 2^39 are exact in fp32, and terms too small to be exact truncate
+// to 0 either way); only their sums run in fp64.
+__device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(256) void k_ln_quant(const bf16_t* __restrict__ x, 
         }
     }
     __shared__ float redm[4];
-    __shared__ int64_t red1[4], red2[4];
+    __shared__ double red1[4], red2[4];
     xm = wave_max(xm);
     if constexpr (WPR > 1) {
         if (lane == 0) redm[wave] = xm;
@@ -343,23 +352,23 @@ __global__ __launch_bounds__(256) void k_ln_quant(const bf16_t* __restrict__ x, 
     }
     int E = 0;
     frexpf(xm, &E);
-    const double c1 = ldexp(1.0, 40 - E), c2 = ldexp(1.0, 40 - 2 * E);
-    int64_t s1 = 0, s2 = 0;
+    // ldexpf scales exactly over the whole range (a constant 2^(39-E) could overflow)
+    double s1 = 0.0, s2 = 0.0;
 #pragma unroll
     for (int q = 0; q < NV; ++q)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double d = (double)v[q][i];
-            s1 += (int64_t)(d * c1);
-            s2 += (int64_t)(d * d * c2);
+            const float y = ldexpf(v[q][i], -E);
+            s1 += (double)truncf(ldexpf(v[q][i], 39 - E));
+            s2 += (double)truncf(ldexpf(y * y, 39));
         }
     // convert again below rather than keeping 8 doubles per group alive
 #pragma unroll
     for (int q = 0; q < NV; ++q)
 #pragma unroll
         for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[q][i]));
-    s1 = wave_sum_i64(s1);
-    s2 = wave_sum_i64(s2);
+    s1 = wave_sum_f64(s1);
+    s2 = wave_sum_f64(s2);
     if constexpr (WPR > 1) {
         if (lane == 0) {
             red1[wave] = s1;
@@ -377,11 +386,11 @@ __global__ __launch_bounds__(256) void k_ln_quant(const bf16_t* __restrict__ x, 
     }
     double mu = 0.0, var = 0.0;
     if (xm > 0.0f) {
-        mu = ldexp((double)s1, E - 40) / (double)K;
-        var = ldexp((double)s2, 2 * E - 40) / (double)K - mu * mu;
+        mu = ldexp(s1, E - 39) / (double)K;
+        var = ldexp(s2, 2 * E - 39) / (double)K - mu * mu;
         if (var < 0.0) var = 0.0;
     }
-    const double rstd = 1.0 / sqrt(var + (double)eps);
+    const float mu32 = (float)mu, rstd32 = (float)(1.0 / sqrt(var + (double)eps));
 
     float m = 0.0f;
 #pragma unroll
@@ -400,7 +409,7 @@ __global__ __launch_bounds__(256) void k_ln_quant(const bf16_t* __restrict__ x, 
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float n = (float)(((double)v[q][i] - mu) * rstd);
+                const float n = (v[q][i] - mu32) * rstd32;
                 const float tt = n * gw[i];
                 v[q][i] = beta ? tt + bw[i] : tt;
                 m = fmaxf(m, fabsf(v[q][i]));
