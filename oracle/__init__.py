@@ -67,6 +67,8 @@ def lib():
         L.sqo_gemm_i8.argtypes = [vp, i64, vp, i64, i64, i64, i64, vp, i64, ctypes.c_int]
         L.sqo_dequant.argtypes = [vp, i64, f32p, ctypes.c_int, f32p, i64, i64, vp, vp, i64]
         L.sqo_quant_sym.argtypes = [f32p, i64, ctypes.c_int, vp, f32p]
+        L.sqo_outlier_columns.argtypes = [f32p, i64, ctypes.c_float, vp, vp]
+        L.sqo_llm_int8.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, f32p, vp, i64, vp, f32p, vp, vp, vp]
         L.sqo_float_to_bf16.argtypes = [ctypes.c_float]
         L.sqo_float_to_bf16.restype = ctypes.c_uint16
         L.sqo_floats_to_bf16.argtypes = [vp, i64, vp]
@@ -287,6 +289,54 @@ def search_alpha(x, w, calib, alphas, gran: int = PER_TOKEN, nthreads: int = 8):
         errs[float(a)] = rel_fro(w8a8_linear(x, w, float(a), gran, calib=calib, nthreads=nthreads)["y32"], y)
     best = min(errs, key=lambda a: (errs[a], list(errs).index(a)))
     return best, errs
+
+
+# ---- LLM.int8()-style decomposition (comparator) -------------------------------
+
+def outlier_columns(amax_x: np.ndarray, threshold: float):
+    """Outlier input channels (page "4.2 W8A8 量化与 SmoothQuant" section 2; page
+    "量化：只压权重，与训练后量化（PTQ）", SmoothQuant W8A8 results): the channels whose
+    max |x| strictly exceeds the threshold.  Returns (idx int32 ascending,
+    keep float32 with 0 on outlier channels and 1 elsewhere)."""
+    a = np.ascontiguousarray(amax_x, dtype=np.float32)
+    K = a.size
+    idx = np.empty(max(K, 1), np.int32)
+    keep = np.empty(K, np.float32)
+    n = lib().sqo_outlier_columns(_p(a), K, ctypes.c_float(threshold), _p(idx), _p(keep))
+    if n < 0:
+        raise ValueError("oracle outlier_columns rejected its arguments")
+    return idx[:n].copy(), keep
+
+
+def llm_int8(x_bf16: np.ndarray, w_bf16: np.ndarray, wq: np.ndarray, w_scale: np.ndarray, threshold: float,
+             amax_x: np.ndarray | None = None, rows=None):
+    """The mixed-precision product of the bf16 activation x[M, K] and weight
+    w[K, N]: outlier channels (from amax_x, the channel maxima of the whole x,
+    computed here when None) in 16 bits, the rest in INT8 per token with the
+    offline weight codes wq[N, K] / w_scale[N] of W itself.  rows selects the
+    token rows to evaluate (all when None).  Returns a dict with idx, xq,
+    x_scale, y32, ybf16 and bound (sum of |x w| over the outlier channels)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    M, K = x.shape
+    K2, N = w.shape
+    if K != K2:
+        raise ValueError("reduction sizes differ")
+    if amax_x is None:
+        amax_x = calib_absmax(x)
+    idx, keep = outlier_columns(amax_x, threshold)
+    xr = x if rows is None else np.ascontiguousarray(x[np.asarray(rows)])
+    R = xr.shape[0]
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    ws = np.ascontiguousarray(w_scale, dtype=np.float32)
+    xq = np.empty((R, K), np.int8)
+    xs = np.empty(R, np.float32)
+    y32 = np.empty((R, N), np.float32)
+    ybf = np.empty((R, N), np.uint16)
+    bound = np.empty((R, N), np.float64)
+    _check(lib().sqo_llm_int8(_p(xr), R, K, K, _p(w), N, N, _p(wq), _p(ws), _p(idx), idx.size, _p(xq), _p(xs),
+                              _p(y32), _p(ybf), _p(bound)), "llm_int8")
+    return dict(idx=idx, keep=keep, xq=xq, x_scale=xs, y32=y32, ybf16=ybf, bound=bound)
 
 
 # ---- fp64 ideal path -----------------------------------------------------------

@@ -509,3 +509,111 @@ int sqo_dequant(const int32_t *acc, int64_t ldc, const float *x_scale, int gran,
     }
     return 0;
 }
+
+/* ---- LLM.int8()-style mixed-precision decomposition (comparator) --------- */
+
+/* The earlier route the pages set SmoothQuant against ([P3] section 2, the
+ * mixed-precision route; [P4] SmoothQuant W8A8, its results paragraph): the
+ * input channels of X are split at run time.  Channel j is an outlier when
+ * some |x[i, j]| of the activation being multiplied exceeds a threshold (the
+ * pages give 6); outlier channels are multiplied in 16 bits, the others in
+ * INT8, and the two products are added.
+ *
+ * Outlier selection from the per-channel maxima amax_x (of the whole X, as
+ * step 1 computes them): idx receives the outlier channels in ascending
+ * order, keep[j] = 0 for an outlier channel and 1 otherwise.  "Exceeds" is
+ * read as strictly greater.  Returns the number of outlier channels, or -1. */
+int sqo_outlier_columns(const float *amax_x, int64_t K, float threshold, int32_t *idx, float *keep)
+{
+    if (K < 0 || K > 2147483647LL)
+        return -1;
+    int32_t n = 0;
+    for (int64_t j = 0; j < K; ++j) {
+        int out = amax_x[j] > threshold;
+        if (out)
+            idx[n++] = (int32_t)j;
+        if (keep)
+            keep[j] = out ? 0.0f : 1.0f;
+    }
+    return n;
+}
+
+/* The decomposed product for the token rows x[0..R) (bf16 patterns, row
+ * stride ldx) with a given outlier set idx[0..n_out) (ascending):
+ *  - INT8 part: per token i, a_i = max over regular channels of |x[i, j]|,
+ *    x_scale_i = fl(a_i / 127), codes rne(fl(x[i, j] * fl(127 / a_i))) clipped
+ *    to +-127 on the regular channels and 0 on the outlier channels (they are
+ *    taken out of this product); acc[i, k] = sum over regular j of
+ *    xq[i, j] * wq[k, j] (exact), y8 = fl(fl(float(acc) * x_scale_i) * w_scale_k)
+ *    with the offline per-output-channel weight codes wq, w_scale of W itself
+ *    (no smoothing);
+ *  - 16-bit part: the bf16 values as given, y16[i, k] = the sum over outlier
+ *    j of x[i, j] * w[j, k], products exact, summed in fp64 and rounded once
+ *    to fp32 (the pages fix no precision for this sum beyond 16-bit operands);
+ *  - y = fl(y8 + y16), stored as fp32 (y32) and/or bf16 (ybf16, RNE).
+ * bound (may be NULL) receives sum over outlier j of |x[i, j] * w[j, k]|, the
+ * scale of the rounding error any fp32 evaluation of y16 may make.  xq
+ * (may be NULL) receives the codes, x_scale the per-token scales. */
+int sqo_llm_int8(const uint16_t *x, int64_t R, int64_t K, int64_t ldx, const uint16_t *w, int64_t N,
+                 int64_t ldw, const int8_t *wq, const float *w_scale, const int32_t *idx, int64_t n_out,
+                 int8_t *xq, float *x_scale, float *y32, uint16_t *ybf16, double *bound)
+{
+    if (R < 0 || K < 0 || N < 0 || ldx < K || ldw < N || n_out < 0 || n_out > K)
+        return -1;
+    for (int64_t t = 0; t < n_out; ++t)
+        if (idx[t] < 0 || idx[t] >= K || (t > 0 && idx[t] <= idx[t - 1]))
+            return -1;
+    char *is_out = (char *)calloc((size_t)(K > 0 ? K : 1), 1);
+    int8_t *codes = (int8_t *)malloc((size_t)(K > 0 ? K : 1));
+    if (!is_out || !codes) {
+        free(is_out);
+        free(codes);
+        return -2;
+    }
+    for (int64_t t = 0; t < n_out; ++t)
+        is_out[idx[t]] = 1;
+    for (int64_t i = 0; i < R; ++i) {
+        const uint16_t *xr = x + i * ldx;
+        float m = 0.0f;
+        for (int64_t j = 0; j < K; ++j) {
+            if (is_out[j])
+                continue;
+            float a = fabsf(bf16_bits_to_float(xr[j]));
+            if (a > m)
+                m = a;
+        }
+        float xs, r;
+        sym_scale(m, 127.0f, &xs, &r);
+        for (int64_t j = 0; j < K; ++j)
+            codes[j] = is_out[j] ? 0 : (int8_t)sym_code(bf16_bits_to_float(xr[j]), r, 127.0f);
+        if (xq)
+            memcpy(xq + i * K, codes, (size_t)K);
+        if (x_scale)
+            x_scale[i] = xs;
+        for (int64_t k = 0; k < N; ++k) {
+            const int8_t *wr = wq + k * K;
+            int32_t acc = 0;
+            for (int64_t j = 0; j < K; ++j)
+                if (!is_out[j])
+                    acc += (int32_t)codes[j] * (int32_t)wr[j];
+            float y8 = ((float)acc * xs) * w_scale[k];
+            double s16 = 0.0, b16 = 0.0;
+            for (int64_t t = 0; t < n_out; ++t) {
+                int64_t j = idx[t];
+                double p = (double)bf16_bits_to_float(xr[j]) * (double)bf16_bits_to_float(w[j * ldw + k]);
+                s16 += p;
+                b16 += fabs(p);
+            }
+            float y = y8 + (float)s16;
+            if (y32)
+                y32[i * N + k] = y;
+            if (ybf16)
+                ybf16[i * N + k] = sqo_float_to_bf16(y);
+            if (bound)
+                bound[i * N + k] = b16;
+        }
+    }
+    free(is_out);
+    free(codes);
+    return 0;
+}

@@ -566,3 +566,132 @@ def test_alpha_search_has_an_interior_optimum():
     assert 0.4 <= best <= 0.6
     # the curve falls towards the optimum from both ends
     assert errs[0.0] > errs[0.2] > errs[best] and errs[1.0] > errs[0.8] > errs[best]
+
+
+# ---- LLM.int8()-style decomposition (page "4.2 W8A8 量化与 SmoothQuant" section 2;
+# page "量化：只压权重，与训练后量化（PTQ）", SmoothQuant W8A8 results paragraph) ------
+
+def _bf16(a):
+    return oracle.f32_to_bf16(np.asarray(a, np.float32))
+
+
+def test_llm_int8_threshold_selects_the_pages_outlier_channel(worked):
+    """With the pages' threshold 6, the worked example's outlier set is the
+    channel the page names as its outlier channel, and nothing else."""
+    g, X, W = worked
+    thr = _gold("printed_constants.json")["llm_int8_threshold"]["threshold"]
+    idx, keep = oracle.outlier_columns(oracle.calib_absmax(X), thr)
+    assert idx.tolist() == [g["outlier_channel_1based"] - 1]
+    assert keep.tolist() == [0.0 if j == g["outlier_channel_1based"] - 1 else 1.0 for j in range(X.shape[1])]
+
+
+def test_llm_int8_threshold_is_strict():
+    """'Exceeds' the threshold: a channel whose max equals it stays regular;
+    the next fp32 value above it is an outlier."""
+    t = np.float32(6.0)
+    amax = np.array([t, np.nextafter(t, np.float32(np.inf)), np.nextafter(t, np.float32(0)), 0.0, 1e30],
+                    np.float32)
+    idx, keep = oracle.outlier_columns(amax, float(t))
+    assert idx.tolist() == [1, 4]
+    assert keep.tolist() == [1.0, 0.0, 1.0, 1.0, 0.0]
+
+
+def test_llm_int8_codes_on_worked_example(worked):
+    """The per-token scale of the INT8 part comes from the regular channels
+    only: fp64 closed form round(127 x / max over regular channels), with the
+    outlier channel's codes 0."""
+    g, X, W = worked
+    xb, wb = _bf16(X), _bf16(W)
+    wq, ws = oracle.quant_weight(wb, None)
+    r = oracle.llm_int8(xb, wb, wq, ws, 6.0)
+    xf = oracle.bf16_to_f32(xb).astype(np.float64)
+    reg = [0, 2]
+    want = np.zeros((3, 3), np.int64)
+    for i in range(3):
+        m = np.abs(xf[i, reg]).max()
+        for j in reg:
+            want[i, j] = int(np.round(xf[i, j] * 127.0 / m))
+    np.testing.assert_array_equal(r["xq"].astype(np.int64), want)
+    np.testing.assert_allclose(r["x_scale"], np.abs(xf[:, reg]).max(axis=1) / 127.0, rtol=2 ** -23)
+
+
+def test_llm_int8_integer_case_is_exact():
+    """No rounding anywhere: regular channels hold integers with each token's
+    regular max exactly 127 (x_scale = 1), outlier channels integers above the
+    threshold 127, W integers with each column's max 127 (w_scale = 1).  Then
+    both halves are exact and the result is the integer product, checked by
+    brute force in Python integers."""
+    rng = np.random.default_rng(5)
+    M, K, N = 5, 24, 7
+    out = [3, 10, 17]
+    x = rng.integers(-127, 128, (M, K))
+    x[:, out] = rng.integers(128, 257, (M, len(out))) * rng.choice([-1, 1], (M, len(out)))
+    reg = [j for j in range(K) if j not in out]
+    for i in range(M):
+        x[i, reg[i % len(reg)]] = 127 if i % 2 else -127
+        x[i, reg] = np.clip(x[i, reg], -127, 127)
+    w = rng.integers(-127, 128, (K, N))
+    for k in range(N):
+        w[(5 * k) % K, k] = -127 if k % 2 else 127
+    xb, wb = _bf16(x), _bf16(w)
+    assert (oracle.bf16_to_f32(xb) == x).all() and (oracle.bf16_to_f32(wb) == w).all()
+    wq, ws = oracle.quant_weight(wb, None)
+    r = oracle.llm_int8(xb, wb, wq, ws, 127.0)
+    assert r["idx"].tolist() == out
+    want = [[sum(int(x[i, j]) * int(w[j, k]) for j in range(K)) for k in range(N)] for i in range(M)]
+    np.testing.assert_array_equal(r["y32"].astype(np.int64), np.array(want))
+    # the bound is the sum of |x w| over the outlier channels only
+    b = [[sum(abs(int(x[i, j]) * int(w[j, k])) for j in out) for k in range(N)] for i in range(M)]
+    np.testing.assert_array_equal(r["bound"], np.array(b, np.float64))
+
+
+def test_llm_int8_without_outliers_is_the_w8a8_baseline():
+    """A threshold above every channel max leaves no outlier: the product is
+    the unsmoothed per-token W8A8 path (the pinned step-4/5 baseline)."""
+    rng = np.random.default_rng(6)
+    x = _bf16(rng.standard_normal((16, 96)))
+    w = _bf16(0.02 * rng.standard_normal((96, 40)))
+    wq, ws = oracle.quant_weight(w, None)
+    r = oracle.llm_int8(x, w, wq, ws, 1e30)
+    b = oracle.w8a8_linear(x, w, None, oracle.PER_TOKEN)
+    assert r["idx"].size == 0
+    np.testing.assert_array_equal(r["xq"], b["xq"])
+    np.testing.assert_array_equal(r["y32"], b["y32"])
+    np.testing.assert_array_equal(r["ybf16"], b["ybf16"])
+
+
+def test_llm_int8_all_outliers_is_the_16bit_product():
+    """A negative threshold makes every channel an outlier: the INT8 part is
+    empty and the result is X W, i.e. numpy's fp64 product rounded to fp32
+    (within one fp32 ulp: the two fp64 sums differ in order)."""
+    rng = np.random.default_rng(7)
+    x = _bf16(rng.standard_normal((9, 70)))
+    w = _bf16(0.02 * rng.standard_normal((70, 33)))
+    wq, ws = oracle.quant_weight(w, None)
+    r = oracle.llm_int8(x, w, wq, ws, -1.0)
+    assert r["idx"].size == 70
+    assert (r["xq"] == 0).all()
+    ref = oracle.matmul_f64(x, w).astype(np.float32)
+    ulp = np.spacing(np.abs(ref))
+    assert (np.abs(r["y32"] - ref) <= ulp).all()
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_llm_int8_keeps_accuracy_on_outlier_data(cfg):
+    """The pages' comparison: direct W8A8 collapses on outlier activations,
+    while the mixed-precision route keeps 16-bit accuracy (and SmoothQuant
+    matches it).  On a reduced draw of the configuration's recipe, the
+    decomposed product's error is far below the unsmoothed per-token W8A8
+    error and not above the smoothed one by more than a small factor."""
+    inp = synth.make(cfg, M=48, K=512, N=96, calib_chunks=2, chunk_tokens=64)
+    x, w = synth.to_numpy(inp.x), synth.to_numpy(inp.w)
+    wq, ws = oracle.quant_weight(w, None)
+    r = oracle.llm_int8(x, w, wq, ws, 6.0)
+    assert set(inp.out_idx.tolist()) <= set(r["idx"].tolist())
+    Y = oracle.matmul_f64(x, w)
+    e_mixed = oracle.rel_fro(r["y32"], Y)
+    e_plain = oracle.rel_fro(oracle.w8a8_linear(x, w, None, oracle.PER_TOKEN)["y32"], Y)
+    e_smooth = oracle.rel_fro(
+        oracle.w8a8_linear(x, w, 0.5, oracle.PER_TOKEN, calib=synth.to_numpy(inp.calib))["y32"], Y)
+    assert e_mixed < 0.2 * e_plain
+    assert e_mixed < 2.0 * e_smooth
