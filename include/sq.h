@@ -255,6 +255,58 @@ sq_status sq_gemm_w8a8(const int8_t *xq, const float *x_scale, sq_act_gran g, co
                        const float *w_scale, int64_t M, int64_t N, int64_t K, void *y, sq_dtype yt,
                        int32_t *acc_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * LLM.int8()-style mixed-precision product, the route the pages set
+ * SmoothQuant against (page "4.2 W8A8 量化与 SmoothQuant" section 2; page
+ * "量化：只压权重，与训练后量化（PTQ）", SmoothQuant W8A8 results paragraph,
+ * which gives the threshold 6): the input channels whose activation magnitude
+ * exceeds a threshold are taken out of the INT8 product and multiplied in
+ * 16 bits, and the two results are added.  Provided as a comparator on the
+ * same data.  One runtime pass (the outlier count never leaves the device):
+ *   sq_calib_absmax(x)        amax_x of the activation being multiplied
+ *                             (amax zeroed first)
+ *   sq_outlier_columns        idx, count, keep
+ *   sq_quant_act(x, inv_s = keep, SQ_PER_TOKEN)
+ *                             xq (0 on outlier channels), x_scale over the
+ *                             regular channels
+ *   sq_gather_outliers        x_o, w_ot
+ *   sq_gemm_w8a8_outlier      y
+ * with the weight codes of W itself (sq_quant_weight with s = NULL), made
+ * once offline.
+ *
+ * sq_outlier_columns: amax_x [K] in.  idx [K] int32 out: the channels with
+ *   amax_x[j] > threshold (strictly), ascending, in idx[0 .. *count).
+ *   count: one int32 out.  keep [K] fp32 out (16-byte aligned): 0 on outlier
+ *   channels, 1 elsewhere (fl(x * 1) = x and fl(x * 0) = 0 for finite x, so
+ *   sq_quant_act with inv_s = keep quantizes only the regular channels).
+ *   threshold must not be NaN.  One workgroup; K as everywhere (K % 16 == 0).
+ * sq_gather_outliers: x [M, K] (ldx) and w [K, N] (ldw), both bf16 (else
+ *   SQ_ERR_UNSUPPORTED; element alignment suffices); idx, count from
+ *   sq_outlier_columns.  kp: row stride of the outputs, a multiple of 16 and at
+ *   least K rounded up to 16 (room for every channel).  x_o [M, kp] and
+ *   w_ot [N, kp] bf16 out, 16-byte aligned: x_o[i, t] = x[i, idx[t]] and
+ *   w_ot[k, t] = w[idx[t], k] for t < count, 0 from count up to the next
+ *   multiple of 16; entries beyond are not written.
+ * sq_gemm_w8a8_outlier: the product of sq_gemm_w8a8 with a per-token x_scale
+ *   (y8 = fl(fl(float(acc) * x_scale_i) * w_scale_k)) plus
+ *   y16[m, n] = sum over t < count of x_o[m, t] * w_ot[n, t]: bf16 products,
+ *   exact in fp32, summed in fp32 by the bf16 matrix cores (v_mfma 32x32x16,
+ *   in the hardware's order of addition, so y16 is within
+ *   count * 2^-23 * sum_t |x_o[m, t] w_ot[n, t]| of the exact sum, not bit
+ *   defined); y = fl(y8 + y16), stored as bf16 (round to nearest even) or fp32
+ *   per yt.  Arguments as sq_gemm_w8a8, plus x_o, w_ot, kp, count from the
+ *   calls above.  M <= 16 runs the tile kernels too (the weight-streaming
+ *   decode kernels have no 16-bit half).
+ */
+sq_status sq_outlier_columns(const float *amax_x, int64_t K, float threshold, int32_t *idx, int32_t *count,
+                             float *keep, hipStream_t stream);
+sq_status sq_gather_outliers(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const void *w,
+                             sq_dtype wt, int64_t N, int64_t ldw, const int32_t *idx, const int32_t *count,
+                             int64_t kp, void *x_o, void *w_ot, hipStream_t stream);
+sq_status sq_gemm_w8a8_outlier(const int8_t *xq, const float *x_scale, const int8_t *wq, const float *w_scale,
+                               int64_t M, int64_t N, int64_t K, const void *x_o, const void *w_ot, int64_t kp,
+                               const int32_t *count, void *y, sq_dtype yt, hipStream_t stream);
+
 /* Bytes of device workspace the call `op` needs for these sizes (0 if none).
  * Sizes the call does not use are ignored. */
 size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran g);
@@ -274,6 +326,8 @@ const char *sq_version(void);
  * Host function: enqueues nothing; it may query the current device's compute
  * unit count (the decode kernel's grid depends on it).  Never fails. */
 const char *sq_gemm_kernel_name(int64_t M, int64_t N, int64_t K);
+/* The same for sq_gemm_w8a8_outlier. */
+const char *sq_gemm_outlier_kernel_name(int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,8 @@ __all__ = [
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
     "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
     "sq_gemm_w8a8", "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
-    "sq_layernorm_quant", "sq_workspace_size",
+    "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier",
+    "sq_gemm_outlier_kernel_name", "sq_workspace_size",
     "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,7 +35,9 @@ SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, S
 
 EXPORTED_SYMBOLS = (
     "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights",
-    "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_workspace_size", "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name",
+    "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
+    "sq_gather_outliers", "sq_gemm_w8a8_outlier", "sq_workspace_size", "sq_status_str", "sq_last_error",
+    "sq_version", "sq_gemm_kernel_name", "sq_gemm_outlier_kernel_name",
 )
 
 
@@ -71,9 +74,12 @@ def lib() -> ctypes.CDLL:
     L.sq_quant_act_static.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     L.sq_fold_layernorm.argtypes = [vp, vp, vp, i64, vp, vp, vp]
     L.sq_layernorm_quant.argtypes = [vp, i32, i64, i64, i64, vp, vp, f32, vp, vp, vp]
+    L.sq_outlier_columns.argtypes = [vp, i64, f32, vp, vp, vp, vp]
+    L.sq_gather_outliers.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp, i64, vp, vp, vp]
+    L.sq_gemm_w8a8_outlier.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, vp, vp, i32, vp]
     for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
               "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
-              "sq_layernorm_quant"):
+              "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier"):
         getattr(L, f).restype = ctypes.c_int
     L.sq_workspace_size.argtypes = [i32, i64, i64, i64, i32]
     L.sq_workspace_size.restype = sz
@@ -85,6 +91,8 @@ def lib() -> ctypes.CDLL:
     L.sq_version.restype = ctypes.c_char_p
     L.sq_gemm_kernel_name.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
     L.sq_gemm_kernel_name.restype = ctypes.c_char_p
+    L.sq_gemm_outlier_kernel_name.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
+    L.sq_gemm_outlier_kernel_name.restype = ctypes.c_char_p
     _lib = L
     return L
 
@@ -104,6 +112,11 @@ def sq_version() -> str:
 def sq_gemm_kernel_name(M: int, N: int, K: int) -> str:
     """Which GEMM kernel sq_gemm_w8a8 launches for an M x N x K product."""
     return lib().sq_gemm_kernel_name(int(M), int(N), int(K)).decode()
+
+
+def sq_gemm_outlier_kernel_name(M: int, N: int, K: int) -> str:
+    """Which GEMM kernel sq_gemm_w8a8_outlier launches for an M x N x K product."""
+    return lib().sq_gemm_outlier_kernel_name(int(M), int(N), int(K)).decode()
 
 
 def sq_workspace_size(op: int, M: int, N: int, K: int, gran: int = SQ_PER_TOKEN) -> int:
@@ -310,3 +323,55 @@ def sq_gemm_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, gran: int, wq: torch.T
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sq_gemm_w8a8(_ptr(xq), _ptr(x_scale), int(gran), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(y),
                               _dtype(y), _ptr(acc_out), _ptr(ws), nbytes, _stream(_dev(xq), stream)))
+
+
+# ---- LLM.int8()-style comparator ---------------------------------------------------
+
+def sq_outlier_columns(amax_x: torch.Tensor, threshold: float, idx: torch.Tensor, count: torch.Tensor,
+                       keep: torch.Tensor, stream=None) -> None:
+    """idx[0:count] = the channels with amax_x > threshold (ascending); keep = 0 there, 1 elsewhere."""
+    K = amax_x.shape[0]
+    _dense(amax_x, "amax_x", (K,), torch.float32)
+    _dense(idx, "idx", (K,), torch.int32)
+    _dense(count, "count", (1,), torch.int32)
+    _dense(keep, "keep", (K,), torch.float32)
+    _check(lib().sq_outlier_columns(_ptr(amax_x), K, float(threshold), _ptr(idx), _ptr(count), _ptr(keep),
+                                    _stream(_dev(amax_x), stream)))
+
+
+def sq_gather_outliers(x: torch.Tensor, w: torch.Tensor, idx: torch.Tensor, count: torch.Tensor,
+                       x_o: torch.Tensor, w_ot: torch.Tensor, stream=None) -> None:
+    """x_o [M, kp] = outlier columns of x [M, K]; w_ot [N, kp] = outlier rows of w [K, N], transposed
+    (bf16, zero-padded to a multiple of 16 channels)."""
+    M, K, ldx = _rows(x)
+    K2, N, ldw = _rows(w)
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    kp = x_o.shape[1] if x_o.dim() == 2 else 0
+    _dense(x_o, "x_o", (M, kp), torch.bfloat16)
+    _dense(w_ot, "w_ot", (N, kp), torch.bfloat16)
+    _dense(idx, "idx", (K,), torch.int32)
+    _dense(count, "count", (1,), torch.int32)
+    _check(lib().sq_gather_outliers(_ptr(x), _dtype(x), M, K, ldx, _ptr(w), _dtype(w), N, ldw, _ptr(idx),
+                                    _ptr(count), kp, _ptr(x_o), _ptr(w_ot), _stream(_dev(x), stream)))
+
+
+def sq_gemm_w8a8_outlier(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                         x_o: torch.Tensor, w_ot: torch.Tensor, count: torch.Tensor, y: torch.Tensor,
+                         stream=None) -> None:
+    """y [M, N] = dequant(Xq . Wq^T) (per-token x_scale) + x_o . w_ot^T over the count outlier channels."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    kp = x_o.shape[1]
+    _dense(xq, "xq", (M, K), torch.int8)
+    _dense(wq, "wq", (N, K), torch.int8)
+    _dense(x_scale, "x_scale", (M,), torch.float32)
+    _dense(w_scale, "w_scale", (N,), torch.float32)
+    _dense(x_o, "x_o", (M, kp), torch.bfloat16)
+    _dense(w_ot, "w_ot", (N, kp), torch.bfloat16)
+    _dense(count, "count", (1,), torch.int32)
+    if y.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("y must be bfloat16 or float32")
+    _dense(y, "y", (M, N), y.dtype)
+    _check(lib().sq_gemm_w8a8_outlier(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(x_o),
+                                      _ptr(w_ot), kp, _ptr(count), _ptr(y), _dtype(y), _stream(_dev(xq), stream)))

@@ -23,7 +23,7 @@ OBJDIR = os.path.join(HERE, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["sq_reduce.hip", "sq_quant.hip", "sq_gemm.hip", "sq_api.cpp"]
+SOURCES = ["sq_reduce.hip", "sq_quant.hip", "sq_gemm.hip", "sq_outlier.hip", "sq_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",
           "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -342,4 +342,77 @@ sq_status sq_gemm_w8a8(const int8_t* xq, const float* x_scale, sq_act_gran g, co
                                             acc_out, stream), fn);
 }
 
+sq_status sq_outlier_columns(const float* amax_x, int64_t K, float threshold, int32_t* idx, int32_t* count,
+                             float* keep, hipStream_t stream) {
+    const char* fn = "sq_outlier_columns";
+    SQ_TRY(check_k(fn, K));
+    if (threshold != threshold) return fail(SQ_ERR_INVALID_ARG, "%s: threshold is NaN", fn);
+    SQ_TRY(check_vec(fn, "amax_x", amax_x, K));
+    SQ_TRY(check_vec(fn, "idx", idx, K));
+    SQ_TRY(check_vec(fn, "keep", keep, K, true));
+    SQ_TRY(check_vec(fn, "count", count, 1));
+    return hip_result(sqk::launch_outlier_columns(amax_x, K, threshold, idx, count, keep, stream), fn);
+}
+
+sq_status sq_gather_outliers(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const void* w,
+                             sq_dtype wt, int64_t N, int64_t ldw, const int32_t* idx, const int32_t* count,
+                             int64_t kp, void* x_o, void* w_ot, hipStream_t stream) {
+    const char* fn = "sq_gather_outliers";
+    SQ_TRY(check_k(fn, K));
+    if (xt != SQ_BF16 || wt != SQ_BF16) return fail(SQ_ERR_UNSUPPORTED, "%s: x and w must be bf16", fn);
+    if (M < 0 || N < 0 || M > kMaxMN || N > kMaxMN)
+        return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld, N = %lld out of range", fn, (long long)M, (long long)N);
+    SQ_TRY(check_matrix(fn, "x", x, xt, M, K, ldx, false));
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
+    if (kp % 16 != 0 || kp < (K + 15) / 16 * 16)
+        return fail(SQ_ERR_INVALID_ARG, "%s: kp = %lld must be a multiple of 16 and at least K rounded up to 16", fn,
+                    (long long)kp);
+    SQ_TRY(check_vec(fn, "idx", idx, K));
+    SQ_TRY(check_vec(fn, "count", count, 1));
+    if (M > 0) SQ_TRY(check_vec(fn, "x_o", x_o, 1, true));
+    if (N > 0) SQ_TRY(check_vec(fn, "w_ot", w_ot, 1, true));
+    if (K == 0) return ok();  // no channel, so no outlier: nothing is read by the GEMM
+    return hip_result(sqk::launch_gather_outliers(static_cast<const uint16_t*>(x), M, ldx,
+                                                  static_cast<const uint16_t*>(w), N, ldw, idx, count, kp,
+                                                  static_cast<uint16_t*>(x_o), static_cast<uint16_t*>(w_ot), stream),
+                      fn);
+}
+
+sq_status sq_gemm_w8a8_outlier(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                               int64_t M, int64_t N, int64_t K, const void* x_o, const void* w_ot, int64_t kp,
+                               const int32_t* count, void* y, sq_dtype yt, hipStream_t stream) {
+    const char* fn = "sq_gemm_w8a8_outlier";
+    SQ_TRY(check_k(fn, K));
+    if (!dtype_ok(yt)) return fail(SQ_ERR_UNSUPPORTED, "%s: output dtype %d", fn, (int)yt);
+    if (M < 0 || N < 0 || M > kMaxMN || N > kMaxMN)
+        return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld, N = %lld out of range", fn, (long long)M, (long long)N);
+    if (kp % 16 != 0 || kp < (K + 15) / 16 * 16)
+        return fail(SQ_ERR_INVALID_ARG, "%s: kp = %lld must be a multiple of 16 and at least K rounded up to 16", fn,
+                    (long long)kp);
+    if (M == 0 || N == 0) return ok();
+    if (K > 0) {
+        if (!xq || !wq) return fail(SQ_ERR_INVALID_ARG, "%s: xq or wq is NULL", fn);
+        if (!aligned16(xq) || !aligned16(wq))
+            return fail(SQ_ERR_INVALID_ARG, "%s: xq and wq must be 16-byte aligned", fn);
+    }
+    SQ_TRY(check_vec(fn, "x_scale", x_scale, M));
+    SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
+    SQ_TRY(check_vec(fn, "count", count, 1));
+    if (kp > 0) {
+        SQ_TRY(check_vec(fn, "x_o", x_o, 1, true));
+        SQ_TRY(check_vec(fn, "w_ot", w_ot, 1, true));
+    }
+    if (!y) return fail(SQ_ERR_INVALID_ARG, "%s: y is NULL", fn);
+    if (!aligned16(y)) return fail(SQ_ERR_INVALID_ARG, "%s: y is not 16-byte aligned", fn);
+    return hip_result(sqk::launch_gemm_w8a8_outlier(xq, x_scale, wq, w_scale, M, N, K,
+                                                    static_cast<const uint16_t*>(x_o),
+                                                    static_cast<const uint16_t*>(w_ot), kp, count, y,
+                                                    yt == SQ_BF16, stream),
+                      fn);
+}
+
+const char* sq_gemm_outlier_kernel_name(int64_t M, int64_t N, int64_t K) {
+    return sqk::gemm_kernel_name(M, N, K, true);
+}
+
 }  // extern "C"

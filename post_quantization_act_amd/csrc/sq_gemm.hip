@@ -62,6 +62,41 @@ __device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int grou
     tn = r / gm;
 }
 
+// The 16-bit half of the LLM.int8()-style product (page "4.2 W8A8 量化与
+// SmoothQuant" section 2): outlier input channels are multiplied in bf16 and
+// added to the dequantized INT8 result.  The operands are compact copies of
+// the outlier channels, k-contiguous and zero-padded to a multiple of 16:
+// w_ot[N, kp] (rows of W) and x_o[M, kp] (columns of X); *count is the number
+// of outlier channels.
+struct OutlierOps {
+    const uint16_t* x_o;
+    const uint16_t* w_ot;
+    const int32_t* count;
+    int64_t kp;
+};
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// sum over outlier channels t of w_ot[n, t] * x_o[m, t] for the 32x32 block of
+// rows n0.. and columns m0.. in the 32x32 accumulator layout, on
+// v_mfma_f32_32x32x16_bf16 (lane l supplies row l % 32 and channels
+// 8 (l / 32) .. +7 of each 16-channel step; products are exact in fp32 and
+// summed in fp32).  Rows past the matrix edge are clamped (never stored).
+__device__ __forceinline__ v16f outlier_block(const OutlierOps& op, int n16, int n0, int m0, int N, int M,
+                                              int lane) {
+    const int fr = lane % 32, fh = lane / 32;
+    const uint16_t* pa = op.w_ot + (int64_t)min(n0 + fr, N - 1) * op.kp + 8 * fh;
+    const uint16_t* pb = op.x_o + (int64_t)min(m0 + fr, M - 1) * op.kp + 8 * fh;
+    v16f o = {};
+    for (int t = 0; t < n16; t += 16) {
+        const uint4 ua = ld16(pa + t), ub = ld16(pb + t);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua), __builtin_bit_cast(v8bf, ub), o, 0,
+                                                    0, 0);
+    }
+    return o;
+}
+
 // Dequantize and store one wavefront's (TN*32) x (TM*32) block of accumulators.
 // 32x32 accumulator layout: the lane holds column (lane % 32) of a 32x32 block
 // (here: m) and rows 8*g + 4*(lane/32) + e, e = 0..3, in registers 4*g + e
@@ -69,21 +104,29 @@ __device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int grou
 // x_scale is read at index m * xs_step: xs_step = 1 per token, 0 per tensor.
 // kOut: 0 bf16, 1 fp32; kAcc: also store the int32 accumulators; kOut >= 2
 // marks N % 4 != 0 (element-wise stores), with the output type kOut - 2.
-template <int TN, int TM, int kOut, bool kAcc>
+// kO: add the 16-bit outlier product, y = fl(y8 + y16) (op is unused otherwise).
+template <int TN, int TM, int kOut, bool kAcc, bool kO = false>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
                                          const float* __restrict__ x_scale, int xs_step,
                                          const float* __restrict__ w_scale, int M, int N, void* __restrict__ y,
-                                         int32_t* __restrict__ acc_out) {
+                                         int32_t* __restrict__ acc_out, const OutlierOps& op = OutlierOps{}) {
     const int fr = lane % 32, fh = lane / 32;
     constexpr bool n_vec = kOut < 2;
     constexpr int kTy = kOut & 1;
+    int n16 = 0;
+    if constexpr (kO) n16 = (__builtin_amdgcn_readfirstlane(op.count[0]) + 15) & ~15;
 #pragma unroll
     for (int b = 0; b < TM; ++b) {
         const int m = mbase + b * 32 + fr;
-        if (m >= M) continue;
-        const float xs = x_scale[m * xs_step];
+        // (every lane takes part in the matrix-core addend, so no early exit
+        // for rows past M when kO)
+        if (!kO && m >= M) continue;
+        const float xs = m < M ? x_scale[m * xs_step] : 0.0f;
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
+            v16f o = {};
+            if constexpr (kO) o = outlier_block(op, n16, nbase + a * 32, mbase + b * 32, N, M, lane);
+            if (kO && m >= M) continue;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + a * 32 + 8 * g + 4 * fh;
@@ -93,10 +136,16 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
                 for (int e = 0; e < 4; ++e) av[e] = acc[a][b][4 * g + e];
                 if constexpr (n_vec) {
                     const float4 ws = *reinterpret_cast<const float4*>(w_scale + n);
-                    const float y0 = ((float)av[0] * xs) * ws.x;
-                    const float y1 = ((float)av[1] * xs) * ws.y;
-                    const float y2 = ((float)av[2] * xs) * ws.z;
-                    const float y3 = ((float)av[3] * xs) * ws.w;
+                    float y0 = ((float)av[0] * xs) * ws.x;
+                    float y1 = ((float)av[1] * xs) * ws.y;
+                    float y2 = ((float)av[2] * xs) * ws.z;
+                    float y3 = ((float)av[3] * xs) * ws.w;
+                    if constexpr (kO) {
+                        y0 += o[4 * g + 0];
+                        y1 += o[4 * g + 1];
+                        y2 += o[4 * g + 2];
+                        y3 += o[4 * g + 3];
+                    }
                     const int64_t off = (int64_t)m * N + n;
                     if constexpr (kTy == 0) {
                         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) =
@@ -109,7 +158,8 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (n + e >= N) break;
-                        const float v = ((float)av[e] * xs) * w_scale[n + e];
+                        float v = ((float)av[e] * xs) * w_scale[n + e];
+                        if constexpr (kO) v += o[4 * g + e];
                         const int64_t off = (int64_t)m * N + n + e;
                         if constexpr (kTy == 0) {
                             static_cast<uint16_t*>(y)[off] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
@@ -150,12 +200,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int BN, int BM, int WGN, int WGM, int NS, int kOut, bool kAcc>
+template <int BN, int BM, int WGN, int WGM, int NS, int kOut, bool kAcc, bool kO>
 __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
                                                    int xs_step, const int8_t* __restrict__ wq,
                                                    const float* __restrict__ w_scale, int M, int N, int K,
                                                    void* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
-                                                   int tiles_m, int group_m) {
+                                                   int tiles_m, int group_m, OutlierOps op) {
     constexpr int NW = WGN * WGM;             // wavefronts per block
     constexpr int WN = BN / WGN, WM = BM / WGM, TN = WN / 32, TM = WM / 32;
     constexpr int ROWS = BN + BM;             // rows of a stage: Wq tile rows, then Xq tile rows
@@ -280,18 +330,18 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
         kstep(1, kt + 1 < nk, nbuf, 0, 0, false, 0);
         buf = nbuf;
     }
-    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
-                                 acc_out);
+    epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
+                                     acc_out, op);
 }
 
 // ---- generic kernel: any K % 16 == 0 -------------------------------------------
 
-template <int BN, int BM, int kOut, bool kAcc>
+template <int BN, int BM, int kOut, bool kAcc, bool kO>
 __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
                                                       int xs_step, const int8_t* __restrict__ wq,
                                                       const float* __restrict__ w_scale, int M, int N, int K,
                                                       void* __restrict__ y, int32_t* __restrict__ acc_out,
-                                                      int tiles_n, int tiles_m, int group_m) {
+                                                      int tiles_n, int tiles_m, int group_m, OutlierOps op) {
     constexpr int WN = BN / 2, WM = BM / 2;
     constexpr int TN = WN / 32, TM = WM / 32;
     constexpr int A_CHUNKS = BN * 8 / 256;  // 16-byte chunks per thread per stage
@@ -414,8 +464,8 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__
             rfrag(cur ^ 1, 0, 0);
         }
     }
-    epilogue<TN, TM, kOut, kAcc>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
-                                 acc_out);
+    epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
+                                     acc_out, op);
 }
 
 // ---- decode kernel: few tokens, the weight stream is the cost ---------------------
@@ -743,62 +793,66 @@ static void launch_decode(const int8_t* xq, const float* x_scale, bool per_tenso
 // ---- launchers ---------------------------------------------------------------------
 
 
-#define SQ_DEFINE_LAUNCH(KERNEL)                                                                                    \
-    template <int BN, int BM>                                                                                      \
-    static void launch_##KERNEL(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,        \
-                                const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out, \
-                                int group_m, hipStream_t st) {                                                     \
-        const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;                                        \
-        const dim3 grid((unsigned)(tiles_n * tiles_m));                                                            \
-        const int step = per_tensor ? 0 : 1; /* x_scale index step */                                              \
-        const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);                                                   \
-        auto go = [&](auto out_c, auto acc_c) {                                                                    \
-            hipLaunchKernelGGL((KERNEL<BN, BM, decltype(out_c)::value, decltype(acc_c)::value>), grid, dim3(256), \
-                               0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n, tiles_m,       \
-                               group_m);                                                                           \
-        };                                                                                                         \
-        using T_ = std::true_type;                                                                                 \
-        using F_ = std::false_type;                                                                                \
-        switch (out) {                                                                                             \
-            case 0: if (acc_out) go(std::integral_constant<int, 0>{}, T_{}); else go(std::integral_constant<int, 0>{}, F_{}); break; \
-            case 1: if (acc_out) go(std::integral_constant<int, 1>{}, T_{}); else go(std::integral_constant<int, 1>{}, F_{}); break; \
-            case 2: if (acc_out) go(std::integral_constant<int, 2>{}, T_{}); else go(std::integral_constant<int, 2>{}, F_{}); break; \
-            default: if (acc_out) go(std::integral_constant<int, 3>{}, T_{}); else go(std::integral_constant<int, 3>{}, F_{}); break; \
-        }                                                                                                          \
-    }
+// Calls go(out, acc, o) with compile-time constants for the output mode
+// (0 bf16, 1 fp32, +2 when N % 4 != 0), the int32 accumulator store and the
+// 16-bit outlier addend (built without the accumulator store).
+template <typename Go>
+static void dispatch_variant(bool y_bf16, int N, bool acc, bool outl, Go&& go) {
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);
+    auto by_out = [&](auto a, auto o) {
+        switch (out) {
+            case 0: go(std::integral_constant<int, 0>{}, a, o); break;
+            case 1: go(std::integral_constant<int, 1>{}, a, o); break;
+            case 2: go(std::integral_constant<int, 2>{}, a, o); break;
+            default: go(std::integral_constant<int, 3>{}, a, o); break;
+        }
+    };
+    if (outl) by_out(F_{}, T_{});
+    else if (acc) by_out(T_{}, F_{});
+    else by_out(F_{}, F_{});
+}
 
-SQ_DEFINE_LAUNCH(k_gemm_generic)
+template <int BN, int BM>
+static void launch_generic(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                           const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
+                           const OutlierOps* op, int group_m, hipStream_t st) {
+    const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+    const dim3 grid((unsigned)(tiles_n * tiles_m));
+    const int step = per_tensor ? 0 : 1;  // x_scale index step
+    const OutlierOps ops = op ? *op : OutlierOps{};
+    dispatch_variant(y_bf16, N, acc_out != nullptr, op != nullptr, [&](auto out_c, auto acc_c, auto o_c) {
+        hipLaunchKernelGGL((k_gemm_generic<BN, BM, decltype(out_c)::value, decltype(acc_c)::value,
+                                           decltype(o_c)::value>),
+                           grid, dim3(256), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n,
+                           tiles_m, group_m, ops);
+    });
+}
 
 template <int BN, int BM, int WGN, int WGM, int NS>
 static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
                         const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
-                        int group_m, hipStream_t st) {
+                        const OutlierOps* op, int group_m, hipStream_t st) {
     const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
     const dim3 grid((unsigned)(tiles_n * tiles_m));
     const int step = per_tensor ? 0 : 1;
-    const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);
-    auto go = [&](auto out_c, auto acc_c) {
-        hipLaunchKernelGGL((k_gemm_ring<BN, BM, WGN, WGM, NS, decltype(out_c)::value, decltype(acc_c)::value>), grid,
-                           dim3(64 * WGN * WGM), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n,
-                           tiles_m, group_m);
-    };
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    switch (out) {
-        case 0: if (acc_out) go(std::integral_constant<int, 0>{}, T_{}); else go(std::integral_constant<int, 0>{}, F_{}); break;
-        case 1: if (acc_out) go(std::integral_constant<int, 1>{}, T_{}); else go(std::integral_constant<int, 1>{}, F_{}); break;
-        case 2: if (acc_out) go(std::integral_constant<int, 2>{}, T_{}); else go(std::integral_constant<int, 2>{}, F_{}); break;
-        default: if (acc_out) go(std::integral_constant<int, 3>{}, T_{}); else go(std::integral_constant<int, 3>{}, F_{}); break;
-    }
+    const OutlierOps ops = op ? *op : OutlierOps{};
+    dispatch_variant(y_bf16, N, acc_out != nullptr, op != nullptr, [&](auto out_c, auto acc_c, auto o_c) {
+        hipLaunchKernelGGL((k_gemm_ring<BN, BM, WGN, WGM, NS, decltype(out_c)::value, decltype(acc_c)::value,
+                                        decltype(o_c)::value>),
+                           grid, dim3(64 * WGN * WGM), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out,
+                           tiles_n, tiles_m, group_m, ops);
+    });
 }
 
 // Which kernel a product of this shape runs (the one rule both the launcher
 // and gemm_kernel_name use).
 enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing256x128, kRing128, kGeneric };
 
-static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
+static GemmPath gemm_path(int64_t M, int64_t N, int64_t K, bool outl = false) {
     if (M <= 0 || N <= 0) return GemmPath::kNone;
-    if (M <= 16 && K > 0) return decode_ring_fits(M, N, K) ? GemmPath::kDecodeRing : GemmPath::kDecode;
+    if (M <= 16 && K > 0 && !outl) return decode_ring_fits(M, N, K) ? GemmPath::kDecodeRing : GemmPath::kDecode;
     const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
                       (uint64_t)M * (uint64_t)K < (1ull << 32);
     if (!ring) return GemmPath::kGeneric;
@@ -815,8 +869,8 @@ static GemmPath gemm_path(int64_t M, int64_t N, int64_t K) {
     return GemmPath::kRing128;
 }
 
-const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
-    switch (gemm_path(M, N, K)) {
+const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl) {
+    switch (gemm_path(M, N, K, outl)) {
         case GemmPath::kDecodeRing:
             return "k_gemm_decode_ring (one block of 16 wavefronts per CU, per-wavefront LDS rings of 128-byte stages)";
         case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
@@ -829,11 +883,11 @@ const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K) {
     }
 }
 
-hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
-                            const float* w_scale, int64_t M64, int64_t N64, int64_t K64, void* y, bool y_bf16,
-                            int32_t* acc_out, hipStream_t st) {
+static hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                              const float* w_scale, int64_t M64, int64_t N64, int64_t K64, void* y, bool y_bf16,
+                              int32_t* acc_out, const OutlierOps* op, hipStream_t st) {
     const int M = (int)M64, N = (int)N64, K = (int)K64;
-    switch (gemm_path(M64, N64, K64)) {
+    switch (gemm_path(M64, N64, K64, op != nullptr)) {
         case GemmPath::kNone: return hipSuccess;
         case GemmPath::kDecodeRing:
             launch_decode_ring(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
@@ -842,20 +896,35 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
             launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
             break;
         case GemmPath::kRing256:
-            launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 4, st);
+            launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 4,
+                                           st);
             break;
         case GemmPath::kRing256x128:
-            launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+            launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8,
+                                           st);
             break;
         case GemmPath::kRing128:
-            launch_ring<128, 128, 2, 4, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8, st);
+            launch_ring<128, 128, 2, 4, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8,
+                                           st);
             break;
         case GemmPath::kGeneric:
-            launch_k_gemm_generic<256, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, 8,
-                                            st);
+            launch_generic<256, 128>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8, st);
             break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                            const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16,
+                            int32_t* acc_out, hipStream_t st) {
+    return launch_gemm(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, nullptr, st);
+}
+
+hipError_t launch_gemm_w8a8_outlier(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                                    int64_t M, int64_t N, int64_t K, const uint16_t* x_o, const uint16_t* w_ot,
+                                    int64_t kp, const int32_t* count, void* y, bool y_bf16, hipStream_t st) {
+    const OutlierOps op{x_o, w_ot, count, kp};
+    return launch_gemm(xq, x_scale, false, wq, w_scale, M, N, K, y, y_bf16, nullptr, &op, st);
 }
 
 }  // namespace sqk

@@ -59,7 +59,26 @@ hipError_t launch_gemm_w8a8(const int8_t* xq, const float* x_scale, bool per_ten
                             const float* w_scale, int64_t M, int64_t N, int64_t K, void* y, bool y_bf16,
                             int32_t* acc_out, hipStream_t st);
 
-// Static description of the GEMM kernel launch_gemm_w8a8 runs for this shape.
-const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K);
+// The same product plus the 16-bit outlier addend of the LLM.int8()-style
+// comparator (per-token x_scale): y = fl(y8 + sum_t w_ot[n, t] x_o[m, t]) over
+// the *count outlier channels, operands [N, kp] and [M, kp] bf16, zero-padded
+// to a multiple of 16 channels.
+hipError_t launch_gemm_w8a8_outlier(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale,
+                                    int64_t M, int64_t N, int64_t K, const uint16_t* x_o, const uint16_t* w_ot,
+                                    int64_t kp, const int32_t* count, void* y, bool y_bf16, hipStream_t st);
+
+// Static description of the GEMM kernel launch_gemm_w8a8 (outl: the outlier
+// variant) runs for this shape.
+const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl = false);
+
+// Outlier channels of the comparator: idx[0..*count) ascending with
+// amax[j] > thr, keep[j] = 0 there and 1 elsewhere (one block).
+hipError_t launch_outlier_columns(const float* amax, int64_t K, float thr, int32_t* idx, int32_t* count, float* keep,
+                                  hipStream_t st);
+// x_o[i, t] = x[i, idx[t]], w_ot[k, t] = w[idx[t], k] for t < *count, zero up to
+// the next multiple of 16 (bf16 patterns; kp % 16 == 0, kp >= that multiple).
+hipError_t launch_gather_outliers(const uint16_t* x, int64_t M, int64_t ldx, const uint16_t* w, int64_t N,
+                                  int64_t ldw, const int32_t* idx, const int32_t* count, int64_t kp, uint16_t* x_o,
+                                  uint16_t* w_ot, hipStream_t st);
 
 }  // namespace sqk

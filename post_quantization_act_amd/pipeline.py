@@ -9,9 +9,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR, sq_calib_absmax,
-               sq_gemm_w8a8, sq_prepare_weights, sq_quant_act, sq_quant_weight, sq_smooth_factors,
-               sq_workspace_size)
+from . import (SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR, SQ_PER_TOKEN,
+               sq_calib_absmax, sq_gather_outliers, sq_gemm_w8a8, sq_gemm_w8a8_outlier, sq_outlier_columns,
+               sq_prepare_weights, sq_quant_act, sq_quant_weight, sq_smooth_factors, sq_workspace_size)
 
 
 @dataclass
@@ -142,3 +142,61 @@ def search_alpha(x_sample: torch.Tensor, w: torch.Tensor, amax_x: torch.Tensor, 
         errs[float(a)] = float(torch.linalg.norm(b.y.double() - y_ref)) / ref
     best = min(errs, key=lambda a: (errs[a], list(errs).index(a)))
     return best, errs
+
+
+# ---- LLM.int8()-style comparator -------------------------------------------------------
+
+@dataclass
+class LlmInt8Buffers:
+    """Device buffers of the mixed-precision comparator: offline weight codes
+    of W itself, and the per-call outlier set, INT8 activations and compact
+    16-bit outlier operands (kp = K rounded up to 16, room for every channel)."""
+    wq: torch.Tensor
+    w_scale: torch.Tensor
+    amax_x: torch.Tensor
+    idx: torch.Tensor
+    count: torch.Tensor
+    keep: torch.Tensor
+    xq: torch.Tensor
+    x_scale: torch.Tensor
+    x_o: torch.Tensor
+    w_ot: torch.Tensor
+    y: torch.Tensor
+    ws_w: torch.Tensor | None
+
+    @classmethod
+    def allocate(cls, M: int, N: int, K: int, device, y_dtype=torch.bfloat16):
+        kp = (K + 15) // 16 * 16
+        nb = sq_workspace_size(SQ_OP_QUANT_WEIGHT, 0, N, K)
+        return cls(
+            wq=torch.empty(N, K, dtype=torch.int8, device=device),
+            w_scale=torch.empty(N, dtype=torch.float32, device=device),
+            amax_x=torch.empty(K, dtype=torch.float32, device=device),
+            idx=torch.empty(K, dtype=torch.int32, device=device),
+            count=torch.empty(1, dtype=torch.int32, device=device),
+            keep=torch.empty(K, dtype=torch.float32, device=device),
+            xq=torch.empty(M, K, dtype=torch.int8, device=device),
+            x_scale=torch.empty(M, dtype=torch.float32, device=device),
+            x_o=torch.empty(M, kp, dtype=torch.bfloat16, device=device),
+            w_ot=torch.empty(N, kp, dtype=torch.bfloat16, device=device),
+            y=torch.empty(M, N, dtype=y_dtype, device=device),
+            ws_w=torch.empty(max(nb, 16), dtype=torch.uint8, device=device) if nb else None,
+        )
+
+
+def llm_int8_prepare(w: torch.Tensor, b: LlmInt8Buffers, stream=None) -> None:
+    """Offline: per-output-channel INT8 codes of W itself (no smoothing)."""
+    sq_quant_weight(w, None, b.wq, b.w_scale, b.ws_w, stream=stream)
+
+
+def llm_int8_forward(x: torch.Tensor, w: torch.Tensor, threshold: float, b: LlmInt8Buffers,
+                     stream=None) -> torch.Tensor:
+    """Runtime pass: outlier channels of this x (max |x| > threshold) in 16 bits,
+    the rest per-token INT8, summed (five library calls, no host sync)."""
+    b.amax_x.zero_()
+    sq_calib_absmax(x, b.amax_x, stream=stream)
+    sq_outlier_columns(b.amax_x, threshold, b.idx, b.count, b.keep, stream=stream)
+    sq_quant_act(x, b.keep, SQ_PER_TOKEN, b.xq, b.x_scale, stream=stream)
+    sq_gather_outliers(x, w, b.idx, b.count, b.x_o, b.w_ot, stream=stream)
+    sq_gemm_w8a8_outlier(b.xq, b.x_scale, b.wq, b.w_scale, b.x_o, b.w_ot, b.count, b.y, stream=stream)
+    return b.y

@@ -192,3 +192,39 @@ def test_layernorm_rejects():
     _expect(L.sq_layernorm_quant(FAKE, sq.SQ_BF16, 4, 32, 32, FAKE, None, f(-1.0), FAKE, FAKE, None), -1, "eps")
     _expect(L.sq_fold_layernorm(None, None, FAKE, 8, FAKE, None, None), -1, "gamma is NULL")
     _expect(L.sq_fold_layernorm(FAKE, FAKE, FAKE, 8, FAKE, None, None), -1, "beta_out is NULL")
+
+
+def test_llm_int8_entry_points_reject():
+    L = _L()
+    f = ctypes.c_float
+    # outlier selection
+    _expect(L.sq_outlier_columns(FAKE, 20, f(6.0), FAKE, FAKE, FAKE, None), -1, "multiple of 16")
+    _expect(L.sq_outlier_columns(FAKE, 32, f(float("nan")), FAKE, FAKE, FAKE, None), -1, "NaN")
+    _expect(L.sq_outlier_columns(FAKE, 32, f(6.0), FAKE, None, FAKE, None), -1, "count is NULL")
+    _expect(L.sq_outlier_columns(FAKE, 32, f(6.0), FAKE, FAKE, MISALIGNED, None), -1, "keep")
+    # gather
+    g = lambda **kw: [FAKE, kw.get("xt", sq.SQ_BF16), 8, kw.get("K", 32), kw.get("K", 32), FAKE,
+                      kw.get("wt", sq.SQ_BF16), 24,
+                      24, FAKE, kw.get("count", FAKE), kw.get("kp", 32), kw.get("x_o", FAKE), FAKE, None]
+    _expect(L.sq_gather_outliers(*g(xt=sq.SQ_F32)), -2, "bf16")
+    _expect(L.sq_gather_outliers(*g(kp=24)), -1, "kp = 24")
+    _expect(L.sq_gather_outliers(*g(K=48, kp=32)), -1, "kp = 32")
+    _expect(L.sq_gather_outliers(*g(count=None)), -1, "count is NULL")
+    _expect(L.sq_gather_outliers(*g(x_o=MISALIGNED)), -1, "x_o")
+    # outlier GEMM
+    m = lambda **kw: [FAKE, FAKE, kw.get("wq", FAKE), FAKE, 4, 8, kw.get("K", 32), FAKE, FAKE, kw.get("kp", 32),
+                      kw.get("count", FAKE), kw.get("y", FAKE), kw.get("yt", sq.SQ_BF16), None]
+    _expect(L.sq_gemm_w8a8_outlier(*m(K=24)), -1, "multiple of 16")
+    _expect(L.sq_gemm_w8a8_outlier(*m(kp=16)), -1, "kp = 16")
+    _expect(L.sq_gemm_w8a8_outlier(*m(count=None)), -1, "count is NULL")
+    _expect(L.sq_gemm_w8a8_outlier(*m(wq=MISALIGNED)), -1, "16-byte aligned")
+    _expect(L.sq_gemm_w8a8_outlier(*m(y=None)), -1, "y is NULL")
+    _expect(L.sq_gemm_w8a8_outlier(*m(yt=9)), -2, "output dtype")
+
+
+def test_outlier_gemm_kernel_choice():
+    """The outlier variant uses the same tile kernels, and the general one
+    where the plain product would stream weights (M <= 16)."""
+    assert sq.sq_gemm_outlier_kernel_name(2048, 4096, 4096) == sq.sq_gemm_kernel_name(2048, 4096, 4096)
+    assert sq.sq_gemm_outlier_kernel_name(16, 28672, 8192).startswith("k_gemm_ring")
+    assert sq.sq_gemm_outlier_kernel_name(16, 100, 1040).startswith("k_gemm_generic")
