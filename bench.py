@@ -21,6 +21,11 @@ The JSON line carries, besides the whole-step throughput:
   alpha_sweep   relative Frobenius error of the smoothed and unsmoothed W8A8
                 output (fp32) against X W (fp64) for the large workload's
                 alphas, on a 256-token sample;
+  llm_int8_comparator
+                the LLM.int8()-style mixed-precision route (outlier channels
+                above 6 in bf16, the rest INT8) against SmoothQuant on the
+                attention-projection workload: runtime per call, GEMMs alone,
+                and fp32 output error against X W (fp64);
   cpu_baseline  the CPU oracle as it stands, on the host cores, over the same
                 step workload (the GEMM on a row sample when needed).
 
@@ -294,6 +299,92 @@ def _large(torch, sq, synth, pipeline, dev):
     return out, out_sweep
 
 
+def _comparator(torch, sq, synth, pipeline, dev):
+    """SmoothQuant against the LLM.int8()-style mixed-precision route on the
+    attention-projection workload (2048 x 4096 x 4096, 41 outlier channels):
+    runtime time of each per call (inputs rotating over sets larger than the
+    Infinity Cache), the two GEMMs alone, and the output error of each against
+    X W in fp64 on a 256-token sample."""
+    tm = _Timer(torch)
+    cfg = synth.CONFIGS[2]
+    M, K, N = cfg.M, cfg.K, cfg.N
+    nsets = 6  # 6 x (16.8 MB x + 33.5 MB w + 16.8 MB codes) > 256 MB
+    print(f"# comparator: drawing {nsets} sets of {cfg.name}", file=sys.stderr, flush=True)
+    sets = [synth.make(cfg, device=dev, variant=v) for v in range(nsets)]
+    sqb = [pipeline.W8A8Buffers.allocate(M, N, K, sq.SQ_PER_TOKEN, dev) for _ in range(nsets)]
+    lb = [pipeline.LlmInt8Buffers.allocate(M, N, K, dev) for _ in range(nsets)]
+    for inp, b, l in zip(sets, sqb, lb):
+        pipeline.calibrate(inp.calib, b.amax_x)
+        pipeline.prepare_weights(inp.w, 0.5, b)
+        pipeline.llm_int8_prepare(inp.w, l)
+        pipeline.llm_int8_forward(inp.x, inp.w, 6.0, l)
+    torch.cuda.synchronize()
+    n_out = [int(l.count.item()) for l in lb]
+
+    def sq_run(i):
+        k = i % nsets
+        pipeline.forward(sets[k].x, sq.SQ_PER_TOKEN, sqb[k], smoothed=True)
+
+    def l8_run(i):
+        k = i % nsets
+        pipeline.llm_int8_forward(sets[k].x, sets[k].w, 6.0, lb[k])
+
+    def sq_gemm(i):
+        b = sqb[i % nsets]
+        sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y)
+
+    def l8_gemm(i):
+        l = lb[i % nsets]
+        sq.sq_gemm_w8a8_outlier(l.xq, l.x_scale, l.wq, l.w_scale, l.x_o, l.w_ot, l.count, l.y)
+
+    reps = 4 * nsets
+    t_sq, t_l8 = tm(sq_run, reps=reps, warm=nsets), tm(l8_run, reps=reps, warm=nsets)
+    g_sq, g_l8 = tm(sq_gemm, reps=reps, warm=nsets), tm(l8_gemm, reps=reps, warm=nsets)
+    ops = 2.0 * M * N * K
+
+    # errors of the fp32 outputs on set 0 against X W in fp64 (256 sampled tokens)
+    inp = sets[0]
+    rows = torch.arange(0, M, M // 256, device=dev)[:256]
+    y_ref = inp.x[rows].double() @ inp.w.double()
+    nrm = float(torch.linalg.norm(y_ref))
+
+    def err(y):
+        return round(float(torch.linalg.norm(y[rows].double() - y_ref)) / nrm, 6)
+
+    b32 = pipeline.W8A8Buffers.allocate(M, N, K, sq.SQ_PER_TOKEN, dev, y_dtype=torch.float32)
+    b32.amax_x.copy_(sqb[0].amax_x)
+    pipeline.prepare_weights(inp.w, 0.5, b32)
+    pipeline.forward(inp.x, sq.SQ_PER_TOKEN, b32, smoothed=True)
+    e_sq = err(b32.y)
+    pipeline.prepare_weights(inp.w, None, b32)
+    pipeline.forward(inp.x, sq.SQ_PER_TOKEN, b32, smoothed=False)
+    e_plain = err(b32.y)
+    l32 = pipeline.LlmInt8Buffers.allocate(M, N, K, dev, y_dtype=torch.float32)
+    pipeline.llm_int8_prepare(inp.w, l32)
+    pipeline.llm_int8_forward(inp.x, inp.w, 6.0, l32)
+    e_l8 = err(l32.y)
+    torch.cuda.synchronize()
+    out = {
+        "workload": cfg.name, "threshold": 6.0, "outlier_channels": n_out[0],
+        "outlier_channels_all_sets": n_out,
+        "smoothquant_runtime_us": round(t_sq, 1),
+        "llm_int8_runtime_us": round(t_l8, 1),
+        "runtime_ratio_llm_int8_over_smoothquant": round(t_l8 / t_sq, 3),
+        "smoothquant_gemm_us": round(g_sq, 1),
+        "llm_int8_gemm_us": round(g_l8, 1),
+        "smoothquant_gemm_pct_int8_peak": round(100 * ops / g_sq / 1e6 / INT8_PEAK_TOPS, 1),
+        "llm_int8_gemm_kernel": sq.sq_gemm_outlier_kernel_name(M, N, K),
+        "error_rel_fro_fp32": {"smoothquant_alpha_0.5_per_token": e_sq, "llm_int8": e_l8,
+                               "unsmoothed_per_token": e_plain},
+        "runtime_steps": {"smoothquant": "quant_act (smoothing fused) + gemm_w8a8",
+                          "llm_int8": "absmax of x + outlier_columns + quant_act (keep mask) + gather_outliers "
+                                      "+ gemm_w8a8_outlier"},
+    }
+    del sets, sqb, lb, b32, l32, y_ref
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -435,6 +526,7 @@ def main():
         del sets
         torch.cuda.empty_cache()
         out["large"], out["alpha_sweep"] = _large(torch, sq, synth, pipeline, dev)
+        out["llm_int8_comparator"] = _comparator(torch, sq, synth, pipeline, dev)
     if not args.no_cpu:
         print("# CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = _cpu_baseline(cfg, args.cpu_seconds)

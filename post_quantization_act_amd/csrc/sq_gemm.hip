@@ -78,23 +78,45 @@ struct OutlierOps {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// sum over outlier channels t of w_ot[n, t] * x_o[m, t] for the 32x32 block of
-// rows n0.. and columns m0.. in the 32x32 accumulator layout, on
-// v_mfma_f32_32x32x16_bf16 (lane l supplies row l % 32 and channels
-// 8 (l / 32) .. +7 of each 16-channel step; products are exact in fp32 and
-// summed in fp32).  Rows past the matrix edge are clamped (never stored).
-__device__ __forceinline__ v16f outlier_block(const OutlierOps& op, int n16, int n0, int m0, int N, int M,
-                                              int lane) {
+// Sums over the outlier channels t of w_ot[n, t] * x_o[m, t] for the TN 32x32
+// blocks of rows nbase + 32 a .. and columns m0 .., in the 32x32 accumulator
+// layout, on v_mfma_f32_32x32x16_bf16 (lane l supplies row l % 32 and
+// channels 8 (l / 32) .. +7 of each 16-channel step; products are exact in
+// fp32 and summed in fp32).  All TN + 1 fragments of a step are loaded
+// together, one step ahead of the matrix cores.  Rows past the matrix edge
+// are clamped (never stored).
+template <int TN>
+__device__ __forceinline__ void outlier_blocks(const OutlierOps& op, int n16, int nbase, int m0, int N, int M,
+                                               int lane, v16f (&o)[TN]) {
     const int fr = lane % 32, fh = lane / 32;
-    const uint16_t* pa = op.w_ot + (int64_t)min(n0 + fr, N - 1) * op.kp + 8 * fh;
-    const uint16_t* pb = op.x_o + (int64_t)min(m0 + fr, M - 1) * op.kp + 8 * fh;
-    v16f o = {};
-    for (int t = 0; t < n16; t += 16) {
-        const uint4 ua = ld16(pa + t), ub = ld16(pb + t);
-        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua), __builtin_bit_cast(v8bf, ub), o, 0,
-                                                    0, 0);
+    const uint16_t* pa[TN];
+#pragma unroll
+    for (int a = 0; a < TN; ++a) {
+        pa[a] = op.w_ot + (int64_t)min(nbase + a * 32 + fr, N - 1) * op.kp + 8 * fh;
+        o[a] = v16f{};
     }
-    return o;
+    const uint16_t* pb = op.x_o + (int64_t)min(m0 + fr, M - 1) * op.kp + 8 * fh;
+    if (n16 == 0) return;
+    uint4 ua[TN], ub = ld16(pb);
+#pragma unroll
+    for (int a = 0; a < TN; ++a) ua[a] = ld16(pa[a]);
+    for (int t = 16;; t += 16) {
+        const bool more = t < n16;  // uniform over the wavefront
+        uint4 na[TN], nb;
+        if (more) {
+            nb = ld16(pb + t);
+#pragma unroll
+            for (int a = 0; a < TN; ++a) na[a] = ld16(pa[a] + t);
+        }
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+            o[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ua[a]), __builtin_bit_cast(v8bf, ub),
+                                                           o[a], 0, 0, 0);
+        if (!more) break;
+        ub = nb;
+#pragma unroll
+        for (int a = 0; a < TN; ++a) ua[a] = na[a];
+    }
 }
 
 // Dequantize and store one wavefront's (TN*32) x (TM*32) block of accumulators.
@@ -122,11 +144,12 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
         // for rows past M when kO)
         if (!kO && m >= M) continue;
         const float xs = m < M ? x_scale[m * xs_step] : 0.0f;
+        v16f ob[kO ? TN : 1];
+        if constexpr (kO) outlier_blocks<TN>(op, n16, nbase, mbase + b * 32, N, M, lane, ob);
+        if (kO && m >= M) continue;
 #pragma unroll
         for (int a = 0; a < TN; ++a) {
-            v16f o = {};
-            if constexpr (kO) o = outlier_block(op, n16, nbase + a * 32, mbase + b * 32, N, M, lane);
-            if (kO && m >= M) continue;
+            const v16f& o = ob[kO ? a : 0];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = nbase + a * 32 + 8 * g + 4 * fh;

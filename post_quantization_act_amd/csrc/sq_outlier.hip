@@ -63,8 +63,10 @@ __global__ __launch_bounds__(256) void k_gather_x(const uint16_t* __restrict__ x
     for (int t = lane; t < n16; t += kWave) o[t] = t < n ? xr[idx[t]] : (uint16_t)0;
 }
 
-// One thread per output channel k: w_ot[k, t] = w[idx[t], k], eight channels
-// t per 16-byte store; loads of consecutive k are coalesced.
+// One thread per output channel k and slice of outlier channels:
+// w_ot[k, t] = w[idx[t], k], eight channels t per 16-byte store, the octets of
+// t dealt round-robin over gridDim.y slices; loads of consecutive k are
+// coalesced.
 __global__ __launch_bounds__(256) void k_gather_w(const uint16_t* __restrict__ w, int64_t N, int64_t ldw,
                                                   const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
                                                   int64_t kp, uint16_t* __restrict__ w_ot) {
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void k_gather_w(const uint16_t* __restrict__ w
     const int n = __builtin_amdgcn_readfirstlane(count[0]);
     const int n16 = (n + 15) & ~15;
     uint16_t* o = w_ot + k * kp;
-    for (int t0 = 0; t0 < n16; t0 += 8) {
+    for (int t0 = 8 * (int)blockIdx.y; t0 < n16; t0 += 8 * (int)gridDim.y) {
         uint32_t v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -85,6 +87,8 @@ __global__ __launch_bounds__(256) void k_gather_w(const uint16_t* __restrict__ w
         *reinterpret_cast<uint4*>(o + t0) = make_uint4(v[0], v[1], v[2], v[3]);
     }
 }
+
+constexpr int kGatherSlices = 8;
 
 hipError_t launch_outlier_columns(const float* amax, int64_t K, float thr, int32_t* idx, int32_t* count, float* keep,
                                   hipStream_t st) {
@@ -99,8 +103,8 @@ hipError_t launch_gather_outliers(const uint16_t* x, int64_t M, int64_t ldx, con
                                   kp, x_o);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (N > 0) hipLaunchKernelGGL(k_gather_w, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, w, N, ldw, idx,
-                                  count, kp, w_ot);
+    if (N > 0) hipLaunchKernelGGL(k_gather_w, dim3((unsigned)((N + 255) / 256), kGatherSlices), dim3(256), 0, st, w,
+                                  N, ldw, idx, count, kp, w_ot);
     return hipGetLastError();
 }
 
