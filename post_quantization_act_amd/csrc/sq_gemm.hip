@@ -879,16 +879,21 @@ static GemmPath gemm_path(int64_t M, int64_t N, int64_t K, bool outl = false) {
     const bool ring = K > 0 && K % kBK == 0 && (uint64_t)N * (uint64_t)K < (1ull << 32) &&
                       (uint64_t)M * (uint64_t)K < (1ull << 32);
     if (!ring) return GemmPath::kGeneric;
-    // 256 x 256 tiles (one block per CU, two-stage 128 KB ring) when there are
-    // at least two per CU.  Otherwise 256 x 128 tiles (one block per CU,
-    // three-stage 144 KB ring) if they need no more rounds over the CUs than
-    // 128 x 128 tiles (two blocks per CU) would; else 128 x 128.
-    const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
-    if (t256 >= 512) return GemmPath::kRing256;
+    // Tile shape by estimated time: rounds of tiles over the CUs, each round
+    // weighted by the measured time of a stage per CU relative to 256 x 128
+    // tiles (one block per CU, three-stage 144 KB ring): 256 x 256 tiles (one
+    // block per CU, two-stage 128 KB ring) take about 1.6x for twice the work,
+    // a CU running two 128 x 128 blocks about 1.2x.  Weights x5 in integers;
+    // ties go to the larger tile.
     const int64_t cus = device_cu_count();
+    const int64_t t256 = ((N + 255) / 256) * ((M + 255) / 256);
     const int64_t t_wide = ((N + 255) / 256) * ((M + 127) / 128);
     const int64_t t128 = ((N + 127) / 128) * ((M + 127) / 128);
-    if ((t_wide + cus - 1) / cus <= (t128 + 2 * cus - 1) / (2 * cus)) return GemmPath::kRing256x128;
+    const int64_t c256 = 8 * ((t256 + cus - 1) / cus);
+    const int64_t c_wide = 5 * ((t_wide + cus - 1) / cus);
+    const int64_t c128 = 6 * ((t128 + 2 * cus - 1) / (2 * cus));
+    if (c256 <= c_wide && c256 <= c128) return GemmPath::kRing256;
+    if (c_wide <= c128) return GemmPath::kRing256x128;
     return GemmPath::kRing128;
 }
 

@@ -44,14 +44,17 @@ def test_status_strings_and_version():
 def test_gemm_kernel_choice():
     """The shape rule of the GEMM dispatch (for a 256-CU device; without a GPU
     the library assumes 256): decode kernels for M <= 16, the LDS ring kernel
-    for K % 128 == 0 (256 x 256 tiles once there are 512 of them, else
-    256 x 128 unless that needs more rounds over the CUs than 128 x 128), the
-    register-staged kernel otherwise."""
+    for K % 128 == 0 (the tile shape whose rounds over the CUs, weighted by
+    relative stage time 1.6 / 1.0 / 1.2 for 256 x 256 / 256 x 128 / two
+    128 x 128 blocks, cost least), the register-staged kernel otherwise."""
     assert sq.sq_gemm_kernel_name(16, 28672, 8192).startswith("k_gemm_decode_ring")
     assert sq.sq_gemm_kernel_name(16, 100, 1040).startswith("k_gemm_decode (")
     assert sq.sq_gemm_kernel_name(2048, 4096, 4096).startswith("k_gemm_ring<256,128")
     assert sq.sq_gemm_kernel_name(33000, 100, 384).startswith("k_gemm_ring<128,128")
     assert sq.sq_gemm_kernel_name(4096, 14336, 4096).startswith("k_gemm_ring<256,256")
+    assert sq.sq_gemm_kernel_name(4096, 4096, 4096).startswith("k_gemm_ring<256,256")  # one full round
+    assert sq.sq_gemm_kernel_name(2400, 8000, 4096).startswith("k_gemm_ring<256,128")   # 320 tiles: 2 rounds
+    assert sq.sq_gemm_kernel_name(3072, 4096, 4096).startswith("k_gemm_ring<256,256")   # 192 tiles, 1 round
     assert sq.sq_gemm_kernel_name(8192, 49152, 12288).startswith("k_gemm_ring<256,256")
     assert sq.sq_gemm_kernel_name(300, 520, 1040).startswith("k_gemm_generic")
     assert sq.sq_gemm_kernel_name(0, 5, 16).startswith("none")

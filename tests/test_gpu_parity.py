@@ -89,6 +89,8 @@ CASES = [
     (33000, 384, 100, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # enough output tiles for the 256 x 256 GEMM path, ragged M, N % 4 != 0, three stages
     (4100, 384, 16398, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
+    # exactly one round of 256 x 256 tiles over 256 CUs, two stages
+    (4096, 256, 4096, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 256),
     # decode path (M <= 16): ragged N, K not a multiple of 64, per-tensor scale
     (16, 1040, 100, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     # LDS-ring decode path (K % 2048 == 0): 257 channel groups over 256 blocks, per-tensor
