@@ -153,19 +153,18 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // ---- steps 2 + 3a fused: one read of W gives amax_w, s, inv_s and the
 // column maxima of diag(s) W ------------------------------------------------
 //
-// A block of 512 threads streams the rows [r0, r1) of W (bf16, 16-byte
-// aligned rows, N % 8 == 0).  Each iteration takes RB rows: row slot
-// t / TPR (TPR = 512 / RB threads per row); thread t % TPR of a slot owns
-// the 8-column groups q = t % TPR + TPR i, i < GPT, and keeps their running
-// column maxima in registers.  Per row: max |w| over the slot (shuffles, then
-// LDS across its wavefronts behind one barrier), s_j by the same fp64 rule
-// as k_row_absmax_factors, then the running maxima take |fl(s_j w)|.  The
-// next row's loads are issued once s_j is known (the fp64 factor then runs
-// with one row buffer live) and stay in flight through the update and the
-// next reduction; the barrier waits on LDS only, and nothing else touches
-// global memory in
-// the loop: amax_x is staged in LDS before, the per-row results are written
-// after it.  The block's column maxima (its RB slots combined through LDS)
+// A block of NT threads (512, or 1024 for the widest exact-alpha rows)
+// streams the rows [r0, r1) of W (bf16, 16-byte aligned rows, N % 8 == 0).
+// Each iteration takes RB rows: row slot t / TPR (TPR = NT / RB threads per
+// row); thread t % TPR of a slot owns the 8-column groups q = t % TPR + TPR i,
+// i < GPT, and keeps their running column maxima in registers (GR groups) or
+// LDS (GL more).  Per row: max |w| over the slot (shuffles, then LDS across
+// its wavefronts behind one barrier), s_j by the same fp64 rule as
+// k_row_absmax_factors, then the running maxima take |fl(s_j w)|.  The next
+// row's loads are issued at the top of the iteration and stay in flight
+// through the reduction, the factor and the update; the barrier waits on LDS
+// only, and nothing else touches global memory in the loop: amax_x is staged
+// in LDS before, the per-row results are written after it.  The block's column maxima (its RB slots combined through LDS)
 // leave as plain stores to partial[blockIdx.x][N]; k_colmax_reduce takes the
 // maximum over blocks.
 constexpr int kPrepThreads = 512;
@@ -175,8 +174,8 @@ __device__ __forceinline__ void lds_only_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int RB, int GR, int GL, bool kGeneral>
-__global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __restrict__ w, int64_t K, int64_t N,
+template <int RB, int GR, int GL, bool kGeneral, int NT = kPrepThreads>
+__global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, int64_t K, int64_t N,
                                                             int64_t ld, const float* __restrict__ amax_x,
                                                             float alpha, float* __restrict__ s,
                                                             float* __restrict__ inv_s, float* __restrict__ amax_w,
@@ -184,18 +183,18 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __rest
     // GR groups keep their running maxima in registers, GL more in LDS
     // (thread-major, so each access is conflict-free)
     constexpr int GPT = GR + GL;
-    constexpr int TPR = kPrepThreads / RB, WPR = TPR / kWave;
+    constexpr int TPR = NT / RB, WPR = TPR / kWave;
     static_assert(RB == 1 || GL == 0, "LDS-held maxima only with one row per iteration");
-    __shared__ float red[2][kPrepThreads / kWave];
+    __shared__ float red[2][NT / kWave];
     __shared__ float axl[kPrepMaxRows], srow[kPrepMaxRows], irow[kPrepMaxRows], arow[kPrepMaxRows];
     __shared__ float comb[RB > 1 ? (RB - 1) * TPR * 8 * GPT : 1];
-    __shared__ float cml[GL > 0 ? GL * 8 * kPrepThreads : 1];
+    __shared__ float cml[GL > 0 ? GL * 8 * NT : 1];
     const int t = threadIdx.x, slot = t / TPR, ts = t % TPR, wave = t / kWave, lane = t % kWave;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
     const int nrows = (int)min((int64_t)rows_per_block, K - r0);
-    for (int i = t; i < nrows; i += kPrepThreads) axl[i] = amax_x[r0 + i];
+    for (int i = t; i < nrows; i += NT) axl[i] = amax_x[r0 + i];
 #pragma unroll
-    for (int i = 0; i < GL * 8; ++i) cml[i * kPrepThreads + t] = 0.0f;
+    for (int i = 0; i < GL * 8; ++i) cml[i * NT + t] = 0.0f;
     const int iters = (nrows + RB - 1) / RB;
 
     float cm[GR][8];
@@ -216,6 +215,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __rest
     if (iters > 0) load_rows(0, cur);
     for (int it = 0; it < iters; ++it) {
         const int rl = it * RB + slot;
+        // the next rows' loads go out first, so they are in flight during this
+        // row's reduction, factor and column update
+        if (it + 1 < iters) load_rows(it + 1, nxt);
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
@@ -243,7 +245,6 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __rest
                 irow[rl] = ij;
                 arow[rl] = rm;
             }
-            if (it + 1 < iters) load_rows(it + 1, nxt);
 #pragma unroll
             for (int i = 0; i < GPT; ++i) {
                 const uint32_t u[4] = {cur[i].x, cur[i].y, cur[i].z, cur[i].w};
@@ -254,14 +255,12 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __rest
                         cm[i < GR ? i : 0][2 * h] = fmaxf(cm[i < GR ? i : 0][2 * h], a0);
                         cm[i < GR ? i : 0][2 * h + 1] = fmaxf(cm[i < GR ? i : 0][2 * h + 1], a1);
                     } else {
-                        float* c = cml + ((i - GR) * 8 + 2 * h) * kPrepThreads + t;
+                        float* c = cml + ((i - GR) * 8 + 2 * h) * NT + t;
                         c[0] = fmaxf(c[0], a0);
-                        c[kPrepThreads] = fmaxf(c[kPrepThreads], a1);
+                        c[NT] = fmaxf(c[NT], a1);
                     }
                 }
             }
-        } else if (it + 1 < iters) {
-            load_rows(it + 1, nxt);
         }
 #pragma unroll
         for (int i = 0; i < GPT; ++i) cur[i] = nxt[i];
@@ -283,7 +282,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __rest
             float o[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                o[e] = i < GR ? cm[i < GR ? i : 0][e] : cml[((i - GR) * 8 + e) * kPrepThreads + t];
+                o[e] = i < GR ? cm[i < GR ? i : 0][e] : cml[((i - GR) * 8 + e) * NT + t];
             if constexpr (RB > 1) {
                 for (int sl = 1; sl < RB; ++sl)
 #pragma unroll
@@ -294,7 +293,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep_rows(const bf16_t* __rest
             *reinterpret_cast<float4*>(dst + 4) = make_float4(o[4], o[5], o[6], o[7]);
         }
     }
-    for (int i = t; i < nrows; i += kPrepThreads) {
+    for (int i = t; i < nrows; i += NT) {
         s[r0 + i] = srow[i];
         inv_s[r0 + i] = irow[i];
         if (amax_w) amax_w[r0 + i] = arow[i];
@@ -426,7 +425,7 @@ int prep_blocks(int64_t K) {
 
 bool prep_fused_supported(const void* w, bool bf16, int64_t N, int64_t ld, float alpha) {
     const bool exact = alpha == 0.0f || alpha == 0.5f || alpha == 1.0f;
-    const int64_t max_groups = (int64_t)kPrepThreads * (exact ? 12 : 8);
+    const int64_t max_groups = exact ? 1024 * 6 : (int64_t)kPrepThreads * 8;
     return bf16 && N > 0 && N % 8 == 0 && N / 8 <= max_groups && rows_aligned16(w, ld, 2);
 }
 
@@ -439,9 +438,10 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
     const int rpb = (int)((K + nb - 1) / nb);
     const int64_t groups = N / 8;
     const bf16_t* wb = static_cast<const bf16_t*>(w);
-#define SQ_PREP(RB, GR, GL, G)                                                                                    \
-    hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G>), dim3((unsigned)nb), dim3(kPrepThreads), 0, st, wb, K, N, ld,    \
-                       amax_x, alpha, s, inv_s, amax_w, partial, rpb)
+#define SQ_PREP_NT(RB, GR, GL, G, NT)                                                                             \
+    hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G, NT>), dim3((unsigned)nb), dim3(NT), 0, st, wb, K, N, ld, amax_x,  \
+                       alpha, s, inv_s, amax_w, partial, rpb)
+#define SQ_PREP(RB, GR, GL, G) SQ_PREP_NT(RB, GR, GL, G, kPrepThreads)
     // alpha in {0, 1/2, 1} needs no fp64 pow: fewer registers, wider rows
     const bool general = !(alpha == 0.0f || alpha == 0.5f || alpha == 1.0f);
     if (general) {
@@ -460,9 +460,10 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
         else if (groups <= 2048) SQ_PREP(1, 4, 0, false);
         else if (groups <= 3072) SQ_PREP(1, 6, 0, false);
         else if (groups <= 4096) SQ_PREP(1, 8, 0, false);
-        else SQ_PREP(1, 4, 8, false);
+        else SQ_PREP_NT(1, 5, 1, false, 1024);  // up to 6144 groups: 5 in registers, 1 in LDS
     }
 #undef SQ_PREP
+#undef SQ_PREP_NT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, partial, nb, N, colmax);

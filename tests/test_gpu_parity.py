@@ -287,7 +287,8 @@ PREP_CASES = [
     (5472, 24576, 1.0, torch.bfloat16),   # six groups, alpha = 1, 22 rows per block, last block 16
     (5472, 24600, 0.5, torch.bfloat16),   # 3075 groups: eight per thread, the last ones partly masked
     (4096, 32768, 0.6, torch.bfloat16),   # eight groups, general alpha
-    (2736, 49152, 0.5, torch.bfloat16),   # twelve groups: 4 in registers, 8 in LDS
+    (2736, 49152, 0.5, torch.bfloat16),   # 1024 threads, six groups: 5 in registers, 1 in LDS
+    (3408, 40008, 1.0, torch.bfloat16),   # 5001 groups over 1024 threads: the LDS group partly masked
     # the two-call sequence: small W, general alpha beyond 32768 columns, N % 8 != 0, fp32
     (304, 1000, 0.5, torch.bfloat16),
     (2736, 49152, 0.75, torch.bfloat16),
