@@ -199,6 +199,50 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
     }
 }
 
+// The bf16 epilogue through LDS (N % 8 == 0, LDS free after the main loop):
+// per group of 32 token rows, the wavefront writes its dequantized outputs
+// into its own [m][n] LDS region (row stride WN + 8 elements, 16-byte aligned
+// rows), then copies them out 16 bytes (8 outputs) per lane along n, so each
+// store instruction covers whole 256-byte runs of rows of y instead of 64
+// scattered 8-byte pieces.  Same arithmetic as epilogue<> per element.
+// sx, sw: the wavefront's token and weight scales, staged in LDS.
+template <int TN, int TM>
+__device__ __forceinline__ void epilogue_bf16_lds(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
+                                                  const float* sx, const float* sw, int M, int N,
+                                                  uint16_t* __restrict__ y, uint16_t* ldsw) {
+    constexpr int WN = TN * 32, RS = WN + 8, CH = WN / 8;
+    static_assert((32 * CH) % 64 == 0, "copy-out chunks");
+    const int fr = lane % 32, fh = lane / 32;
+#pragma unroll
+    for (int b = 0; b < TM; ++b) {
+        const float xs = sx[b * 32 + fr];
+#pragma unroll
+        for (int a = 0; a < TN; ++a) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = a * 32 + 8 * g + 4 * fh;
+                const float4 ws = *reinterpret_cast<const float4*>(sw + nl);
+                const float y0 = ((float)acc[a][b][4 * g + 0] * xs) * ws.x;
+                const float y1 = ((float)acc[a][b][4 * g + 1] * xs) * ws.y;
+                const float y2 = ((float)acc[a][b][4 * g + 2] * xs) * ws.z;
+                const float y3 = ((float)acc[a][b][4 * g + 3] * xs) * ws.w;
+                *reinterpret_cast<uint2*>(ldsw + fr * RS + nl) = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wavefront's writes land before its reads
+#pragma unroll
+        for (int i = 0; i < 32 * CH / 64; ++i) {
+            const int c = lane + 64 * i;
+            const int ml = c / CH, nc = c % CH;
+            const int mm = mbase + b * 32 + ml, n = nbase + nc * 8;
+            const uint4 v = *reinterpret_cast<const uint4*>(ldsw + ml * RS + nc * 8);
+            if (mm < M && n < N) *reinterpret_cast<uint4*>(y + (int64_t)mm * N + n) = v;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next group reuses the region
+    }
+}
+
 // ---- ring kernel: global -> LDS copies without registers -----------------------
 
 // One 16-byte-per-lane copy from global memory (base + voff) to LDS at
@@ -208,6 +252,14 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
 // barrier that publishes the stage.
 __device__ __forceinline__ void copy16_to_lds(const int8_t* base, uint32_t voff, uint32_t lds_off) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_off), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
+// One dword per lane from global memory (base + voff) to LDS at lds_off + 4 * lane.
+__device__ __forceinline__ void copy4_to_lds(const void* base, uint32_t voff, uint32_t lds_off) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                  :
                  : "s"(lds_off), "v"(voff), "s"(base)
                  : "memory", "m0");
@@ -308,6 +360,23 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
         }
     };
 
+    // The tile's scales for the bf16 epilogue: w_scale of its BN rows of Wq,
+    // then x_scale of its BM token rows (clamped at the edges), copied into
+    // LDS ahead of the first stage (older than every copy, so the prologue's
+    // wait covers them).
+    constexpr bool kLdsEpi = kOut == 0 && !kAcc && !kO;
+    __shared__ __align__(16) float scl[kLdsEpi ? BN + BM : 1];
+    if constexpr (kLdsEpi) {
+        static_assert(BN % 64 == 0 && BM % 64 == 0 && (BN + BM) / 64 <= NW, "scale staging");
+        if (wave < (BN + BM) / 64) {
+            const int r = wave * 64 + lane;
+            const uint32_t la = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char*)scl + wave * 256);
+            if (wave * 64 < BN)
+                copy4_to_lds(w_scale, (uint32_t)min(n0 + r, N - 1) * 4u, la);
+            else
+                copy4_to_lds(x_scale, (uint32_t)(min(m0 + r - BN, M - 1) * xs_step) * 4u, la);
+        }
+    }
     // Prologue: stages 0 .. NS-1 in flight, wait for stage 0.
     const int nk = K / kBK;
 #pragma unroll
@@ -352,6 +421,16 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
         lds_barrier();
         kstep(1, kt + 1 < nk, nbuf, 0, 0, false, 0);
         buf = nbuf;
+    }
+    if constexpr (kLdsEpi) {
+        static_assert(NW * 32 * (WN + 8) * 2 <= NS * STAGE * 16, "LDS for the bf16 epilogue");
+        if (N % 8 == 0) {
+            lds_barrier();  // every wavefront is done reading the ring
+            uint16_t* ldsw = reinterpret_cast<uint16_t*>(lds) + wave * 32 * (WN + 8);
+            epilogue_bf16_lds<TN, TM>(acc, n0 + wn * WN, m0 + wm * WM, lane, scl + BN + wm * WM, scl + wn * WN, M,
+                                      N, static_cast<uint16_t*>(y), ldsw);
+            return;
+        }
     }
     epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
                                      acc_out, op);
