@@ -214,6 +214,96 @@ __global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int6
     else code_row(std::false_type{});
 }
 
+// bf16 rows with per-token scales (mode 0) or a fixed per-tensor maximum
+// (mode 2), K <= 16384: a block of 4 wavefronts walks rows blockIdx.x,
+// blockIdx.x + gridDim.x, ...  Each thread owns the NV 8-channel groups
+// t + 256 q of every row and keeps their inv_s in registers for all its rows
+// (loaded once, instead of once per row); the next row's 16-byte loads are in
+// flight while the current row is reduced (one barrier per row, LDS slots
+// alternating between rows) and coded.  Codes and scales as k_quant_act.
+template <int NV, bool kStatic>
+__global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          int64_t ld, const float* __restrict__ inv_s,
+                                                          int8_t* __restrict__ xq, float* __restrict__ x_scale,
+                                                          const uint32_t* __restrict__ gmax) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, t = threadIdx.x;
+    const int64_t groups = K / 8;
+    float is[NV][8];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t g = t + (int64_t)q * 256;
+        if (inv_s && g < groups) {
+            const float4 a = *reinterpret_cast<const float4*>(inv_s + g * 8);
+            const float4 b = *reinterpret_cast<const float4*>(inv_s + g * 8 + 4);
+            is[q][0] = a.x; is[q][1] = a.y; is[q][2] = a.z; is[q][3] = a.w;
+            is[q][4] = b.x; is[q][5] = b.y; is[q][6] = b.z; is[q][7] = b.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) is[q][i] = 1.0f;  // fl(x * 1) = x
+        }
+    }
+    float scale = 0.0f, r = 0.0f;
+    if constexpr (kStatic) {
+        group_scale(__uint_as_float(*gmax), scale, r);
+        if (blockIdx.x == 0 && t == 0) x_scale[0] = scale;
+    }
+    __shared__ float red[2][4];
+    uint4 cur[NV], nxt[NV];
+    auto load = [&](int64_t row, uint4 (&d)[NV]) {
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int64_t g = t + (int64_t)q * 256;
+            d[q] = (row < M && g < groups) ? ld16_stream(x + row * ld + g * 8) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    int64_t row = blockIdx.x;
+    load(row, cur);
+    for (int it = 0; row < M; ++it, row += gridDim.x) {
+        load(row + gridDim.x, nxt);
+        float v[NV][8];
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const uint32_t u[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[q][2 * h] = bf16_lo(u[h]) * is[q][2 * h];
+                v[q][2 * h + 1] = bf16_hi(u[h]) * is[q][2 * h + 1];
+            }
+            if constexpr (!kStatic) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[q][i]));
+            }
+        }
+        if constexpr (!kStatic) {
+            m = wave_max(m);
+            if (lane == 0) red[it & 1][wave] = m;
+            __syncthreads();
+            m = fmaxf(fmaxf(red[it & 1][0], red[it & 1][1]), fmaxf(red[it & 1][2], red[it & 1][3]));
+            group_scale(m, scale, r);
+            if (t == 0) x_scale[row] = scale;
+        }
+        auto code_row = [&](auto fast) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const int64_t g = t + (int64_t)q * 256;
+                if (g < groups) {
+                    int c[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
+                    st8_stream(xq + row * K + g * 8,
+                               make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+                }
+            }
+        };
+        if (r <= 3.402823466e38f) code_row(std::true_type{});
+        else code_row(std::false_type{});
+#pragma unroll
+        for (int q = 0; q < NV; ++q) cur[q] = nxt[q];
+    }
+}
+
 // Rows longer than the register-resident variants hold (K > 16384): four
 // wavefronts per row loop over it twice, once for the max, once for codes
 // (the second pass re-reads the row, mostly from L2).
@@ -454,10 +544,48 @@ static void launch_act_rows(const T* x, int64_t M, int64_t K, int64_t ld, const 
                        mode, xq, x_scale, gmax);
 }
 
+// Blocks resident per CU for the register footprint of NV groups (measured
+// best grids: about the resident count, fewer for the wider rows).
+static int act_stream_blocks_per_cu(int nv) { return nv <= 2 ? 8 : nv <= 6 ? 3 : 2; }
+
+template <int NV>
+static void launch_act_stream_nv(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode,
+                                 int8_t* xq, float* x_scale, const uint32_t* gmax, hipStream_t st) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t grid = std::min<int64_t>(M, (int64_t)cus * act_stream_blocks_per_cu(NV));
+    if (mode == 2)
+        hipLaunchKernelGGL((k_quant_act_stream<NV, true>), dim3((unsigned)grid), dim3(256), 0, st, x, M, K, ld, inv_s,
+                           xq, x_scale, gmax);
+    else
+        hipLaunchKernelGGL((k_quant_act_stream<NV, false>), dim3((unsigned)grid), dim3(256), 0, st, x, M, K, ld,
+                           inv_s, xq, x_scale, gmax);
+}
+
+static void launch_act_stream(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode,
+                              int8_t* xq, float* x_scale, const uint32_t* gmax, hipStream_t st) {
+    switch ((K / 8 + 255) / 256) {
+        case 1: return launch_act_stream_nv<1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        case 2: return launch_act_stream_nv<2>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        case 3: return launch_act_stream_nv<3>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        case 4: return launch_act_stream_nv<4>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        case 5: return launch_act_stream_nv<5>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        case 6: return launch_act_stream_nv<6>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        case 7: return launch_act_stream_nv<7>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        default: return launch_act_stream_nv<8>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    }
+}
+
 template <typename T>
 static void dispatch_act(const T* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode, int8_t* xq,
                          float* x_scale, uint32_t* gmax, hipStream_t st) {
     const int64_t groups = K / 8;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if ((mode == 0 || mode == 2) && groups <= 8 * 256 && rows_aligned16(x, ld, 2))
+            return launch_act_stream(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+    }
     if (groups <= 1 * kWave) return launch_act_rows<T, 1, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
     if (groups <= 2 * kWave) return launch_act_rows<T, 2, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
     if (groups <= 4 * kWave) return launch_act_rows<T, 4, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
