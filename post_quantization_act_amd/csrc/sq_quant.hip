@@ -23,6 +23,7 @@ namespace sqk {
 // channel (wq is [N, K], K contiguous).
 constexpr int kQwTile = 128;
 constexpr int kQwStride = kQwTile + 8;
+constexpr int kQwGroup = 16;
 
 template <typename T, bool kScaled, bool kVec>
 __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t K, int64_t N, int64_t ld,
@@ -32,15 +33,22 @@ __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, i
     __shared__ float r_s[kQwTile];
     __shared__ __align__(16) uint8_t tile[kQwTile * kQwStride];
 
-    const int64_t k0 = (int64_t)blockIdx.x * kQwTile;
-    const int64_t j0 = (int64_t)blockIdx.y * kQwTile;
+    // 1-D grid over the tiles in groups of kQwGroup output-channel tiles,
+    // input-channel tiles fastest inside a group: the blocks in flight together
+    // write whole rows of wq (contiguous) and read kQwGroup * 256-byte runs of
+    // each row of W.
+    const int64_t tj = (K + kQwTile - 1) / kQwTile;
+    const int64_t per = (int64_t)kQwGroup * tj;
+    const int64_t grp = blockIdx.x / per, rem = blockIdx.x % per;
+    const int64_t k0 = (grp * kQwGroup + rem / tj) * kQwTile;
+    const int64_t j0 = (rem % tj) * kQwTile;
     const int t = threadIdx.x;
     if (t < kQwTile) {
         const int64_t k = k0 + t;
         float scale = 0.0f, r = 0.0f;
         if (k < N) {
             group_scale(__uint_as_float(colmax[k]), scale, r);
-            if (blockIdx.y == 0) w_scale[k] = scale;
+            if (j0 == 0) w_scale[k] = scale;
         }
         r_s[t] = r;
     }
@@ -361,7 +369,9 @@ __global__ __launch_bounds__(256) void k_quant_act_long(const T* __restrict__ x,
 hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
                                const uint32_t* colmax, int8_t* wq, float* w_scale, hipStream_t st) {
     if (K <= 0 || N <= 0) return hipSuccess;
-    dim3 grid((unsigned)((N + kQwTile - 1) / kQwTile), (unsigned)((K + kQwTile - 1) / kQwTile));
+    const int64_t tiles = ((N + kQwTile - 1) / kQwTile) * ((K + kQwTile - 1) / kQwTile);
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;  // beyond 2^45 weights: not addressable in one grid
+    dim3 grid((unsigned)tiles);
     const bool vec = rows_aligned16(w, ld, bf16 ? 2 : 4);
     auto go = [&](auto tag, auto scaled, auto vecc) {
         using T = decltype(tag);
