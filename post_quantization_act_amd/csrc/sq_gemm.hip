@@ -345,7 +345,9 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
     // One k-step: NMF MFMAs on fragment slot `sl`; between them, the reads of
     // k-step `rks` of LDS buffer `rbuf` into slot `rsl`, and the copies of
     // stage `ckt`.  sched_barrier keeps this interleaving in program order.
-    auto kstep = [&](int sl, bool rd, int rbuf, int rks, int rsl, bool cp, int ckt) {
+    // Copies [c_lo, c_hi) of stage ckt are spread over the k-step's MFMAs.
+    auto kstep = [&](int sl, bool rd, int rbuf, int rks, int rsl, bool cp, int ckt, int c_lo, int c_hi) {
+        const int cn = c_hi - c_lo, cper = (cn + NMF - 1) / NMF;
 #pragma unroll
         for (int j = 0; j < NMF; ++j) {
             const int a = j / TM, b = j % TM;
@@ -355,10 +357,17 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
                 if (rd && j * DR + u < NRD) read_frag(rbuf, rks, j * DR + u, rsl);
 #pragma unroll
             for (int u = 0; u < DD; ++u)
-                if (cp && j * DD + u < L) copy(ckt, j * DD + u);
+                if (cp && u < cper && j * cper + u < cn) copy(ckt, c_lo + j * cper + u);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    // A stage's L copies go out in PARTS parts: the first in k-step 3 of the
+    // iteration that frees its buffer, the others in k-steps 0 .. PARTS-2 of
+    // the next iteration, so the copy traffic is not one burst per stage.
+    // Stage kt+1's last part then still precedes the L copies of stage kt+2
+    // (NS = 3) or is itself waited for (NS = 2): the vmcnt waits are unchanged.
+    constexpr int PARTS = (NS >= 3 && L % 3 == 0) ? 3 : (L % 2 == 0 ? 2 : 1);
+    constexpr int LP = L / PARTS;
 
     // The tile's scales for the bf16 epilogue: w_scale of its BN rows of Wq,
     // then x_scale of its BM token rows (clamped at the edges), copied into
@@ -399,27 +408,29 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
     int kt = 0, buf = 0;
     for (; kt + NS < nk; ++kt) {
         const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+        const bool late = kt > 0;  // the rest of stage kt-1+NS's copies
         __builtin_amdgcn_sched_barrier(0);
-        kstep(0, true, buf, 1, 1, false, 0);
-        kstep(1, true, buf, 2, 0, false, 0);
-        kstep(0, true, buf, 3, 1, false, 0);
+        kstep(0, true, buf, 1, 1, late && PARTS > 1, kt - 1 + NS, LP, 2 * LP);
+        kstep(1, true, buf, 2, 0, late && PARTS > 2, kt - 1 + NS, 2 * LP, 3 * LP);
+        kstep(0, true, buf, 3, 1, false, 0, 0, 0);
         // This wavefront's copies of stage kt+1 have landed (those of stages
         // kt+2 .. kt+NS-1 may stay in flight); after the barrier every
         // wavefront's have, and every read of this stage's buffer is done.
         wait_vmcnt<L*(NS - 2)>();
         lds_barrier();
-        kstep(1, true, nbuf, 0, 0, true, kt + NS);
+        kstep(1, true, nbuf, 0, 0, true, kt + NS, 0, LP);
         buf = nbuf;
     }
     for (; kt < nk; ++kt) {
         const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+        const bool late = kt > 0 && kt - 1 + NS < nk;
         __builtin_amdgcn_sched_barrier(0);
-        kstep(0, true, buf, 1, 1, false, 0);
-        kstep(1, true, buf, 2, 0, false, 0);
-        kstep(0, true, buf, 3, 1, false, 0);
+        kstep(0, true, buf, 1, 1, late && PARTS > 1, kt - 1 + NS, LP, 2 * LP);
+        kstep(1, true, buf, 2, 0, late && PARTS > 2, kt - 1 + NS, 2 * LP, 3 * LP);
+        kstep(0, true, buf, 3, 1, false, 0, 0, 0);
         wait_vmcnt<0>();
         lds_barrier();
-        kstep(1, kt + 1 < nk, nbuf, 0, 0, false, 0);
+        kstep(1, kt + 1 < nk, nbuf, 0, 0, false, 0, 0, 0);
         buf = nbuf;
     }
     if constexpr (kLdsEpi) {
