@@ -213,11 +213,9 @@ sq_status sq_prepare_weights(const float* amax_x, const void* w, sq_dtype wt, in
     uint32_t* colmax = static_cast<uint32_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)N * sizeof(uint32_t)));
     hipError_t e;
-    // The one-read pass streams each block's rows one (or a few) at a time; it
-    // wins once W is large enough for the saved read of W to dominate (at
-    // 4096 x 4096 the more parallel separate passes are faster).
-    const bool big = (uint64_t)K * (uint64_t)N >= (128ull << 20);
-    if (big && sqk::prep_fused_supported(w, bf16, N, ldw, alpha)) {
+    // The one-read pass (row maxima, factors and column maxima together) is
+    // faster than the separate passes at every size it supports.
+    if (sqk::prep_fused_supported(w, bf16, N, ldw, alpha)) {
         e = sqk::launch_prepare_weights(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, partial, colmax, stream);
     } else {
         e = sqk::launch_row_absmax_factors(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, stream);

@@ -301,20 +301,45 @@ __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, 
 }
 
 // colmax[k] = max over blocks b of partial[b][k], as fp32 bit patterns.
-__global__ __launch_bounds__(256) void k_colmax_reduce(const float* __restrict__ partial, int nb, int64_t N,
-                                                       uint32_t* __restrict__ colmax) {
-    const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (k >= N) return;
-    float m0 = 0.0f, m1 = 0.0f, m2 = 0.0f, m3 = 0.0f;
-    int b = 0;
-    for (; b + 3 < nb; b += 4) {
-        m0 = fmaxf(m0, partial[(int64_t)b * N + k]);
-        m1 = fmaxf(m1, partial[(int64_t)(b + 1) * N + k]);
-        m2 = fmaxf(m2, partial[(int64_t)(b + 2) * N + k]);
-        m3 = fmaxf(m3, partial[(int64_t)(b + 3) * N + k]);
+// A block of 1024 threads takes 64 columns: 16 column lanes of 4 floats
+// (16-byte loads; N % 8 == 0 on this path) x 64 row lanes striding over the
+// nb partial rows with four loads in flight, then the 64 row lanes are
+// combined through LDS.
+constexpr int kRedCols = 64, kRedRowLanes = 64;
+__global__ __launch_bounds__(1024) void k_colmax_reduce(const float* __restrict__ partial, int nb, int64_t N,
+                                                        uint32_t* __restrict__ colmax) {
+    const int cl = threadIdx.x % 16, rl = threadIdx.x / 16;
+    const int64_t c = (int64_t)blockIdx.x * kRedCols + cl * 4;
+    float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c < N) {
+        auto take = [&](const float4 v) {
+            m[0] = fmaxf(m[0], v.x);
+            m[1] = fmaxf(m[1], v.y);
+            m[2] = fmaxf(m[2], v.z);
+            m[3] = fmaxf(m[3], v.w);
+        };
+        int b = rl;
+        for (; b + 3 * kRedRowLanes < nb; b += 4 * kRedRowLanes) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v[u] = *reinterpret_cast<const float4*>(partial + (int64_t)(b + u * kRedRowLanes) * N + c);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) take(v[u]);
+        }
+        for (; b < nb; b += kRedRowLanes) take(*reinterpret_cast<const float4*>(partial + (int64_t)b * N + c));
     }
-    for (; b < nb; ++b) m0 = fmaxf(m0, partial[(int64_t)b * N + k]);
-    colmax[k] = __float_as_uint(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+    __shared__ float red[kRedRowLanes][kRedCols];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[rl][cl * 4 + e] = m[e];
+    __syncthreads();
+    if (threadIdx.x < kRedCols) {
+        float r = 0.0f;
+#pragma unroll 8
+        for (int q = 0; q < kRedRowLanes; ++q) r = fmaxf(r, red[q][threadIdx.x]);
+        const int64_t gc = (int64_t)blockIdx.x * kRedCols + threadIdx.x;
+        if (gc < N) colmax[gc] = __float_as_uint(r);
+    }
 }
 
 // Static per-tensor activation maximum from the calibration statistics:
@@ -442,22 +467,25 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
     hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G, NT>), dim3((unsigned)nb), dim3(NT), 0, st, wb, K, N, ld, amax_x,  \
                        alpha, s, inv_s, amax_w, partial, rpb)
 #define SQ_PREP(RB, GR, GL, G) SQ_PREP_NT(RB, GR, GL, G, kPrepThreads)
-    // alpha in {0, 1/2, 1} needs no fp64 pow: fewer registers, wider rows
+    // Rows per iteration so that each thread has 4-8 loads of 16 bytes in
+    // flight per row set (several rows at once for narrow W: with one row per
+    // iteration a 4096-column row is one 16-byte load per thread).  alpha in
+    // {0, 1/2, 1} needs no fp64 pow: fewer registers, wider rows.
     const bool general = !(alpha == 0.0f || alpha == 0.5f || alpha == 1.0f);
     if (general) {
         if (groups <= 128) SQ_PREP(4, 1, 0, true);
-        else if (groups <= 256) SQ_PREP(2, 1, 0, true);
-        else if (groups <= 512) SQ_PREP(1, 1, 0, true);
-        else if (groups <= 1024) SQ_PREP(1, 2, 0, true);
-        else if (groups <= 2048) SQ_PREP(1, 4, 0, true);
+        else if (groups <= 256) SQ_PREP(4, 2, 0, true);
+        else if (groups <= 512) SQ_PREP(4, 4, 0, true);
+        else if (groups <= 1024) SQ_PREP(4, 8, 0, true);
+        else if (groups <= 2048) SQ_PREP(2, 8, 0, true);
         else if (groups <= 3072) SQ_PREP(1, 6, 0, true);
         else SQ_PREP(1, 8, 0, true);
     } else {
         if (groups <= 128) SQ_PREP(4, 1, 0, false);
-        else if (groups <= 256) SQ_PREP(2, 1, 0, false);
-        else if (groups <= 512) SQ_PREP(1, 1, 0, false);
-        else if (groups <= 1024) SQ_PREP(1, 2, 0, false);
-        else if (groups <= 2048) SQ_PREP(1, 4, 0, false);
+        else if (groups <= 256) SQ_PREP(4, 2, 0, false);
+        else if (groups <= 512) SQ_PREP(4, 4, 0, false);
+        else if (groups <= 1024) SQ_PREP(4, 8, 0, false);
+        else if (groups <= 2048) SQ_PREP(2, 8, 0, false);
         else if (groups <= 3072) SQ_PREP(1, 6, 0, false);
         else if (groups <= 4096) SQ_PREP(1, 8, 0, false);
         else SQ_PREP_NT(1, 5, 1, false, 1024);  // up to 6144 groups: 5 in registers, 1 in LDS
@@ -466,7 +494,8 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
 #undef SQ_PREP_NT
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, partial, nb, N, colmax);
+    hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((N + kRedCols - 1) / kRedCols)), dim3(1024), 0, st, partial, nb,
+                       N, colmax);
     return hipGetLastError();
 }
 

@@ -276,21 +276,28 @@ def test_determinism_repeat_runs():
 
 
 PREP_CASES = [
-    # K, N, alpha, dtype.  W of at least 2^27 elements takes the one-read pass: every
-    # row layout of it, both factor kinds (alpha in {0, 1/2, 1} without pow, others
-    # with it), ragged rows per block and ragged column groups.
-    (131072, 1024, 0.5, torch.bfloat16),  # 4 rows per iteration, 512 blocks of 256 rows
-    (65536, 2048, 0.75, torch.bfloat16),  # 2 rows per iteration, general alpha
-    (32768, 4096, 0.5, torch.bfloat16),   # one group per thread
-    (16384, 8192, 0.4, torch.bfloat16),   # two groups, general alpha
-    (8192, 16384, 0.0, torch.bfloat16),   # four groups, alpha = 0
+    # K, N, alpha, dtype.  bf16 W with N % 8 == 0 takes the one-read pass: every
+    # row layout of it (rows per iteration x 8-column groups per thread), both
+    # factor kinds (alpha in {0, 1/2, 1} without pow, others with it), ragged rows
+    # per block, blocks with fewer rows than one iteration takes, ragged groups.
+    (131072, 1024, 0.5, torch.bfloat16),  # 4 rows per iteration, one group, 512 blocks of 256 rows
+    (65536, 2048, 0.75, torch.bfloat16),  # 4 rows, two groups, general alpha
+    (32768, 4096, 0.5, torch.bfloat16),   # 4 rows, four groups
+    (4096, 4096, 0.5, torch.bfloat16),    # the attention-projection weight: 16 rows per block
+    (16384, 8192, 0.4, torch.bfloat16),   # 4 rows, eight groups, general alpha
+    (2000, 8192, 1.0, torch.bfloat16),    # 4 rows, eight groups, 8 rows per block (250 blocks)
+    (8192, 16384, 0.0, torch.bfloat16),   # 2 rows, eight groups, alpha = 0
+    (3008, 16376, 0.3, torch.bfloat16),   # 2 rows, eight groups (the last partly masked), general alpha
+    (304, 800, 0.5, torch.bfloat16),      # 2 rows per block for 4 row slots: two slots idle
+    (16, 4096, 1.0, torch.bfloat16),      # one row per block
+    (1008, 2048, 0.75, torch.bfloat16),   # 4 rows per block, general alpha
     (5472, 24576, 1.0, torch.bfloat16),   # six groups, alpha = 1, 22 rows per block, last block 16
     (5472, 24600, 0.5, torch.bfloat16),   # 3075 groups: eight per thread, the last ones partly masked
     (4096, 32768, 0.6, torch.bfloat16),   # eight groups, general alpha
     (2736, 49152, 0.5, torch.bfloat16),   # 1024 threads, six groups: 5 in registers, 1 in LDS
     (3408, 40008, 1.0, torch.bfloat16),   # 5001 groups over 1024 threads: the LDS group partly masked
-    # the two-call sequence: small W, general alpha beyond 32768 columns, N % 8 != 0, fp32
-    (304, 1000, 0.5, torch.bfloat16),
+    # the two-call sequence: general alpha beyond 32768 columns, N % 8 != 0, fp32
+    (304, 1001, 0.5, torch.bfloat16),
     (2736, 49152, 0.75, torch.bfloat16),
     (112, 1001, 0.5, torch.bfloat16),
     (208, 512, 0.5, torch.float32),
