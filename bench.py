@@ -56,7 +56,8 @@ def _parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", type=int, default=2, help="workload of the step: 2 = attention projection")
+    p.add_argument("--config", default="attn_proj_2048x4096x4096_bf16",
+                   help="workload of the step, by name (the attention projection by default)")
     p.add_argument("--pool-gb", type=float, default=1.0, help="rotate inputs over at least this many GB")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-large", action="store_true", help="skip the large-shape kernel table and alpha sweep")
@@ -177,7 +178,7 @@ def _large(torch, sq, synth, pipeline, dev):
     large shapes, the decode weight stream, and the alpha sweep."""
     tm = _Timer(torch)
     out = {}
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS[synth.LARGE]
     M, K, N, T = cfg.M, cfg.K, cfg.N, cfg.calib_tokens
     print(f"# large: drawing {cfg.name} ({T} calibration tokens)", file=sys.stderr, flush=True)
     inp = synth.make(cfg, device=dev)
@@ -306,7 +307,7 @@ def _comparator(torch, sq, synth, pipeline, dev):
     Infinity Cache), the two GEMMs alone, and the output error of each against
     X W in fp64 on a 256-token sample."""
     tm = _Timer(torch)
-    cfg = synth.CONFIGS[2]
+    cfg = synth.CONFIGS[synth.ATTN_PROJ]
     M, K, N = cfg.M, cfg.K, cfg.N
     nsets = 6  # 6 x (16.8 MB x + 33.5 MB w + 16.8 MB codes) > 256 MB
     print(f"# comparator: drawing {nsets} sets of {cfg.name}", file=sys.stderr, flush=True)

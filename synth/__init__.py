@@ -42,7 +42,7 @@ class Config:
     gran: str = "per_token"  # activation granularity
     w_prequant: bool = False  # weights arrive smoothed and quantized (decode shape)
     notes: str = ""
-    index: int = 0
+    seed_tag: int = 0        # salt of the workload's random streams
 
     @property
     def calib_tokens(self) -> int:
@@ -53,20 +53,27 @@ class Config:
         return torch.float32 if self.x_dtype == "f32" else torch.bfloat16
 
 
-CONFIGS = {
-    1: Config("tiny_linear_64x256x256_f32", 64, 256, 256, "f32", "normal", 3, 100.0, 100.0, 0.02,
-              0, 0, (0.5,), "per_tensor", index=1,
-              notes="calibrates on X itself; per-tensor dynamic activation scale"),
-    2: Config("attn_proj_2048x4096x4096_bf16", 2048, 4096, 4096, "bf16", "normal", 41, 50.0, 150.0,
-              0.02, 16, 512, (0.5,), index=2),
-    3: Config("mlp_up_4096x4096x14336_bf16", 4096, 4096, 14336, "bf16", "normal", 41, 100.0, 100.0,
-              0.02, 16, 512, (0.5,), index=3),
-    4: Config("decode_16x8192x28672_bf16", 16, 8192, 28672, "bf16", "normal", 82, 100.0, 100.0,
-              0.02, 16, 512, (0.5,), w_prequant=True, index=4),
-    5: Config("large_8192x12288x49152_bf16_t4", 8192, 12288, 49152, "bf16", "t4", 61, 200.0, 200.0,
-              0.015, 512, 512, (0.4, 0.5, 0.6, 0.75), index=5,
-              notes="calibration is 512 sequences x 512 tokens"),
-}
+TINY = "tiny_linear_64x256x256_f32"
+ATTN_PROJ = "attn_proj_2048x4096x4096_bf16"
+MLP_UP = "mlp_up_4096x4096x14336_bf16"
+DECODE = "decode_16x8192x28672_bf16"
+LARGE = "large_8192x12288x49152_bf16_t4"
+ALL = (TINY, ATTN_PROJ, MLP_UP, DECODE, LARGE)
+
+CONFIGS = {c.name: c for c in (
+    Config(TINY, 64, 256, 256, "f32", "normal", 3, 100.0, 100.0, 0.02,
+           0, 0, (0.5,), "per_tensor", seed_tag=1,
+           notes="calibrates on X itself; per-tensor dynamic activation scale"),
+    Config(ATTN_PROJ, 2048, 4096, 4096, "bf16", "normal", 41, 50.0, 150.0,
+           0.02, 16, 512, (0.5,), seed_tag=2),
+    Config(MLP_UP, 4096, 4096, 14336, "bf16", "normal", 41, 100.0, 100.0,
+           0.02, 16, 512, (0.5,), seed_tag=3),
+    Config(DECODE, 16, 8192, 28672, "bf16", "normal", 82, 100.0, 100.0,
+           0.02, 16, 512, (0.5,), w_prequant=True, seed_tag=4),
+    Config(LARGE, 8192, 12288, 49152, "bf16", "t4", 61, 200.0, 200.0,
+           0.015, 512, 512, (0.4, 0.5, 0.6, 0.75), seed_tag=5,
+           notes="calibration is 512 sequences x 512 tokens"),
+)}
 
 
 def seed_for(*parts) -> int:
@@ -130,12 +137,12 @@ class Inputs:
     out_fac: torch.Tensor = field(default=None)
 
 
-def make(cfg: Config | int, device="cpu", M=None, K=None, N=None, calib_chunks=None,
+def make(cfg: Config | str, device="cpu", M=None, K=None, N=None, calib_chunks=None,
          chunk_tokens=None, variant=0, with_w=True) -> Inputs:
     """Draw one configuration's inputs (optionally at a reduced size with the
     same recipe).  ``variant`` selects an independent set of draws (the
     benchmark rotates several so timed reads come from HBM, not cache)."""
-    if isinstance(cfg, int):
+    if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     M = cfg.M if M is None else M
     K = cfg.K if K is None else K
@@ -144,8 +151,8 @@ def make(cfg: Config | int, device="cpu", M=None, K=None, N=None, calib_chunks=N
     ctok = cfg.chunk_tokens if chunk_tokens is None else chunk_tokens
     n_out = cfg.n_out if K == cfg.K else max(1, round(cfg.n_out * K / cfg.K))
     dt = cfg.torch_dtype
-    out_idx, out_fac = outlier_set(K, n_out, cfg.out_lo, cfg.out_hi, (cfg.index, K), device)
-    tag = (cfg.index, M, K, N, variant)
+    out_idx, out_fac = outlier_set(K, n_out, cfg.out_lo, cfg.out_hi, (cfg.seed_tag, K), device)
+    tag = (cfg.seed_tag, M, K, N, variant)
     x = activations(M, K, cfg.body, out_idx, out_fac, dt, _gen(device, *tag, "x"), device)
     w = weights(K, N, cfg.w_std, dt, _gen(device, *tag, "w"), device) if with_w else None
     if chunks == 0:

@@ -35,13 +35,14 @@ def _sample(n, k, seed):
     return np.unique(np.concatenate([idx, [0, n - 1]]))
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
-def test_full_size_config(cfg_id):
-    cfg = synth.CONFIGS[cfg_id]
+@pytest.mark.parametrize("name", synth.ALL)
+def test_full_size_config(name):
+    cfg = synth.CONFIGS[name]
+    tag = cfg.seed_tag
     alpha = 0.5
     gran = sq.SQ_PER_TENSOR if cfg.gran == "per_tensor" else sq.SQ_PER_TOKEN
     ogran = oracle.PER_TENSOR if cfg.gran == "per_tensor" else oracle.PER_TOKEN
-    _say(f"config {cfg_id} {cfg.name}: drawing inputs on the GPU")
+    _say(f"workload {cfg.name}: drawing inputs on the GPU")
     inp = synth.make(cfg, device=DEV)
     M, K, N = cfg.M, cfg.K, cfg.N
     b = pipeline.W8A8Buffers.allocate(M, N, K, gran, DEV)
@@ -59,7 +60,7 @@ def test_full_size_config(cfg_id):
     np.testing.assert_array_equal(_np(b.inv_s), inv_s, err_msg="inv_s")
 
     _say("  oracle: sampled output channels and tokens")
-    cols = _sample(N, 96, cfg_id)
+    cols = _sample(N, 96, tag)
     wq_o, ws_o = oracle.quant_weight(np.ascontiguousarray(w[:, cols]), s)
     np.testing.assert_array_equal(_np(b.w_scale)[cols], ws_o, err_msg="w_scale")
     np.testing.assert_array_equal(_np(b.wq)[cols], wq_o, err_msg="wq")
@@ -68,11 +69,11 @@ def test_full_size_config(cfg_id):
         xq_all, xs_o = oracle.quant_act(x, inv_s, ogran)
         np.testing.assert_array_equal(_np(b.x_scale), xs_o, err_msg="x_scale")
         np.testing.assert_array_equal(_np(b.xq), xq_all, err_msg="xq")
-        rows = _sample(M, 96, cfg_id + 10)
+        rows = _sample(M, 96, tag + 10)
         xq_o = xq_all[rows]
         xs_rows = xs_o
     else:
-        rows = _sample(M, 96, cfg_id + 10)
+        rows = _sample(M, 96, tag + 10)
         xq_o, xs_rows = oracle.quant_act(np.ascontiguousarray(x[rows]), inv_s, ogran)
         np.testing.assert_array_equal(_np(b.x_scale)[rows], xs_rows, err_msg="x_scale")
         np.testing.assert_array_equal(_np(b.xq)[rows], xq_o, err_msg="xq")
@@ -84,13 +85,14 @@ def test_full_size_config(cfg_id):
     _say(f"  sampled {len(rows)} tokens x {len(cols)} channels bit-exact")
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
-def test_full_size_gemm_freivalds(cfg_id):
+@pytest.mark.parametrize("name", [synth.ATTN_PROJ, synth.MLP_UP, synth.DECODE, synth.LARGE])
+def test_full_size_gemm_freivalds(name):
     """int32 accumulators of the full product: acc . r == Xq . (Wq^T r)."""
-    cfg = synth.CONFIGS[cfg_id]
+    cfg = synth.CONFIGS[name]
+    tag = cfg.seed_tag
     M, K, N = cfg.M, cfg.K, cfg.N
     g = torch.Generator(device=DEV)
-    g.manual_seed(1000 + cfg_id)
+    g.manual_seed(1000 + tag)
     xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=DEV, generator=g)
     wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=DEV, generator=g)
     xs = torch.rand(M, device=DEV, generator=g) * 0.01
@@ -99,11 +101,11 @@ def test_full_size_gemm_freivalds(cfg_id):
     acc = torch.empty(M, N, dtype=torch.int32, device=DEV)
     sq.sq_gemm_w8a8(xq, xs, sq.SQ_PER_TOKEN, wq, ws, y, acc)
     torch.cuda.synchronize()
-    _say(f"config {cfg_id}: GEMM {M}x{N}x{K} done; Freivalds on the host")
+    _say(f"workload {cfg.name}: GEMM {M}x{N}x{K} done; Freivalds on the host")
     A = _np(xq).astype(np.int64)
     B = _np(wq).astype(np.int64)
     C = _np(acc).astype(np.int64)
-    rng = np.random.default_rng(cfg_id)
+    rng = np.random.default_rng(tag)
     for _ in range(2):
         r = rng.choice(np.array([-1, 1], dtype=np.int64), size=N)
         lhs = C @ r
@@ -118,7 +120,7 @@ def test_full_size_gemm_freivalds(cfg_id):
 
 def test_all_alphas_large_config_factors():
     """Factors for every alpha of the large workload, from one weight pass."""
-    cfg = synth.CONFIGS[5]
+    cfg = synth.CONFIGS[synth.LARGE]
     K = cfg.K
     g = torch.Generator(device="cpu")
     g.manual_seed(5)

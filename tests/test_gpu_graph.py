@@ -20,7 +20,7 @@ def _snapshot(b):
 
 @pytest.mark.parametrize("gran", [sq.SQ_PER_TOKEN, sq.SQ_PER_TENSOR])
 def test_graph_replays_match_eager(gran):
-    cfg = synth.CONFIGS[2]
+    cfg = synth.CONFIGS[synth.ATTN_PROJ]
     M, K, N = 320, 1024, 768
     a = synth.make(cfg, device=DEV, M=M, K=K, N=N, calib_chunks=2, chunk_tokens=256, variant=0)
     c = synth.make(cfg, device=DEV, M=M, K=K, N=N, calib_chunks=2, chunk_tokens=256, variant=1)

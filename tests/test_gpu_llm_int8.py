@@ -205,7 +205,7 @@ def test_llm_int8_attention_projection_full_size():
     """The 2048 x 4096 x 4096 attention-projection workload (41 outlier
     channels x U[50, 150]): the outlier set, codes and gathered operands in
     full, the output on a seeded sample of token rows."""
-    inp = synth.make(2, with_w=True, calib_chunks=1, chunk_tokens=16)
+    inp = synth.make(synth.ATTN_PROJ, with_w=True, calib_chunks=1, chunk_tokens=16)
     print("llm_int8 full size 2048x4096x4096 kernel=" + sq.sq_gemm_outlier_kernel_name(2048, 4096, 4096),
           flush=True)
     b = _run(inp.x, inp.w, 6.0)

@@ -194,7 +194,7 @@ def test_floor_on_dead_channels():
 
 # ---- exact identity (fp64) --------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", synth.ALL)
 def test_equivalence_identity_fp64(cfg):
     """X diag(s)^-1 diag(s) W = X W (page "大模型训练、适配与推理" section 3.5):
     in fp64 the two products agree to rounding, rel err <= 1e-12, on each
@@ -329,7 +329,7 @@ def test_bf16_rounding_matches_torch():
 # ---- calibration resume and the direction of the effect ----------------------------
 
 def test_calibration_chunked_equals_single_pass():
-    inp = synth.make(2, M=16, K=256, N=8, calib_chunks=6, chunk_tokens=40)
+    inp = synth.make(synth.ATTN_PROJ, M=16, K=256, N=8, calib_chunks=6, chunk_tokens=40)
     c = synth.to_numpy(inp.calib)
     whole = oracle.calib_absmax(c)
     amax = None
@@ -342,7 +342,7 @@ def test_calibration_chunked_equals_single_pass():
     np.testing.assert_array_equal(whole, np.abs(oracle.bf16_to_f32(c)).max(axis=0))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 5])
+@pytest.mark.parametrize("cfg", [synth.TINY, synth.ATTN_PROJ, synth.LARGE])
 def test_smoothing_reduces_error_on_outliers(cfg):
     """On outlier-bearing inputs the smoothed W8A8 output is closer to X W than
     plain per-tensor W8A8 (direction given by the accuracy table of page
@@ -676,7 +676,7 @@ def test_llm_int8_all_outliers_is_the_16bit_product():
     assert (np.abs(r["y32"] - ref) <= ulp).all()
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", [synth.ATTN_PROJ, synth.MLP_UP])
 def test_llm_int8_keeps_accuracy_on_outlier_data(cfg):
     """The pages' comparison: direct W8A8 collapses on outlier activations,
     while the mixed-precision route keeps 16-bit accuracy (and SmoothQuant
