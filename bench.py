@@ -420,7 +420,7 @@ def main():
     b = pipeline.W8A8Buffers.allocate(M, N, K, gran, dev)
     stream = torch.cuda.current_stream(dev)
 
-    stages = ["calib_absmax", "prepare_weights", "quant_act", "gemm_w8a8"]
+    stages = ["calib_absmax", "prepare_and_quant_act", "gemm_w8a8"]
 
     def step(i, ev=None):
         s = sets[i % pool]
@@ -429,15 +429,13 @@ def main():
         pipeline.calibrate(s.calib, b.amax_x)
         if ev is not None:
             ev[1].record(stream)
-        sq.sq_prepare_weights(b.amax_x, s.w, alpha, b.s, b.inv_s, b.amax_w, b.wq, b.w_scale, b.ws_p)
+        sq.sq_prepare_and_quant_act(b.amax_x, s.w, alpha, b.s, b.inv_s, b.amax_w, b.wq, b.w_scale, s.x, gran, b.xq,
+                                    b.x_scale, b.ws_pa)
         if ev is not None:
             ev[2].record(stream)
-        sq.sq_quant_act(s.x, b.inv_s, gran, b.xq, b.x_scale, b.ws_a)
-        if ev is not None:
-            ev[3].record(stream)
         sq.sq_gemm_w8a8(b.xq, b.x_scale, gran, b.wq, b.w_scale, b.y)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     if args.launch == "graph":
         graphs = [pipeline.CapturedPass(st.x, st.w, st.calib, alpha, gran, b) for st in sets]
@@ -475,8 +473,7 @@ def main():
     ops = 2.0 * M * N * K
     bytes_alg = {
         "calib_absmax": T * K * esz + 8 * K,
-        "prepare_weights": 2 * K * N * esz + N * K + 4 * N + 16 * K,
-        "quant_act": M * K * esz + M * K + 4 * M + 4 * K,
+        "prepare_and_quant_act": (2 * K * N * esz + N * K + 4 * N + 16 * K) + (M * K * esz + M * K + 4 * M + 4 * K),
         "gemm_w8a8": M * K + N * K + 2 * M * N + 4 * (M + N),
     }
     kernels = {}
@@ -489,8 +486,10 @@ def main():
     kernels["gemm_w8a8"].update({"ops": ops, "TOPS": round(gemm_tops, 1),
                                  "pct_int8_peak": round(100 * gemm_tops / INT8_PEAK_TOPS, 1)})
     kernels["note"] = ("HIP-event intervals per call from separate eager passes (not the timed ones): calib_absmax "
-                       "includes zeroing the running max; prepare_weights is steps 2 + 3 (one read of W for row and "
-                       "column maxima, a reduction of per-block maxima, one read + write for the codes)")
+                       "includes zeroing the running max; prepare_and_quant_act is steps 2-4 (one read of W for row "
+                       "and column maxima, a reduction of per-block maxima, then the weight codes and the activation "
+                       "codes in one launch); algorithmic bytes are those of steps 2 + 3 (2 B per W element read, "
+                       "1 written) plus step 4 (2 B per X element read, 1 written)")
 
     if args.copy_probe_mb > 0:
         # a plain copy of known size whose source is not cache resident: 1 GiB

@@ -91,7 +91,8 @@ typedef enum {
     SQ_OP_QUANT_WEIGHT = 2,
     SQ_OP_QUANT_ACT = 3,
     SQ_OP_GEMM_W8A8 = 4,
-    SQ_OP_PREPARE_WEIGHTS = 5
+    SQ_OP_PREPARE_WEIGHTS = 5,
+    SQ_OP_PREPARE_AND_QUANT_ACT = 6
 } sq_op;
 
 /*
@@ -187,6 +188,34 @@ sq_status sq_prepare_weights(const float *amax_x, const void *w, sq_dtype wt, in
 sq_status sq_quant_act(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx,
                        const float *inv_s, sq_act_gran g, int8_t *xq, float *x_scale, void *ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Steps 2, 3 and 4 in one call -- the factors, the weight codes and the
+ * activation codes of one batch (page "4.2 W8A8 量化与 SmoothQuant" section
+ * 7.1; page "大模型训练、适配与推理" section 3.5).
+ *
+ * Computes exactly what sq_prepare_weights(amax_x, w, ..., alpha, s, inv_s,
+ * amax_w, wq, w_scale, ...) followed by sq_quant_act(x, ..., inv_s, g, xq,
+ * x_scale, ...) compute, with the same arguments and results; it rejects
+ * what either of them rejects.  For bf16 W and X with 16-byte aligned rows, W
+ * as the one-read pass of sq_prepare_weights takes it, K <= 4096 and
+ * SQ_PER_TOKEN, the weight codes and the activation codes are written by one
+ * launch (each alone leaves the memory system idle during its start and tail
+ * at these sizes).  Other inputs take the two calls internally.
+ *
+ *   amax_x, w, wt, K, N, ldw, alpha, s, inv_s, amax_w, wq, w_scale
+ *                   as sq_prepare_weights;
+ *   x, xt, M, ldx, g, xq, x_scale   as sq_quant_act (x is [M, K]);
+ *   ws              workspace of sq_workspace_size(SQ_OP_PREPARE_AND_QUANT_ACT,
+ *                   M, N, K, g) bytes, 16-byte aligned: the workspace of
+ *                   sq_prepare_weights, then (rounded to 256 bytes) that of
+ *                   sq_quant_act.
+ */
+sq_status sq_prepare_and_quant_act(const float *amax_x, const void *w, sq_dtype wt, int64_t K, int64_t N,
+                                   int64_t ldw, float alpha, float *s, float *inv_s, float *amax_w, int8_t *wq,
+                                   float *w_scale, const void *x, sq_dtype xt, int64_t M, int64_t ldx,
+                                   sq_act_gran g, int8_t *xq, float *x_scale, void *ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 /*
  * LayerNorm fold (page "4.2 W8A8 量化与 SmoothQuant" section 6: the factor

@@ -20,7 +20,8 @@ __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
     "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
-    "sq_gemm_w8a8", "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
+    "sq_gemm_w8a8", "sq_prepare_weights", "sq_prepare_and_quant_act", "SQ_OP_PREPARE_WEIGHTS",
+    "SQ_OP_PREPARE_AND_QUANT_ACT", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
     "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier",
     "sq_gemm_outlier_kernel_name", "sq_workspace_size",
     "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
@@ -31,11 +32,12 @@ _LIB_PATH = os.path.join(_HERE, "libsq.so")
 
 SQ_F32, SQ_BF16 = 0, 1
 SQ_PER_TOKEN, SQ_PER_TENSOR = 0, 1
-SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, SQ_OP_GEMM_W8A8, SQ_OP_PREPARE_WEIGHTS = range(6)
+(SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, SQ_OP_GEMM_W8A8, SQ_OP_PREPARE_WEIGHTS,
+ SQ_OP_PREPARE_AND_QUANT_ACT) = range(7)
 
 EXPORTED_SYMBOLS = (
     "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights",
-    "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
+    "sq_prepare_and_quant_act", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
     "sq_gather_outliers", "sq_gemm_w8a8_outlier", "sq_workspace_size", "sq_status_str", "sq_last_error",
     "sq_version", "sq_gemm_kernel_name", "sq_gemm_outlier_kernel_name",
 )
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.sq_quant_act.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.sq_gemm_w8a8.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
     L.sq_prepare_weights.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.sq_prepare_and_quant_act.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp, vp, vp, i32, i64, i64,
+                                           i32, vp, vp, vp, sz, vp]
     L.sq_static_act_max.argtypes = [vp, vp, i64, vp, vp]
     L.sq_quant_act_static.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
     L.sq_fold_layernorm.argtypes = [vp, vp, vp, i64, vp, vp, vp]
@@ -240,6 +244,32 @@ def sq_prepare_weights(amax_x: torch.Tensor, w: torch.Tensor, alpha: float, s: t
     _check(lib().sq_prepare_weights(_ptr(amax_x), _ptr(w), _dtype(w), K, N, ld, ctypes.c_float(alpha), _ptr(s),
                                     _ptr(inv_s), _ptr(amax_w), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
                                     _stream(_dev(w, amax_x), stream)))
+
+
+def sq_prepare_and_quant_act(amax_x: torch.Tensor, w: torch.Tensor, alpha: float, s: torch.Tensor,
+                             inv_s: torch.Tensor, amax_w: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor,
+                             x: torch.Tensor, gran: int, xq: torch.Tensor, x_scale: torch.Tensor,
+                             ws: torch.Tensor | None, stream=None) -> None:
+    """Steps 2, 3 and 4 in one call: sq_prepare_weights(amax_x, w, alpha, ...) then
+    sq_quant_act(x, inv_s, gran, xq, x_scale, ...), with the same results."""
+    K, N, ldw = _rows(w)
+    M, Kx, ldx = _rows(x)
+    if Kx != K:
+        raise ValueError(f"x has {Kx} channels, w has {K}")
+    _dense(amax_x, "amax_x", (K,), torch.float32)
+    _dense(s, "s", (K,), torch.float32)
+    _dense(inv_s, "inv_s", (K,), torch.float32)
+    if amax_w is not None:
+        _dense(amax_w, "amax_w", (K,), torch.float32)
+    _dense(wq, "wq", (N, K), torch.int8)
+    _dense(w_scale, "w_scale", (N,), torch.float32)
+    _dense(xq, "xq", (M, K), torch.int8)
+    _dense(x_scale, "x_scale", (1,) if gran == SQ_PER_TENSOR else (M,), torch.float32)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sq_prepare_and_quant_act(_ptr(amax_x), _ptr(w), _dtype(w), K, N, ldw, ctypes.c_float(alpha), _ptr(s),
+                                          _ptr(inv_s), _ptr(amax_w), _ptr(wq), _ptr(w_scale), _ptr(x), _dtype(x), M,
+                                          ldx, int(gran), _ptr(xq), _ptr(x_scale), _ptr(ws), nbytes,
+                                          _stream(_dev(w, x), stream)))
 
 
 def sq_fold_layernorm(gamma: torch.Tensor, beta: torch.Tensor | None, inv_s: torch.Tensor, gamma_out: torch.Tensor,

@@ -120,6 +120,9 @@ size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran 
                                         round256((size_t)sqk::prep_blocks(K) * (size_t)N * sizeof(float))
                                   : 0;
         case SQ_OP_QUANT_ACT: return g == SQ_PER_TENSOR ? 256 : 0;
+        case SQ_OP_PREPARE_AND_QUANT_ACT:
+            return round256(sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, M, N, K, g)) +
+                   sq_workspace_size(SQ_OP_QUANT_ACT, M, N, K, g);
         default: return 0;
     }
 }
@@ -251,6 +254,62 @@ sq_status sq_quant_act(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t
     hipError_t e = sqk::launch_fill_u32(gmax, 1, 0u, stream);
     if (e == hipSuccess) e = sqk::launch_quant_act(x, bf, M, K, ldx, inv_s, 1, xq, x_scale, gmax, stream);
     if (e == hipSuccess) e = sqk::launch_quant_act(x, bf, M, K, ldx, inv_s, 2, xq, x_scale, gmax, stream);
+    return hip_result(e, fn);
+}
+
+sq_status sq_prepare_and_quant_act(const float* amax_x, const void* w, sq_dtype wt, int64_t K, int64_t N,
+                                   int64_t ldw, float alpha, float* s, float* inv_s, float* amax_w, int8_t* wq,
+                                   float* w_scale, const void* x, sq_dtype xt, int64_t M, int64_t ldx,
+                                   sq_act_gran g, int8_t* xq, float* x_scale, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    const char* fn = "sq_prepare_and_quant_act";
+    // sq_quant_act's checks first, so that a rejection enqueues nothing on
+    // either path; sq_prepare_weights makes its own below
+    SQ_TRY(check_k(fn, K));
+    if (g != SQ_PER_TOKEN && g != SQ_PER_TENSOR) return fail(SQ_ERR_UNSUPPORTED, "%s: granularity %d", fn, (int)g);
+    if (M > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld too large", fn, (long long)M);
+    SQ_TRY(check_matrix(fn, "x", x, xt, M, K, ldx));
+    SQ_TRY(check_vec(fn, "inv_s", inv_s, K, true));
+    SQ_TRY(check_vec(fn, "x_scale", x_scale, g == SQ_PER_TENSOR ? (M > 0 ? 1 : 0) : M));
+    if (M > 0 && K > 0) {
+        if (!xq) return fail(SQ_ERR_INVALID_ARG, "%s: xq is NULL", fn);
+        if (!aligned16(xq)) return fail(SQ_ERR_INVALID_ARG, "%s: xq is not 16-byte aligned", fn);
+    }
+    const size_t need = sq_workspace_size(SQ_OP_PREPARE_AND_QUANT_ACT, M, N, K, g);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned16(ws)))
+        return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned) required, got %zu", fn, need,
+                    ws ? ws_bytes : (size_t)0);
+    const size_t wsp = round256(sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, M, N, K, g));
+    void* ws_a = ws && wsp < ws_bytes ? static_cast<void*>(static_cast<char*>(ws) + wsp) : nullptr;
+    const size_t ws_a_bytes = ws_bytes > wsp ? ws_bytes - wsp : 0;
+
+    const bool fast = M > 0 && K > 0 && N > 0 && wt == SQ_BF16 && xt == SQ_BF16 && g == SQ_PER_TOKEN &&
+                      sqk::prep_fused_supported(w, true, N, ldw, alpha);
+    if (!fast) {
+        SQ_TRY(sq_prepare_weights(amax_x, w, wt, K, N, ldw, alpha, s, inv_s, amax_w, wq, w_scale, ws, wsp, stream));
+        return sq_quant_act(x, xt, M, K, ldx, inv_s, g, xq, x_scale, ws_a, ws_a_bytes, stream);
+    }
+    // sq_prepare_weights' checks
+    if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(SQ_ERR_INVALID_ARG, "%s: alpha = %g is not in [0, 1]", fn, alpha);
+    if (N > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: N = %lld too large", fn, (long long)N);
+    SQ_TRY(check_vec(fn, "amax_x", amax_x, K));
+    SQ_TRY(check_vec(fn, "s", s, K));
+    if (amax_w) SQ_TRY(check_vec(fn, "amax_w", amax_w, K));
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
+    SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
+    if (!wq) return fail(SQ_ERR_INVALID_ARG, "%s: wq is NULL", fn);
+    if (!aligned16(wq)) return fail(SQ_ERR_INVALID_ARG, "%s: wq is not 16-byte aligned", fn);
+
+    uint32_t* colmax = static_cast<uint32_t*>(ws);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)N * sizeof(uint32_t)));
+    hipError_t e = sqk::launch_prepare_weights(w, true, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, partial, colmax,
+                                               stream);
+    if (e != hipSuccess) return hip_result(e, fn);
+    e = sqk::launch_codes_both(w, K, N, ldw, s, colmax, wq, w_scale, x, M, ldx, inv_s, xq, x_scale, stream);
+    if (e == hipErrorNotSupported) {  // K > 4096 or X rows not 16-byte aligned: the two code launches
+        e = sqk::launch_quant_weight(w, true, K, N, ldw, s, colmax, wq, w_scale, stream);
+        if (e == hipSuccess) e = sqk::launch_quant_act(x, true, M, K, ldx, inv_s, 0, xq, x_scale, nullptr, stream);
+    }
     return hip_result(e, fn);
 }
 

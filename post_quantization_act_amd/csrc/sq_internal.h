@@ -43,6 +43,13 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
 // Activation quantization.  mode 0: per token.  mode 1: max of |x * inv_s|
 // over the tensor into *gmax (no codes).  mode 2: codes with the scale from
 // *gmax (x_scale[0]).
+// Weight codes (as launch_quant_weight with s) and per-token activation codes
+// (as launch_quant_act mode 0 with inv_s) in one launch, for bf16 W and X with
+// 16-byte aligned rows and K <= 4096.  hipErrorNotSupported (nothing
+// enqueued) for other inputs.
+hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, const float* s, const uint32_t* colmax,
+                             int8_t* wq, float* w_scale, const void* x, int64_t M, int64_t ldx, const float* inv_s,
+                             int8_t* xq, float* x_scale, hipStream_t st);
 hipError_t launch_quant_act(const void* x, bool bf16, int64_t M, int64_t K, int64_t ld, const float* inv_s,
                             int mode, int8_t* xq, float* x_scale, uint32_t* gmax, hipStream_t st);
 

@@ -26,10 +26,10 @@ constexpr int kQwStride = kQwTile + 8;
 constexpr int kQwGroup = 16;
 
 template <typename T, bool kScaled, bool kVec>
-__global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t K, int64_t N, int64_t ld,
-                                                      const float* __restrict__ s,
-                                                      const uint32_t* __restrict__ colmax,
-                                                      int8_t* __restrict__ wq, float* __restrict__ w_scale) {
+__device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restrict__ w, int64_t K, int64_t N,
+                                                  int64_t ld, const float* __restrict__ s,
+                                                  const uint32_t* __restrict__ colmax, int8_t* __restrict__ wq,
+                                                  float* __restrict__ w_scale) {
     __shared__ float r_s[kQwTile];
     __shared__ __align__(16) uint8_t tile[kQwTile * kQwStride];
 
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, i
     // each row of W.
     const int64_t tj = (K + kQwTile - 1) / kQwTile;
     const int64_t per = (int64_t)kQwGroup * tj;
-    const int64_t grp = blockIdx.x / per, rem = blockIdx.x % per;
+    const int64_t grp = bid / per, rem = bid % per;
     const int64_t k0 = (grp * kQwGroup + rem / tj) * kQwTile;
     const int64_t j0 = (rem % tj) * kQwTile;
     const int t = threadIdx.x;
@@ -121,6 +121,14 @@ __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, i
             *reinterpret_cast<uint4*>(wq + k * K + j) = make_uint4(a.x, a.y, b.x, b.y);
         }
     }
+}
+
+template <typename T, bool kScaled, bool kVec>
+__global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t K, int64_t N, int64_t ld,
+                                                      const float* __restrict__ s,
+                                                      const uint32_t* __restrict__ colmax,
+                                                      int8_t* __restrict__ wq, float* __restrict__ w_scale) {
+    quant_weight_tile<T, kScaled, kVec>(blockIdx.x, w, K, N, ld, s, colmax, wq, w_scale);
 }
 
 // ---- activations -------------------------------------------------------------
@@ -230,10 +238,11 @@ __global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int6
 // flight while the current row is reduced (one barrier per row, LDS slots
 // alternating between rows) and coded.  Codes and scales as k_quant_act.
 template <int NV, bool kStatic>
-__global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restrict__ x, int64_t M, int64_t K,
-                                                          int64_t ld, const float* __restrict__ inv_s,
-                                                          int8_t* __restrict__ xq, float* __restrict__ x_scale,
-                                                          const uint32_t* __restrict__ gmax) {
+__device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk, const bf16_t* __restrict__ x,
+                                                     int64_t M, int64_t K, int64_t ld,
+                                                     const float* __restrict__ inv_s, int8_t* __restrict__ xq,
+                                                     float* __restrict__ x_scale,
+                                                     const uint32_t* __restrict__ gmax) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, t = threadIdx.x;
     const int64_t groups = K / 8;
     float is[NV][8];
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restri
     float scale = 0.0f, r = 0.0f;
     if constexpr (kStatic) {
         group_scale(__uint_as_float(*gmax), scale, r);
-        if (blockIdx.x == 0 && t == 0) x_scale[0] = scale;
+        if (bid == 0 && t == 0) x_scale[0] = scale;
     }
     __shared__ float red[2][4];
     uint4 cur[NV], nxt[NV];
@@ -264,10 +273,10 @@ __global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restri
             d[q] = (row < M && g < groups) ? ld16_stream(x + row * ld + g * 8) : make_uint4(0, 0, 0, 0);
         }
     };
-    int64_t row = blockIdx.x;
+    int64_t row = bid;
     load(row, cur);
-    for (int it = 0; row < M; ++it, row += gridDim.x) {
-        load(row + gridDim.x, nxt);
+    for (int it = 0; row < M; ++it, row += nblk) {
+        load(row + nblk, nxt);
         float v[NV][8];
         float m = 0.0f;
 #pragma unroll
@@ -310,6 +319,34 @@ __global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restri
 #pragma unroll
         for (int q = 0; q < NV; ++q) cur[q] = nxt[q];
     }
+}
+
+template <int NV, bool kStatic>
+__global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          int64_t ld, const float* __restrict__ inv_s,
+                                                          int8_t* __restrict__ xq, float* __restrict__ x_scale,
+                                                          const uint32_t* __restrict__ gmax) {
+    quant_act_stream_rows<NV, kStatic>(blockIdx.x, gridDim.x, x, M, K, ld, inv_s, xq, x_scale, gmax);
+}
+
+// Step 3's codes and step 4's per-token codes in one launch: both need only
+// s / inv_s and the column maxima, and each alone leaves the memory system
+// idle during its start and tail at attention-projection sizes.  Blocks
+// [0, tiles) code 128 x 128 weight tiles (bf16, 16-byte aligned rows), the
+// others walk token rows with the block count as their stride.
+template <int NV>
+__global__ __launch_bounds__(256) void k_codes_both(const bf16_t* __restrict__ w, int64_t K, int64_t N, int64_t ldw,
+                                                    const float* __restrict__ s,
+                                                    const uint32_t* __restrict__ colmax, int8_t* __restrict__ wq,
+                                                    float* __restrict__ w_scale, int64_t tiles,
+                                                    const bf16_t* __restrict__ x, int64_t M, int64_t ldx,
+                                                    const float* __restrict__ inv_s, int8_t* __restrict__ xq,
+                                                    float* __restrict__ x_scale) {
+    if ((int64_t)blockIdx.x < tiles)
+        quant_weight_tile<bf16_t, true, true>(blockIdx.x, w, K, N, ldw, s, colmax, wq, w_scale);
+    else
+        quant_act_stream_rows<NV, false>((int64_t)blockIdx.x - tiles, (int64_t)gridDim.x - tiles, x, M, K, ldx,
+                                         inv_s, xq, x_scale, nullptr);
 }
 
 // Rows longer than the register-resident variants hold (K > 16384): four
@@ -605,6 +642,32 @@ static void dispatch_act(const T* x, int64_t M, int64_t K, int64_t ld, const flo
     if (groups <= 8 * 4 * kWave) return launch_act_rows<T, 8, 4>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
     hipLaunchKernelGGL((k_quant_act_long<T>), dim3((unsigned)M), dim3(256), 0, st, x, M, K, ld, inv_s, mode, xq,
                        x_scale, gmax);
+}
+
+hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, const float* s, const uint32_t* colmax,
+                             int8_t* wq, float* w_scale, const void* x, int64_t M, int64_t ldx, const float* inv_s,
+                             int8_t* xq, float* x_scale, hipStream_t st) {
+    if (K <= 0 || N <= 0 || M <= 0 || !s || !inv_s) return hipErrorNotSupported;
+    const int64_t groups = K / 8;
+    if (K % 8 != 0 || groups > 2 * 256 || !rows_aligned16(w, ldw, 2) || !rows_aligned16(x, ldx, 2))
+        return hipErrorNotSupported;
+    const int64_t tiles = ((N + kQwTile - 1) / kQwTile) * ((K + kQwTile - 1) / kQwTile);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t rows = std::min<int64_t>(M, (int64_t)cus * act_stream_blocks_per_cu(2));
+    if (tiles + rows > 0x7FFFFFFF) return hipErrorNotSupported;
+    const dim3 grid((unsigned)(tiles + rows));
+    const bf16_t* wb = static_cast<const bf16_t*>(w);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    if (groups <= 256)
+        hipLaunchKernelGGL((k_codes_both<1>), grid, dim3(256), 0, st, wb, K, N, ldw, s, colmax, wq, w_scale, tiles, xb,
+                           M, ldx, inv_s, xq, x_scale);
+    else
+        hipLaunchKernelGGL((k_codes_both<2>), grid, dim3(256), 0, st, wb, K, N, ldw, s, colmax, wq, w_scale, tiles, xb,
+                           M, ldx, inv_s, xq, x_scale);
+    return hipGetLastError();
 }
 
 template <int NV, int WPR>

@@ -9,9 +9,10 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR, SQ_PER_TOKEN,
-               sq_calib_absmax, sq_gather_outliers, sq_gemm_w8a8, sq_gemm_w8a8_outlier, sq_outlier_columns,
-               sq_prepare_weights, sq_quant_act, sq_quant_weight, sq_smooth_factors, sq_workspace_size)
+from . import (SQ_OP_PREPARE_AND_QUANT_ACT, SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR,
+               SQ_PER_TOKEN, sq_calib_absmax, sq_gather_outliers, sq_gemm_w8a8, sq_gemm_w8a8_outlier,
+               sq_outlier_columns, sq_prepare_and_quant_act, sq_prepare_weights, sq_quant_act, sq_quant_weight,
+               sq_smooth_factors, sq_workspace_size)
 
 
 @dataclass
@@ -29,6 +30,7 @@ class W8A8Buffers:
     ws_w: torch.Tensor | None
     ws_a: torch.Tensor | None
     ws_p: torch.Tensor | None
+    ws_pa: torch.Tensor | None
 
     @classmethod
     def allocate(cls, M: int, N: int, K: int, gran: int, device, y_dtype=torch.bfloat16, with_acc=False):
@@ -47,6 +49,7 @@ class W8A8Buffers:
             ws_w=ws(sq_workspace_size(SQ_OP_QUANT_WEIGHT, M, N, K, gran)),
             ws_a=ws(sq_workspace_size(SQ_OP_QUANT_ACT, M, N, K, gran)),
             ws_p=ws(sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, M, N, K, gran)),
+            ws_pa=ws(sq_workspace_size(SQ_OP_PREPARE_AND_QUANT_ACT, M, N, K, gran)),
         )
 
 
@@ -79,13 +82,27 @@ def forward(x: torch.Tensor, gran: int, b: W8A8Buffers, smoothed: bool = True, s
     return b.y
 
 
+def prepare_and_quantize(x: torch.Tensor, w: torch.Tensor, alpha: float, gran: int, b: W8A8Buffers,
+                         stream=None) -> None:
+    """Steps 2-4 in one call (the weight codes and the activation codes may share a launch)."""
+    sq_prepare_and_quant_act(b.amax_x, w, alpha, b.s, b.inv_s, b.amax_w, b.wq, b.w_scale, x, gran, b.xq, b.x_scale,
+                             b.ws_pa, stream=stream)
+
+
 def smoothquant_w8a8(x, w, calib, alpha: float | None, gran: int, b: W8A8Buffers, stream=None,
                      fused: bool = True) -> torch.Tensor:
-    """All five steps.  alpha=None runs the unsmoothed W8A8 baseline (no calibration)."""
-    if alpha is not None:
-        calibrate(calib, b.amax_x, stream=stream)
-    prepare_weights(w, alpha, b, stream=stream, fused=fused)
-    return forward(x, gran, b, smoothed=alpha is not None, stream=stream)
+    """All five steps.  alpha=None runs the unsmoothed W8A8 baseline (no calibration).  fused: steps 2-4
+    through sq_prepare_and_quant_act; otherwise sq_smooth_factors, sq_quant_weight, sq_quant_act."""
+    if alpha is None:
+        prepare_weights(w, None, b, stream=stream)
+        return forward(x, gran, b, smoothed=False, stream=stream)
+    calibrate(calib, b.amax_x, stream=stream)
+    if fused:
+        prepare_and_quantize(x, w, alpha, gran, b, stream=stream)
+        sq_gemm_w8a8(b.xq, b.x_scale, gran, b.wq, b.w_scale, b.y, b.acc, stream=stream)
+        return b.y
+    prepare_weights(w, alpha, b, stream=stream, fused=False)
+    return forward(x, gran, b, smoothed=True, stream=stream)
 
 
 class CapturedPass:

@@ -71,6 +71,11 @@ def test_workspace_sizes():
     assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 100) >= 4096 * 4 + 100 * 4096 * 4
     assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 300) < 4096 * 4 + 256 * 4096 * 4  # 150 blocks
     assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 0, 4096) == 0
+    # prepare_and_quant_act: prepare_weights' workspace, then (256-byte aligned) quant_act's
+    for g in (sq.SQ_PER_TOKEN, sq.SQ_PER_TENSOR):
+        p = sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 2048, 4096, 4096, g)
+        a = sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, 2048, 4096, 4096, g)
+        assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_AND_QUANT_ACT, 2048, 4096, 4096, g) == (p + 255) // 256 * 256 + a
 
 
 FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
@@ -174,6 +179,37 @@ def test_prepare_weights_rejects():
     _expect(L.sq_prepare_weights(*args(K=33)), -1, "K = 33")
     _expect(L.sq_prepare_weights(*args(ws=None, wsb=0)), -3, "workspace")
     _expect(L.sq_prepare_weights(*args(wsb=64)), -3, "workspace")
+
+
+def test_prepare_and_quant_act_rejects():
+    """Every rejection comes before anything is enqueued (no GPU here)."""
+    L = _L()
+    f = ctypes.c_float
+
+    def args(**kw):
+        return [kw.get("amax_x", FAKE), kw.get("w", FAKE), kw.get("wt", sq.SQ_BF16), kw.get("K", 32), kw.get("N", 64),
+                kw.get("ldw", 64), f(kw.get("alpha", 0.5)), kw.get("s", FAKE), kw.get("inv_s", FAKE), None,
+                kw.get("wq", FAKE), FAKE, kw.get("x", FAKE), kw.get("xt", sq.SQ_BF16), kw.get("M", 8),
+                kw.get("ldx", 32), kw.get("g", sq.SQ_PER_TOKEN), kw.get("xq", FAKE), FAKE, kw.get("ws", FAKE),
+                kw.get("wsb", 1 << 20), None]
+
+    fn = L.sq_prepare_and_quant_act
+    _expect(fn(*args(alpha=1.5)), -1, "alpha")
+    _expect(fn(*args(K=33)), -1, "K = 33")
+    _expect(fn(*args(s=None)), -1, "s is NULL")
+    _expect(fn(*args(w=None)), -1, "w is NULL")
+    _expect(fn(*args(wq=MISALIGNED)), -1, "wq")
+    _expect(fn(*args(inv_s=MISALIGNED)), -1, "inv_s is not 16-byte aligned")
+    _expect(fn(*args(xq=MISALIGNED)), -1, "xq")
+    _expect(fn(*args(x=None)), -1, "x is NULL")
+    _expect(fn(*args(ldx=36)), -1, "row stride")
+    _expect(fn(*args(g=7)), -2, "granularity")
+    _expect(fn(*args(ws=None, wsb=0)), -3, "workspace")
+    # per tensor also needs quant_act's 256 bytes after prepare_weights' workspace
+    p = sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 8, 64, 32, sq.SQ_PER_TENSOR)
+    _expect(fn(*args(g=sq.SQ_PER_TENSOR, wsb=(p + 255) // 256 * 256)), -3, "workspace")
+    # the slow path (fp32 W) rejects with prepare_weights' own checks, also before any launch
+    _expect(fn(*args(wt=sq.SQ_F32, alpha=-0.5)), -1, "alpha")
 
 
 def test_static_scale_rejects():
