@@ -363,6 +363,64 @@ __global__ __launch_bounds__(256) void k_codes_both(const bf16_t* __restrict__ w
                                          inv_s, xq, x_scale, nullptr);
 }
 
+// The per-tensor maximum a = max_ij |fl(x_ij inv_s_j)| (the first of the two
+// passes of dynamic per-tensor step 4): blocks walk token rows with a grid
+// stride, two rows' loads in flight, each thread keeps the inv_s of its
+// channel groups in registers and one running maximum; one atomicMax per
+// block on the fp32 bit pattern (*gmax starts at 0).
+template <int NV>
+__global__ __launch_bounds__(256) void k_act_absmax_stream(const bf16_t* __restrict__ x, int64_t M, int64_t K,
+                                                           int64_t ld, const float* __restrict__ inv_s,
+                                                           uint32_t* __restrict__ gmax) {
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, t = threadIdx.x;
+    const int64_t groups = K / 8;
+    float is[NV][8];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+        const int64_t g = t + (int64_t)q * 256;
+        if (inv_s && g < groups) {
+            const float4 a = *reinterpret_cast<const float4*>(inv_s + g * 8);
+            const float4 b = *reinterpret_cast<const float4*>(inv_s + g * 8 + 4);
+            is[q][0] = a.x; is[q][1] = a.y; is[q][2] = a.z; is[q][3] = a.w;
+            is[q][4] = b.x; is[q][5] = b.y; is[q][6] = b.z; is[q][7] = b.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) is[q][i] = 1.0f;
+        }
+    }
+    float m = 0.0f;
+    const int64_t stride = gridDim.x;
+    for (int64_t row = blockIdx.x; row < M; row += 2 * stride) {
+        uint4 u[2][NV];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const int64_t rr = row + r * stride, g = t + (int64_t)q * 256;
+                u[r][q] = (rr < M && g < groups) ? ld16_stream(x + rr * ld + g * 8) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const uint32_t w[4] = {u[r][q].x, u[r][q].y, u[r][q].z, u[r][q].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    m = fmaxf(m, fabsf(bf16_lo(w[h]) * is[q][2 * h]));
+                    m = fmaxf(m, fabsf(bf16_hi(w[h]) * is[q][2 * h + 1]));
+                }
+            }
+    }
+    __shared__ float red[4];
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (t == 0) {
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        if (m > 0.0f) atomicMax(gmax, __float_as_uint(m));
+    }
+}
+
 // Rows longer than the register-resident variants hold (K > 16384): four
 // wavefronts per row loop over it twice, once for the max, once for codes
 // (the second pass re-reads the row, mostly from L2).
@@ -639,13 +697,37 @@ static void launch_act_stream(const bf16_t* x, int64_t M, int64_t K, int64_t ld,
     }
 }
 
+// Grid for the max pass: about four blocks per CU (the register footprint
+// allows it for every NV), each walking about M / grid rows.
+static void launch_act_absmax_stream(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* inv_s,
+                                     uint32_t* gmax, hipStream_t st) {
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    const int64_t grid = std::min<int64_t>(M, (int64_t)cus * 4);
+    const dim3 g((unsigned)grid);
+    switch ((K / 8 + 255) / 256) {
+        case 1: hipLaunchKernelGGL((k_act_absmax_stream<1>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 2: hipLaunchKernelGGL((k_act_absmax_stream<2>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 3: hipLaunchKernelGGL((k_act_absmax_stream<3>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 4: hipLaunchKernelGGL((k_act_absmax_stream<4>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 5: hipLaunchKernelGGL((k_act_absmax_stream<5>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 6: hipLaunchKernelGGL((k_act_absmax_stream<6>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 7: hipLaunchKernelGGL((k_act_absmax_stream<7>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        default: hipLaunchKernelGGL((k_act_absmax_stream<8>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+    }
+}
+
 template <typename T>
 static void dispatch_act(const T* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode, int8_t* xq,
                          float* x_scale, uint32_t* gmax, hipStream_t st) {
     const int64_t groups = K / 8;
     if constexpr (std::is_same<T, bf16_t>::value) {
-        if ((mode == 0 || mode == 2) && groups <= 8 * 256 && rows_aligned16(x, ld, 2))
+        if (groups <= 8 * 256 && rows_aligned16(x, ld, 2)) {
+            if (mode == 1) return launch_act_absmax_stream(x, M, K, ld, inv_s, gmax, st);
             return launch_act_stream(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
+        }
     }
     if (groups <= 1 * kWave) return launch_act_rows<T, 1, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
     if (groups <= 2 * kWave) return launch_act_rows<T, 2, 1>(x, M, K, ld, inv_s, mode, xq, x_scale, gmax, st);
