@@ -111,6 +111,14 @@ sq_status sq_calib_absmax(const void *x, sq_dtype xt, int64_t T, int64_t K, int6
                           float *amax, hipStream_t stream);
 
 /*
+ * Start of a calibration: amax[j] = 0 for j < K (K >= 0; amax may be NULL when
+ * K is 0).  One small kernel and no memset, so the call may be recorded in a
+ * HIP graph; the same as clearing amax any other way before the first
+ * sq_calib_absmax.
+ */
+sq_status sq_calib_reset(float *amax, int64_t K, hipStream_t stream);
+
+/*
  * Step 2 -- smoothing factors (page "大模型训练、适配与推理" section 3.5; page
  * "4.2 W8A8 量化与 SmoothQuant" section 4; W_j is row j of W, the row that
  * multiplies activation channel j).

@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
-    "lib", "lib_path", "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
+    "lib", "lib_path", "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
     "sq_gemm_w8a8", "sq_prepare_weights", "sq_prepare_and_quant_act", "SQ_OP_PREPARE_WEIGHTS",
     "SQ_OP_PREPARE_AND_QUANT_ACT", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
     "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier",
@@ -36,8 +36,8 @@ SQ_PER_TOKEN, SQ_PER_TENSOR = 0, 1
  SQ_OP_PREPARE_AND_QUANT_ACT) = range(7)
 
 EXPORTED_SYMBOLS = (
-    "sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights",
-    "sq_prepare_and_quant_act", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
+    "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
+    "sq_prepare_weights", "sq_prepare_and_quant_act", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
     "sq_gather_outliers", "sq_gemm_w8a8_outlier", "sq_workspace_size", "sq_status_str", "sq_last_error",
     "sq_version", "sq_gemm_kernel_name", "sq_gemm_outlier_kernel_name",
 )
@@ -67,6 +67,7 @@ def lib() -> ctypes.CDLL:
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sz = ctypes.c_size_t
     L.sq_calib_absmax.argtypes = [vp, i32, i64, i64, i64, vp, vp]
+    L.sq_calib_reset.argtypes = [vp, i64, vp]
     L.sq_smooth_factors.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp]
     L.sq_quant_weight.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, sz, vp]
     L.sq_quant_act.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
@@ -192,6 +193,13 @@ def sq_calib_absmax(x: torch.Tensor, amax: torch.Tensor, stream=None) -> None:
     T, K, ld = _rows(x)
     _dense(amax, "amax", (K,), torch.float32)
     _check(lib().sq_calib_absmax(_ptr(x), _dtype(x), T, K, ld, _ptr(amax), _stream(_dev(x, amax), stream)))
+
+
+def sq_calib_reset(amax: torch.Tensor, stream=None) -> None:
+    """amax[:] = 0, the start of a calibration (a library kernel, safe to record in a HIP graph)."""
+    K = amax.shape[0]
+    _dense(amax, "amax", (K,), torch.float32)
+    _check(lib().sq_calib_reset(_ptr(amax), K, _stream(_dev(amax), stream)))
 
 
 def sq_smooth_factors(amax_x: torch.Tensor, w: torch.Tensor | None, alpha: float, s: torch.Tensor,

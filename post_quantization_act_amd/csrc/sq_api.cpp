@@ -138,6 +138,15 @@ sq_status sq_calib_absmax(const void* x, sq_dtype xt, int64_t T, int64_t K, int6
                                              reinterpret_cast<uint32_t*>(amax), stream), fn);
 }
 
+sq_status sq_calib_reset(float* amax, int64_t K, hipStream_t stream) {
+    const char* fn = "sq_calib_reset";
+    if (K < 0) return fail(SQ_ERR_INVALID_ARG, "%s: K = %lld is negative", fn, (long long)K);
+    if (K > kMaxMN) return fail(SQ_ERR_INVALID_ARG, "%s: K = %lld too large", fn, (long long)K);
+    SQ_TRY(check_vec(fn, "amax", amax, K));
+    if (K == 0) return ok();
+    return hip_result(sqk::launch_fill_u32(reinterpret_cast<uint32_t*>(amax), K, 0u, stream), fn);
+}
+
 sq_status sq_smooth_factors(const float* amax_x, const void* w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
                             float alpha, float* s, float* inv_s, float* amax_w, hipStream_t stream) {
     const char* fn = "sq_smooth_factors";

@@ -12,7 +12,7 @@ import torch
 from . import (SQ_OP_PREPARE_AND_QUANT_ACT, SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR,
                SQ_PER_TOKEN, sq_calib_absmax, sq_gather_outliers, sq_gemm_w8a8, sq_gemm_w8a8_outlier,
                sq_outlier_columns, sq_prepare_and_quant_act, sq_prepare_weights, sq_quant_act, sq_quant_weight,
-               sq_smooth_factors, sq_workspace_size)
+               sq_calib_reset, sq_smooth_factors, sq_workspace_size)
 
 
 @dataclass
@@ -56,7 +56,7 @@ class W8A8Buffers:
 def calibrate(calib, amax_x: torch.Tensor, reset: bool = True, stream=None) -> None:
     """Step 1 over one [T, K] tensor or a sequence of chunks."""
     if reset:
-        amax_x.zero_()
+        sq_calib_reset(amax_x, stream=stream)
     chunks = calib if isinstance(calib, (list, tuple)) else [calib]
     for c in chunks:
         sq_calib_absmax(c, amax_x, stream=stream)
@@ -109,9 +109,9 @@ class CapturedPass:
     """All five calls recorded once into a HIP graph over fixed tensors (x, w,
     calib and the buffers in b), then replayed with a single launch.
 
-    The library enqueues only kernels (its buffer clears are fill kernels, and
-    so is torch's zero_ of the running maximum), so the recorded graph holds
-    no memset nodes.  Inputs are read where they lie at replay time: write new
+    The library enqueues only kernels (its buffer clears, the clear of the
+    running maximum included, are fill kernels), so the recorded graph holds no
+    memset nodes.  Inputs are read where they lie at replay time: write new
     data into the same tensors between replays."""
 
     def __init__(self, x, w, calib, alpha: float | None, gran: int, b: W8A8Buffers, warmup: int = 1):

@@ -91,6 +91,14 @@ def _expect(rc, status, pattern):
     assert re.search(pattern, sq.sq_last_error()), sq.sq_last_error()
 
 
+def test_calib_reset_rejects():
+    L = _L()
+    _expect(L.sq_calib_reset(FAKE, -1, None), -1, "negative")
+    _expect(L.sq_calib_reset(None, 16, None), -1, "amax is NULL")
+    _expect(L.sq_calib_reset(ctypes.c_void_p(0x10002), 16, None), -1, "4-byte aligned")
+    assert L.sq_calib_reset(None, 0, None) == 0  # nothing to clear, nothing enqueued
+
+
 def test_calib_rejects_bad_k_and_null():
     L = _L()
     _expect(L.sq_calib_absmax(FAKE, sq.SQ_BF16, 8, 20, 20, FAKE, None), -1, "multiple of 16")

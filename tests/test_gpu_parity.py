@@ -219,6 +219,15 @@ def test_calibration_chunks_and_resume():
     sq.sq_calib_absmax(ct, a1)  # idempotent
     torch.cuda.synchronize()
     np.testing.assert_array_equal(_np(a1), _np(a2))
+    # sq_calib_reset starts a new calibration: a larger earlier maximum is gone
+    a2.fill_(1e30)
+    sq.sq_calib_reset(a2)
+    sq.sq_calib_absmax(ct, a2)
+    odd = torch.full((1000 + 16,), 7.0, device=DEV)  # a length that is no multiple of the fill block
+    sq.sq_calib_reset(odd[:1000])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(a2), _np(a1))
+    assert not odd[:1000].any() and bool((odd[1000:] == 7.0).all())
 
 
 def test_strided_inputs():
