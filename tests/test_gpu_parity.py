@@ -380,3 +380,40 @@ def test_prepare_weights_without_amax_w_and_empty():
     sq.sq_prepare_weights(e, w0, 0.5, e, e, None, torch.empty(8, 0, dtype=torch.int8, device=DEV), wsc, None)
     torch.cuda.synchronize()
     assert torch.equal(wsc, torch.zeros(8, **f32))
+
+
+@pytest.mark.parametrize("M,N", [(256, 256), (8, 64), (300, 130)])
+def test_gemm_largest_k_extremes(M, N):
+    """K = 131072, the largest the library takes: with every code at +-127 the
+    int32 accumulators reach +-K 127^2 = +-2114060288, just below 2^31, and must
+    come out exact (ring, decode and ragged tiles); random codes at the same K
+    pass Freivalds' check."""
+    K = 131072
+    _say(f"gemm K={K} M={M} N={N}: kernel {sq.sq_gemm_kernel_name(M, N, K)}")
+    xq = torch.full((M, K), 127, dtype=torch.int8, device=DEV)
+    sign = torch.where(torch.arange(N, device=DEV) % 2 == 0, 1, -1).to(torch.int8)
+    wq = (torch.full((N, K), 127, dtype=torch.int8, device=DEV) * sign[:, None]).contiguous()
+    xs = torch.full((M,), 1.0 / 127, device=DEV)
+    ws = torch.full((N,), 2.0 ** -20, device=DEV)
+    y = torch.empty(M, N, dtype=torch.float32, device=DEV)
+    acc = torch.empty(M, N, dtype=torch.int32, device=DEV)
+    sq.sq_gemm_w8a8(xq, xs, sq.SQ_PER_TOKEN, wq, ws, y, acc)
+    torch.cuda.synchronize()
+    peak = K * 127 * 127
+    assert peak < 2 ** 31
+    want = np.where(np.arange(N) % 2 == 0, peak, -peak).astype(np.int64)
+    np.testing.assert_array_equal(_np(acc).astype(np.int64), np.broadcast_to(want, (M, N)))
+    y_o, _ = oracle.dequant(_np(acc), _np(xs), oracle.PER_TOKEN, _np(ws))
+    np.testing.assert_array_equal(_np(y), y_o)
+    # random codes: acc . r == Xq . (Wq^T r) in int64
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + N)
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=DEV, generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=DEV, generator=g)
+    sq.sq_gemm_w8a8(xq, xs, sq.SQ_PER_TOKEN, wq, ws, y, acc)
+    torch.cuda.synchronize()
+    A, B, C = _np(xq).astype(np.int64), _np(wq).astype(np.int64), _np(acc).astype(np.int64)
+    rng = np.random.default_rng(N)
+    for _ in range(2):
+        r = rng.choice(np.array([-1, 1], dtype=np.int64), size=N)
+        np.testing.assert_array_equal(C @ r, A @ (B.T @ r))
