@@ -28,6 +28,8 @@
 // XCD walks a contiguous run of a grouped (m-major within groups of 8 tile
 // rows) raster and concurrent blocks on one XCD share operand panels in its L2.
 #include <algorithm>
+#include <climits>
+#include <cstdint>
 #include <type_traits>
 
 #include "sq_device.h"
@@ -130,8 +132,9 @@ __device__ __forceinline__ void outlier_blocks(const OutlierOps& op, int n16, in
 template <int TN, int TM, int kOut, bool kAcc, bool kO = false>
 __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
                                          const float* __restrict__ x_scale, int xs_step,
-                                         const float* __restrict__ w_scale, int M, int N, void* __restrict__ y,
-                                         int32_t* __restrict__ acc_out, const OutlierOps& op = OutlierOps{}) {
+                                         const float* __restrict__ w_scale, int M, int N, int ldy,
+                                         void* __restrict__ y, int32_t* __restrict__ acc_out,
+                                         const OutlierOps& op = OutlierOps{}) {
     const int fr = lane % 32, fh = lane / 32;
     constexpr bool n_vec = kOut < 2;
     constexpr int kTy = kOut & 1;
@@ -169,7 +172,7 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
                         y2 += o[4 * g + 2];
                         y3 += o[4 * g + 3];
                     }
-                    const int64_t off = (int64_t)m * N + n;
+                    const int64_t off = (int64_t)m * ldy + n;
                     if constexpr (kTy == 0) {
                         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + off) =
                             make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
@@ -183,7 +186,7 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
                         if (n + e >= N) break;
                         float v = ((float)av[e] * xs) * w_scale[n + e];
                         if constexpr (kO) v += o[4 * g + e];
-                        const int64_t off = (int64_t)m * N + n + e;
+                        const int64_t off = (int64_t)m * ldy + n + e;
                         if constexpr (kTy == 0) {
                             static_cast<uint16_t*>(y)[off] = (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
                         } else {
@@ -208,7 +211,7 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
 // sx, sw: the wavefront's token and weight scales, staged in LDS.
 template <int TN, int TM>
 __device__ __forceinline__ void epilogue_bf16_lds(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
-                                                  const float* sx, const float* sw, int M, int N,
+                                                  const float* sx, const float* sw, int M, int N, int ldy,
                                                   uint16_t* __restrict__ y, uint16_t* ldsw) {
     constexpr int WN = TN * 32, RS = WN + 8, CH = WN / 8;
     static_assert((32 * CH) % 64 == 0, "copy-out chunks");
@@ -237,7 +240,7 @@ __device__ __forceinline__ void epilogue_bf16_lds(const v16i (&acc)[TN][TM], int
             const int ml = c / CH, nc = c % CH;
             const int mm = mbase + b * 32 + ml, n = nbase + nc * 8;
             const uint4 v = *reinterpret_cast<const uint4*>(ldsw + ml * RS + nc * 8);
-            if (mm < M && n < N) *reinterpret_cast<uint4*>(y + (int64_t)mm * N + n) = v;
+            if (mm < M && n < N) *reinterpret_cast<uint4*>(y + (int64_t)mm * ldy + n) = v;
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next group reuses the region
     }
@@ -279,8 +282,8 @@ template <int BN, int BM, int WGN, int WGM, int NS, int kOut, bool kAcc, bool kO
 __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
                                                    int xs_step, const int8_t* __restrict__ wq,
                                                    const float* __restrict__ w_scale, int M, int N, int K,
-                                                   void* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
-                                                   int tiles_m, int group_m, OutlierOps op) {
+                                                   void* __restrict__ y, int ldy, int32_t* __restrict__ acc_out,
+                                                   int tiles_n, int tiles_m, int group_m, OutlierOps op) {
     constexpr int NW = WGN * WGM;             // wavefronts per block
     constexpr int WN = BN / WGN, WM = BM / WGM, TN = WN / 32, TM = WM / 32;
     constexpr int ROWS = BN + BM;             // rows of a stage: Wq tile rows, then Xq tile rows
@@ -435,15 +438,15 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
     }
     if constexpr (kLdsEpi) {
         static_assert(NW * 32 * (WN + 8) * 2 <= NS * STAGE * 16, "LDS for the bf16 epilogue");
-        if (N % 8 == 0) {
+        if (N % 8 == 0 && ldy % 8 == 0) {
             lds_barrier();  // every wavefront is done reading the ring
             uint16_t* ldsw = reinterpret_cast<uint16_t*>(lds) + wave * 32 * (WN + 8);
             epilogue_bf16_lds<TN, TM>(acc, n0 + wn * WN, m0 + wm * WM, lane, scl + BN + wm * WM, scl + wn * WN, M,
-                                      N, static_cast<uint16_t*>(y), ldsw);
+                                      N, ldy, static_cast<uint16_t*>(y), ldsw);
             return;
         }
     }
-    epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
+    epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, ldy, y,
                                      acc_out, op);
 }
 
@@ -453,7 +456,7 @@ template <int BN, int BM, int kOut, bool kAcc, bool kO>
 __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__ xq, const float* __restrict__ x_scale,
                                                       int xs_step, const int8_t* __restrict__ wq,
                                                       const float* __restrict__ w_scale, int M, int N, int K,
-                                                      void* __restrict__ y, int32_t* __restrict__ acc_out,
+                                                      void* __restrict__ y, int ldy, int32_t* __restrict__ acc_out,
                                                       int tiles_n, int tiles_m, int group_m, OutlierOps op) {
     constexpr int WN = BN / 2, WM = BM / 2;
     constexpr int TN = WN / 32, TM = WM / 32;
@@ -577,7 +580,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const int8_t* __restrict__
             rfrag(cur ^ 1, 0, 0);
         }
     }
-    epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, y,
+    epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, ldy, y,
                                      acc_out, op);
 }
 
@@ -910,10 +913,10 @@ static void launch_decode(const int8_t* xq, const float* x_scale, bool per_tenso
 // (0 bf16, 1 fp32, +2 when N % 4 != 0), the int32 accumulator store and the
 // 16-bit outlier addend (built without the accumulator store).
 template <typename Go>
-static void dispatch_variant(bool y_bf16, int N, bool acc, bool outl, Go&& go) {
+static void dispatch_variant(bool y_bf16, int N, int ldy, bool acc, bool outl, Go&& go) {
     using T_ = std::true_type;
     using F_ = std::false_type;
-    const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 ? 0 : 2);
+    const int out = (y_bf16 ? 0 : 1) + (N % 4 == 0 && ldy % 4 == 0 ? 0 : 2);
     auto by_out = [&](auto a, auto o) {
         switch (out) {
             case 0: go(std::integral_constant<int, 0>{}, a, o); break;
@@ -935,33 +938,54 @@ static void launch_generic(const int8_t* xq, const float* x_scale, bool per_tens
     const dim3 grid((unsigned)(tiles_n * tiles_m));
     const int step = per_tensor ? 0 : 1;  // x_scale index step
     const OutlierOps ops = op ? *op : OutlierOps{};
-    dispatch_variant(y_bf16, N, acc_out != nullptr, op != nullptr, [&](auto out_c, auto acc_c, auto o_c) {
+    dispatch_variant(y_bf16, N, N, acc_out != nullptr, op != nullptr, [&](auto out_c, auto acc_c, auto o_c) {
         hipLaunchKernelGGL((k_gemm_generic<BN, BM, decltype(out_c)::value, decltype(acc_c)::value,
                                            decltype(o_c)::value>),
-                           grid, dim3(256), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out, tiles_n,
+                           grid, dim3(256), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, N, acc_out, tiles_n,
                            tiles_m, group_m, ops);
     });
 }
 
+// Columns [n0, n0 + N) of the product (wq, w_scale, the outlier rows and the
+// output start at column n0; ldy is the output's row stride).
 template <int BN, int BM, int WGN, int WGM, int NS>
 static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
                         const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
-                        const OutlierOps* op, int group_m, hipStream_t st) {
+                        const OutlierOps* op, int group_m, hipStream_t st, int n0 = 0, int ldy = -1) {
+    if (ldy < 0) ldy = N;
     const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
     const dim3 grid((unsigned)(tiles_n * tiles_m));
     const int step = per_tensor ? 0 : 1;
-    const OutlierOps ops = op ? *op : OutlierOps{};
-    dispatch_variant(y_bf16, N, acc_out != nullptr, op != nullptr, [&](auto out_c, auto acc_c, auto o_c) {
+    OutlierOps ops = op ? *op : OutlierOps{};
+    if (op) ops.w_ot += (int64_t)n0 * ops.kp;
+    void* yc = static_cast<char*>(y) + (int64_t)n0 * (y_bf16 ? 2 : 4);
+    int32_t* accc = acc_out ? acc_out + n0 : nullptr;
+    dispatch_variant(y_bf16, N, ldy, acc_out != nullptr, op != nullptr, [&](auto out_c, auto acc_c, auto o_c) {
         hipLaunchKernelGGL((k_gemm_ring<BN, BM, WGN, WGM, NS, decltype(out_c)::value, decltype(acc_c)::value,
                                         decltype(o_c)::value>),
-                           grid, dim3(64 * WGN * WGM), 0, st, xq, x_scale, step, wq, w_scale, M, N, K, y, acc_out,
-                           tiles_n, tiles_m, group_m, ops);
+                           grid, dim3(64 * WGN * WGM), 0, st, xq, x_scale, step, wq + (int64_t)n0 * K,
+                           w_scale + n0, M, N, K, yc, ldy, accc, tiles_n, tiles_m, group_m, ops);
     });
 }
 
 // Which kernel a product of this shape runs (the one rule both the launcher
 // and gemm_kernel_name use).
-enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing256x128, kRing128, kGeneric };
+enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing256Split, kRing256x128, kRing128, kGeneric };
+
+// When the last round of 256 x 256 tiles over the CUs is at most half full,
+// the columns split: the first n1 columns hold whole rounds of 256 x 256
+// tiles, the rest run as one more launch of 256 x 128 tiles that fills at
+// most one round.  Returns n1 (a multiple of 256), or 0 when no such split
+// exists.
+static int64_t ring256_split_cols(int64_t M, int64_t N, int64_t cus) {
+    const int64_t tm = (M + 255) / 256, tn = (N + 255) / 256;
+    const int64_t tiles = tm * tn, full = tiles / cus, rest = tiles - full * cus;
+    if (full == 0 || rest == 0 || 2 * rest > cus || (full * cus) % tm != 0) return 0;
+    const int64_t tn1 = full * cus / tm;
+    if (tn1 >= tn) return 0;
+    const int64_t tail = ((N - tn1 * 256 + 255) / 256) * ((M + 127) / 128);
+    return tail <= cus ? tn1 * 256 : 0;
+}
 
 static GemmPath gemm_path(int64_t M, int64_t N, int64_t K, bool outl = false) {
     if (M <= 0 || N <= 0) return GemmPath::kNone;
@@ -982,7 +1006,10 @@ static GemmPath gemm_path(int64_t M, int64_t N, int64_t K, bool outl = false) {
     const int64_t c256 = 8 * ((t256 + cus - 1) / cus);
     const int64_t c_wide = 5 * ((t_wide + cus - 1) / cus);
     const int64_t c128 = 6 * ((t128 + 2 * cus - 1) / (2 * cus));
-    if (c256 <= c_wide && c256 <= c128) return GemmPath::kRing256;
+    const int64_t split = ring256_split_cols(M, N, cus);
+    const int64_t c_split = split > 0 ? 8 * (t256 / cus) + 5 : INT64_MAX;
+    if (c256 <= c_wide && c256 <= c128 && c256 <= c_split) return GemmPath::kRing256;
+    if (c_split <= c_wide && c_split <= c128) return GemmPath::kRing256Split;
     if (c_wide <= c128) return GemmPath::kRing256x128;
     return GemmPath::kRing128;
 }
@@ -993,6 +1020,9 @@ const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl) {
             return "k_gemm_decode_ring (one block of 16 wavefronts per CU, per-wavefront LDS rings of 128-byte stages)";
         case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
         case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2,2> (256x256 tile, 8 wavefronts of 64x128, 2 stages)";
+        case GemmPath::kRing256Split:
+            return "k_gemm_ring<256,256,4,2,2> on whole rounds of columns + k_gemm_ring<256,128,2,4,3> on the "
+                   "remaining columns (one round)";
         case GemmPath::kRing256x128:
             return "k_gemm_ring<256,128,2,4,3> (256x128 tile, 8 wavefronts of 128x32, 3 stages)";
         case GemmPath::kRing128: return "k_gemm_ring<128,128,2,4,2> (128x128 tile, 8 wavefronts of 64x32, 2 stages)";
@@ -1017,6 +1047,14 @@ static hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool per_t
             launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 4,
                                            st);
             break;
+        case GemmPath::kRing256Split: {
+            const int n1 = (int)ring256_split_cols(M64, N64, device_cu_count());
+            launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, n1, K, y, y_bf16, acc_out, op, 4,
+                                           st, 0, N);
+            launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N - n1, K, y, y_bf16, acc_out, op,
+                                           8, st, n1, N);
+            break;
+        }
         case GemmPath::kRing256x128:
             launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8,
                                            st);

@@ -57,6 +57,10 @@ def test_gemm_kernel_choice():
     assert sq.sq_gemm_kernel_name(3072, 4096, 4096).startswith("k_gemm_ring<256,256")   # 192 tiles, 1 round
     assert sq.sq_gemm_kernel_name(8192, 49152, 12288).startswith("k_gemm_ring<256,256")
     assert sq.sq_gemm_kernel_name(300, 520, 1040).startswith("k_gemm_generic")
+    # 896 tiles of 256 x 256 (3.5 rounds): 3 rounds of them, then the last 2048 columns as 256 x 128 tiles
+    assert "whole rounds" in sq.sq_gemm_kernel_name(4096, 14336, 4096)
+    assert "whole rounds" in sq.sq_gemm_kernel_name(256, 66536, 128)
+    assert "whole rounds" not in sq.sq_gemm_kernel_name(8192, 49152, 12288)  # 24 whole rounds
     assert sq.sq_gemm_kernel_name(0, 5, 16).startswith("none")
 
 

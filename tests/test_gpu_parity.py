@@ -103,6 +103,10 @@ CASES = [
     (12, 6144, 8200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     # K a multiple of 16 but not of 128: register-staged GEMM path with a K tail
     (300, 1040, 520, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 300),
+    # 260 tiles of 256 x 256: one whole round on the first 65536 columns, the last 1000 as 256 x 128 tiles
+    (256, 128, 66536, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
+    # the same split with N % 4 != 0 (element-wise stores in both launches)
+    (256, 128, 66538, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
 ]
 
 
