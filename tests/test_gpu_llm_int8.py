@@ -107,6 +107,7 @@ def _outlier_data(M, K, N, n_out, seed, fac=100.0):
     (513, 2048, 1000, 20, True),   # ring 256x128 tiles, ragged
     (12, 2048, 4096, 20, True),    # M <= 16: general kernel for the outlier variant
     (64, 256, 64, 40, True),       # 40 outliers: three 16-channel steps
+    (256, 128, 66536, 5, True),    # 260 tiles of 256 x 256: one whole round + the last columns as 256 x 128
 ])
 def test_llm_int8_matches_oracle(M, K, N, n_out, out_bf16):
     print(f"llm_int8 M={M} K={K} N={N} n_out={n_out} bf16={out_bf16} "
