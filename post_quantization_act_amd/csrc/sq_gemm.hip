@@ -689,9 +689,11 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
 // ---- decode kernel, LDS-ring variant (K % 2048 == 0, K <= 16384) ------------------
 //
 // Same product as k_gemm_decode, streamed so that every load instruction reads
-// whole 128-byte lines: one block of 16 wavefronts per CU; wavefront w owns the
-// k-bytes [w K/16, (w+1) K/16), i.e. SPW stages of 128 bytes, and keeps the
-// token operand of that range in registers for the whole kernel.  Work items
+// whole 128-byte lines: one block of 16 wavefronts per CU; wavefront w owns
+// the SPW = K / 2048 chunks of 128 k-bytes that start at byte 2048 sp + 128 w,
+// sp < SPW (so at stage sp the 16 wavefronts read one contiguous 2 KB of every
+// row of the group), and keeps the token operand of those chunks in registers
+// for the whole kernel.  Work items
 // are groups of 16 output channels, dealt round-robin to the blocks.  A stage
 // is 16 weight rows x 128 bytes, copied by two global_load_lds_dwordx4 (8 rows
 // x 128 bytes each, nontemporal: the stream is read once) into the
@@ -732,17 +734,19 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int G = (N + 15) / 16;
     const int ngroups = (G - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int kw = wave * (K / NW);
+    // k-chunks of this wavefront: stage sp covers bytes sp * NW * SB + wave * SB .. + SB of the rows, so
+    // at each stage the 16 wavefronts read one contiguous NW * SB bytes of every row of the group
+    auto kofs = [&](int sp) { return sp * (NW * SB) + wave * SB; };
 
     // token operand: lane l holds token l % 16, 16-byte chunk l / 16 of each 64-byte k-step
     v4i xb[SPW][KS];
     {
-        const int8_t* xr = xq + (int64_t)min(lane % 16, M - 1) * K + kw + 16 * (lane / 16);
+        const int8_t* xr = xq + (int64_t)min(lane % 16, M - 1) * K + 16 * (lane / 16);
 #pragma unroll
         for (int sp = 0; sp < SPW; ++sp)
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const uint4 u = ld16(xr + sp * SB + s * 64);
+                const uint4 u = ld16(xr + kofs(sp) + s * 64);
                 xb[sp][s] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
             }
         // consume them here so the compiler's own waits for these loads come
@@ -769,7 +773,7 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
         for (int i = 0; i < NCP; ++i) {
             const int r = RPC * i + rr;
             const int n = min(16 * g + r, N - 1);
-            const uint32_t off = (uint32_t)n * (uint32_t)K + (uint32_t)(kw + sp * SB + 16 * (cl ^ h(r)));
+            const uint32_t off = (uint32_t)n * (uint32_t)K + (uint32_t)(kofs(sp) + 16 * (cl ^ h(r)));
             copy16_to_lds_nt(wq, off, la + i * 1024);
         }
     };
