@@ -122,3 +122,16 @@ def test_pipeline_fused_equals_unfused():
         torch.cuda.synchronize()
         ys.append(b.y.view(torch.int16).clone())
     assert torch.equal(ys[0], ys[1])
+
+
+def test_combined_weight_rows_not_aligned():
+    """W as a view with an odd row stride (rows not 16-byte aligned) takes the two calls."""
+    M, K, N = 64, 256, 200
+    x, w, amax = _inputs(M, K, N, torch.bfloat16, torch.bfloat16, 5)
+    wide = torch.zeros(K, N + 3, dtype=torch.bfloat16, device=DEV)
+    wide[:, :N] = w
+    wv = wide[:, :N]
+    assert wv.stride(0) == N + 3
+    a, b = _both(x, wv, amax, 0.5, sq.SQ_PER_TOKEN)
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
