@@ -695,3 +695,24 @@ def test_llm_int8_keeps_accuracy_on_outlier_data(cfg):
         oracle.w8a8_linear(x, w, 0.5, oracle.PER_TOKEN, calib=synth.to_numpy(inp.calib))["y32"], Y)
     assert e_mixed < 0.2 * e_plain
     assert e_mixed < 2.0 * e_smooth
+
+
+def test_explainer_demo_shape_smoke():
+    """The explainer page "SmoothQuant大模型平滑量化技术" demonstrates the method on 4 channels x 8
+    tokens of N(3, 1) activations with one value of 200 and N(1, 0.3) weights, at alpha = 0.5, and
+    prints no numbers: a smoke check only (parity unpinned).  Token-major here: X [8 tokens, 4
+    channels], W [4 channels, 4 outputs].  Smoothing brings the activation maximum far below 200,
+    the outlier channel gets the largest factor, and the per-tensor W8A8 product error drops."""
+    rng = np.random.default_rng(42)
+    X = rng.normal(3.0, 1.0, (8, 4)).astype(np.float32)
+    X[3, 2] = 200.0
+    W = rng.normal(1.0, 0.3, (4, 4)).astype(np.float32)
+    ax = oracle.calib_absmax(X)
+    s, inv_s = oracle.smooth_factors(ax, oracle.weight_rowmax(W), 0.5)
+    assert int(np.argmax(s)) == 2
+    Xs = X * inv_s[None, :]
+    assert np.abs(Xs).max() < 200.0 / 4
+    y = oracle.matmul_f64(X, W)
+    plain = oracle.rel_fro(oracle.w8a8_linear(X, W, None, oracle.PER_TENSOR)["y32"], y)
+    smooth = oracle.rel_fro(oracle.w8a8_linear(X, W, 0.5, oracle.PER_TENSOR, calib=X)["y32"], y)
+    assert smooth < plain
