@@ -153,8 +153,9 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // ---- steps 2 + 3a fused: one read of W gives amax_w, s, inv_s and the
 // column maxima of diag(s) W ------------------------------------------------
 //
-// A block of NT threads (512, or 1024 for the widest exact-alpha rows)
-// streams the rows [r0, r1) of W (bf16, 16-byte aligned rows, N % 8 == 0).
+// A block of NT threads (1024 for exact alpha on rows of more than 256
+// 8-column groups, else 512) streams the rows [r0, r1) of W (bf16, 16-byte
+// aligned rows, N % 8 == 0).
 // Each iteration takes RB rows: row slot t / TPR (TPR = NT / RB threads per
 // row); thread t % TPR of a slot owns the 8-column groups q = t % TPR + TPR i,
 // i < GPT, and keeps their running column maxima in registers (GR groups) or
@@ -164,9 +165,9 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // row's loads are issued at the top of the iteration and stay in flight
 // through the reduction, the factor and the update; the barrier waits on LDS
 // only, and nothing else touches global memory in the loop: amax_x is staged
-// in LDS before, the per-row results are written after it.  The block's column maxima (its RB slots combined through LDS)
-// leave as plain stores to partial[blockIdx.x][N]; k_colmax_reduce takes the
-// maximum over blocks.
+// in LDS before, the per-row results are written after it.  The block's
+// column maxima (its RB slots combined through LDS) leave as plain stores to
+// partial[blockIdx.x][N]; k_colmax_reduce takes the maximum over blocks.
 constexpr int kPrepThreads = 512;
 constexpr int kPrepMaxRows = 256;  // rows per block (LDS staging of per-row values)
 
@@ -481,13 +482,15 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
         else if (groups <= 3072) SQ_PREP(1, 6, 0, true);
         else SQ_PREP(1, 8, 0, true);
     } else {
+        // beyond 256 groups: 1024 threads (16 wavefronts per CU stream the
+        // rows 3-8 % faster than 8), half the groups per thread
         if (groups <= 128) SQ_PREP(4, 1, 0, false);
         else if (groups <= 256) SQ_PREP(4, 2, 0, false);
-        else if (groups <= 512) SQ_PREP(4, 4, 0, false);
-        else if (groups <= 1024) SQ_PREP(4, 8, 0, false);
-        else if (groups <= 2048) SQ_PREP(2, 8, 0, false);
-        else if (groups <= 3072) SQ_PREP(1, 6, 0, false);
-        else if (groups <= 4096) SQ_PREP(1, 8, 0, false);
+        else if (groups <= 512) SQ_PREP_NT(4, 2, 0, false, 1024);
+        else if (groups <= 1024) SQ_PREP_NT(4, 4, 0, false, 1024);
+        else if (groups <= 2048) SQ_PREP_NT(2, 4, 0, false, 1024);
+        else if (groups <= 3072) SQ_PREP_NT(1, 3, 0, false, 1024);
+        else if (groups <= 4096) SQ_PREP_NT(1, 4, 0, false, 1024);
         else SQ_PREP_NT(1, 5, 1, false, 1024);  // up to 6144 groups: 5 in registers, 1 in LDS
     }
 #undef SQ_PREP

@@ -308,6 +308,10 @@ PREP_CASES = [
     (5472, 24600, 0.5, torch.bfloat16),   # 3075 groups: eight per thread, the last ones partly masked
     (4096, 32768, 0.6, torch.bfloat16),   # eight groups, general alpha
     (2736, 49152, 0.5, torch.bfloat16),   # 1024 threads, six groups: 5 in registers, 1 in LDS
+    (1504, 3000, 0.5, torch.bfloat16),    # 1024 threads, 4 rows, two groups (375 of 512 used)
+    (784, 6000, 1.0, torch.bfloat16),     # 1024 threads, 4 rows, four groups (750 of 1024 used)
+    (3008, 12000, 0.0, torch.bfloat16),   # 1024 threads, 2 rows, four groups (1500 of 2048 used)
+    (1008, 20000, 0.5, torch.bfloat16),   # 1024 threads, 1 row, three groups (2500 of 3072 used)
     (3408, 40008, 1.0, torch.bfloat16),   # 5001 groups over 1024 threads: the LDS group partly masked
     # the two-call sequence: general alpha beyond 32768 columns, N % 8 != 0, fp32
     (304, 1001, 0.5, torch.bfloat16),
