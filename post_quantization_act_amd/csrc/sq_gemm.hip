@@ -1025,10 +1025,10 @@ const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl) {
         case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
         case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2,2> (256x256 tile, 8 wavefronts of 64x128, 2 stages)";
         case GemmPath::kRing256Split:
-            return "k_gemm_ring<256,256,4,2,2> on whole rounds of columns + k_gemm_ring<256,128,2,4,3> on the "
+            return "k_gemm_ring<256,256,4,2,2> on whole rounds of columns + k_gemm_ring<256,128,4,2,3> on the "
                    "remaining columns (one round)";
         case GemmPath::kRing256x128:
-            return "k_gemm_ring<256,128,2,4,3> (256x128 tile, 8 wavefronts of 128x32, 3 stages)";
+            return "k_gemm_ring<256,128,4,2,3> (256x128 tile, 8 wavefronts of 64x64, 3 stages)";
         case GemmPath::kRing128: return "k_gemm_ring<128,128,2,4,2> (128x128 tile, 8 wavefronts of 64x32, 2 stages)";
         case GemmPath::kGeneric: return "k_gemm_generic<256,128> (register-staged, any K % 16 == 0)";
         default: return "none (empty product)";
@@ -1055,12 +1055,12 @@ static hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool per_t
             const int n1 = (int)ring256_split_cols(M64, N64, device_cu_count());
             launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, n1, K, y, y_bf16, acc_out, op, 4,
                                            st, 0, N);
-            launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N - n1, K, y, y_bf16, acc_out, op,
+            launch_ring<256, 128, 4, 2, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N - n1, K, y, y_bf16, acc_out, op,
                                            8, st, n1, N);
             break;
         }
         case GemmPath::kRing256x128:
-            launch_ring<256, 128, 2, 4, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8,
+            launch_ring<256, 128, 4, 2, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8,
                                            st);
             break;
         case GemmPath::kRing128:
