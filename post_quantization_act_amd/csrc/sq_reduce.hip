@@ -168,6 +168,8 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // in LDS before, the per-row results are written after it.  The block's
 // column maxima (its RB slots combined through LDS) leave as plain stores to
 // partial[blockIdx.x][N]; k_colmax_reduce takes the maximum over blocks.
+// kKeep: plain loads instead of nontemporal ones, for a W that the weight
+// codes read again right after this pass.
 constexpr int kPrepThreads = 512;
 constexpr int kPrepMaxRows = 256;  // rows per block (LDS staging of per-row values)
 
@@ -175,7 +177,7 @@ __device__ __forceinline__ void lds_only_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int RB, int GR, int GL, bool kGeneral, int NT = kPrepThreads>
+template <int RB, int GR, int GL, bool kGeneral, int NT = kPrepThreads, bool kKeep = false>
 __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, int64_t K, int64_t N,
                                                             int64_t ld, const float* __restrict__ amax_x,
                                                             float alpha, float* __restrict__ s,
@@ -210,7 +212,8 @@ __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, 
 #pragma unroll
         for (int i = 0; i < GPT; ++i) {
             const int64_t q = ts + (int64_t)TPR * i;
-            dst[i] = (rl < nrows && 8 * q < N) ? ld16_stream(row + 8 * q) : make_uint4(0, 0, 0, 0);
+            const bool in = rl < nrows && 8 * q < N;
+            dst[i] = in ? (kKeep ? ld16(row + 8 * q) : ld16_stream(row + 8 * q)) : make_uint4(0, 0, 0, 0);
         }
     };
     if (iters > 0) load_rows(0, cur);
@@ -464,9 +467,19 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
     const int rpb = (int)((K + nb - 1) / nb);
     const int64_t groups = N / 8;
     const bf16_t* wb = static_cast<const bf16_t*>(w);
+    // W of up to 128 MB is read without the nontemporal hint, so the caches
+    // (the 256 MB memory-side cache above all) still hold much of it when the
+    // weight codes read it again right after: 1.8 us off steps 2-4 at
+    // 4096x4096.  Larger W streams.
+    const bool keep = (uint64_t)K * (uint64_t)ld * 2u <= (128ull << 20);
+#define SQ_PREP_KEEP(RB, GR, GL, G, NT, KEEP)                                                                     \
+    hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G, NT, KEEP>), dim3((unsigned)nb), dim3(NT), 0, st, wb, K, N, ld,     \
+                       amax_x, alpha, s, inv_s, amax_w, partial, rpb)
 #define SQ_PREP_NT(RB, GR, GL, G, NT)                                                                             \
-    hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G, NT>), dim3((unsigned)nb), dim3(NT), 0, st, wb, K, N, ld, amax_x,  \
-                       alpha, s, inv_s, amax_w, partial, rpb)
+    do {                                                                                                          \
+        if (keep) SQ_PREP_KEEP(RB, GR, GL, G, NT, true);                                                          \
+        else SQ_PREP_KEEP(RB, GR, GL, G, NT, false);                                                              \
+    } while (0)
 #define SQ_PREP(RB, GR, GL, G) SQ_PREP_NT(RB, GR, GL, G, kPrepThreads)
     // Rows per iteration so that each thread has 4-8 loads of 16 bytes in
     // flight per row set (several rows at once for narrow W: with one row per
@@ -495,6 +508,7 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
     }
 #undef SQ_PREP
 #undef SQ_PREP_NT
+#undef SQ_PREP_KEEP
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_colmax_reduce, dim3((unsigned)((N + kRedCols - 1) / kRedCols)), dim3(1024), 0, st, partial, nb,
