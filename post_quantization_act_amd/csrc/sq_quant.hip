@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int6
 // (loaded once, instead of once per row); the next row's 16-byte loads are in
 // flight while the current row is reduced (one barrier per row, LDS slots
 // alternating between rows) and coded.  Codes and scales as k_quant_act.
-template <int NV, bool kStatic>
+template <int NV, bool kStatic, bool kKeepOut = false>
 __device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk, const bf16_t* __restrict__ x,
                                                      int64_t M, int64_t K, int64_t ld,
                                                      const float* __restrict__ inv_s, int8_t* __restrict__ xq,
@@ -323,8 +323,9 @@ __device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk,
 #pragma unroll
                     for (int i = 0; i < 8; ++i)
                         c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
-                    st8_stream(xq + row * K + g * 8,
-                               make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+                    const uint2 pk = make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+                    if constexpr (kKeepOut) *reinterpret_cast<uint2*>(xq + row * K + g * 8) = pk;
+                    else st8_stream(xq + row * K + g * 8, pk);
                 }
             }
         };
@@ -347,8 +348,10 @@ __global__ __launch_bounds__(256) void k_quant_act_stream(const bf16_t* __restri
 // s / inv_s and the column maxima, and each alone leaves the memory system
 // idle during its start and tail at attention-projection sizes.  Blocks
 // [0, tiles) code 128 x 128 weight tiles (bf16, 16-byte aligned rows), the
-// others walk token rows with the block count as their stride.
-template <int NV>
+// others walk token rows with the block count as their stride.  kKeepOut:
+// the activation codes leave as plain stores, so the GEMM that reads them
+// next finds them in the caches (nontemporal stores otherwise).
+template <int NV, bool kKeepOut>
 __global__ __launch_bounds__(256) void k_codes_both(const bf16_t* __restrict__ w, int64_t K, int64_t N, int64_t ldw,
                                                     const float* __restrict__ s,
                                                     const uint32_t* __restrict__ colmax, int8_t* __restrict__ wq,
@@ -359,8 +362,8 @@ __global__ __launch_bounds__(256) void k_codes_both(const bf16_t* __restrict__ w
     if ((int64_t)blockIdx.x < tiles)
         quant_weight_tile<bf16_t, true, true>(blockIdx.x, w, K, N, ldw, s, colmax, wq, w_scale);
     else
-        quant_act_stream_rows<NV, false>((int64_t)blockIdx.x - tiles, (int64_t)gridDim.x - tiles, x, M, K, ldx,
-                                         inv_s, xq, x_scale, nullptr);
+        quant_act_stream_rows<NV, false, kKeepOut>((int64_t)blockIdx.x - tiles, (int64_t)gridDim.x - tiles, x, M, K,
+                                                   ldx, inv_s, xq, x_scale, nullptr);
 }
 
 // The per-tensor maximum a = max_ij |fl(x_ij inv_s_j)| (the first of the two
@@ -757,12 +760,17 @@ hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, c
     const dim3 grid((unsigned)(tiles + rows));
     const bf16_t* wb = static_cast<const bf16_t*>(w);
     const bf16_t* xb = static_cast<const bf16_t*>(x);
-    if (groups <= 256)
-        hipLaunchKernelGGL((k_codes_both<1>), grid, dim3(256), 0, st, wb, K, N, ldw, s, colmax, wq, w_scale, tiles, xb,
-                           M, ldx, inv_s, xq, x_scale);
-    else
-        hipLaunchKernelGGL((k_codes_both<2>), grid, dim3(256), 0, st, wb, K, N, ldw, s, colmax, wq, w_scale, tiles, xb,
-                           M, ldx, inv_s, xq, x_scale);
+    // activation codes of up to 64 MB stay cacheable for the GEMM: 0.9 us off
+    // the 2048x4096x4096 GEMM that follows
+    const bool keep = (uint64_t)M * (uint64_t)K <= (64ull << 20);
+    auto go = [&](auto nv, auto kp) {
+        hipLaunchKernelGGL((k_codes_both<decltype(nv)::value, decltype(kp)::value>), grid, dim3(256), 0, st, wb, K, N,
+                           ldw, s, colmax, wq, w_scale, tiles, xb, M, ldx, inv_s, xq, x_scale);
+    };
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (groups <= 256) { if (keep) go(I1{}, std::true_type{}); else go(I1{}, std::false_type{}); }
+    else { if (keep) go(I2{}, std::true_type{}); else go(I2{}, std::false_type{}); }
     return hipGetLastError();
 }
 
