@@ -207,7 +207,9 @@ __device__ __forceinline__ void epilogue(const v16i (&acc)[TN][TM], int nbase, i
 // into its own [m][n] LDS region (row stride WN + 8 elements, 16-byte aligned
 // rows), then copies them out 16 bytes (8 outputs) per lane along n, so each
 // store instruction covers whole 256-byte runs of rows of y instead of 64
-// scattered 8-byte pieces.  Same arithmetic as epilogue<> per element.
+// scattered 8-byte pieces.  The stores are nontemporal: y is written once,
+// and dirty lines left in L2 would be written back at the end of the launch.
+// Same arithmetic as epilogue<> per element.
 // sx, sw: the wavefront's token and weight scales, staged in LDS.
 template <int TN, int TM>
 __device__ __forceinline__ void epilogue_bf16_lds(const v16i (&acc)[TN][TM], int nbase, int mbase, int lane,
@@ -240,7 +242,7 @@ __device__ __forceinline__ void epilogue_bf16_lds(const v16i (&acc)[TN][TM], int
             const int ml = c / CH, nc = c % CH;
             const int mm = mbase + b * 32 + ml, n = nbase + nc * 8;
             const uint4 v = *reinterpret_cast<const uint4*>(ldsw + ml * RS + nc * 8);
-            if (mm < M && n < N) *reinterpret_cast<uint4*>(y + (int64_t)mm * ldy + n) = v;
+            if (mm < M && n < N) st16_stream(y + (int64_t)mm * ldy + n, v);  // written once
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next group reuses the region
     }
