@@ -20,7 +20,7 @@ namespace sqk {
 // columns, the 8 codes along j as one 8-byte word; rows of the LDS tile are
 // padded to 136 bytes so a wavefront's 8-byte writes spread over all banks.
 // The tile then leaves as 16-byte stores of 16 consecutive j of one output
-// channel (wq is [N, K], K contiguous).
+// channel (wq is [N, K], K contiguous), nontemporal when stream_out is set.
 constexpr int kQwTile = 128;
 constexpr int kQwStride = kQwTile + 8;
 constexpr int kQwGroup = 16;
@@ -29,7 +29,7 @@ template <typename T, bool kScaled, bool kVec>
 __device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restrict__ w, int64_t K, int64_t N,
                                                   int64_t ld, const float* __restrict__ s,
                                                   const uint32_t* __restrict__ colmax, int8_t* __restrict__ wq,
-                                                  float* __restrict__ w_scale) {
+                                                  float* __restrict__ w_scale, bool stream_out) {
     __shared__ float r_s[kQwTile];
     __shared__ __align__(16) uint8_t tile[kQwTile * kQwStride];
 
@@ -132,7 +132,9 @@ __device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restri
             const uint8_t* src = tile + kl * kQwStride + jc * 16;
             uint2 a = *reinterpret_cast<const uint2*>(src);
             uint2 b = *reinterpret_cast<const uint2*>(src + 8);
-            *reinterpret_cast<uint4*>(wq + k * K + j) = make_uint4(a.x, a.y, b.x, b.y);
+            const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
+            if (stream_out) st16_stream(wq + k * K + j, v);  // uniform over the grid
+            else *reinterpret_cast<uint4*>(wq + k * K + j) = v;
         }
     }
 }
@@ -141,8 +143,9 @@ template <typename T, bool kScaled, bool kVec>
 __global__ __launch_bounds__(256) void k_quant_weight(const T* __restrict__ w, int64_t K, int64_t N, int64_t ld,
                                                       const float* __restrict__ s,
                                                       const uint32_t* __restrict__ colmax,
-                                                      int8_t* __restrict__ wq, float* __restrict__ w_scale) {
-    quant_weight_tile<T, kScaled, kVec>(blockIdx.x, w, K, N, ld, s, colmax, wq, w_scale);
+                                                      int8_t* __restrict__ wq, float* __restrict__ w_scale,
+                                                      int stream_out) {
+    quant_weight_tile<T, kScaled, kVec>(blockIdx.x, w, K, N, ld, s, colmax, wq, w_scale, stream_out != 0);
 }
 
 // ---- activations -------------------------------------------------------------
@@ -358,9 +361,9 @@ __global__ __launch_bounds__(256) void k_codes_both(const bf16_t* __restrict__ w
                                                     float* __restrict__ w_scale, int64_t tiles,
                                                     const bf16_t* __restrict__ x, int64_t M, int64_t ldx,
                                                     const float* __restrict__ inv_s, int8_t* __restrict__ xq,
-                                                    float* __restrict__ x_scale) {
+                                                    float* __restrict__ x_scale, int w_stream) {
     if ((int64_t)blockIdx.x < tiles)
-        quant_weight_tile<bf16_t, true, true>(blockIdx.x, w, K, N, ldw, s, colmax, wq, w_scale);
+        quant_weight_tile<bf16_t, true, true>(blockIdx.x, w, K, N, ldw, s, colmax, wq, w_scale, w_stream != 0);
     else
         quant_act_stream_rows<NV, false, kKeepOut>((int64_t)blockIdx.x - tiles, (int64_t)gridDim.x - tiles, x, M, K,
                                                    ldx, inv_s, xq, x_scale, nullptr);
@@ -478,17 +481,22 @@ __global__ __launch_bounds__(256) void k_quant_act_long(const T* __restrict__ x,
 
 // ---- launchers -----------------------------------------------------------------
 
+// Weight codes beyond 64 MB leave as nontemporal stores; smaller ones stay
+// cacheable for the GEMM that reads them next.
+static int weight_codes_stream(int64_t K, int64_t N) { return (uint64_t)K * (uint64_t)N > (64ull << 20) ? 1 : 0; }
+
 hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* s,
                                const uint32_t* colmax, int8_t* wq, float* w_scale, hipStream_t st) {
     if (K <= 0 || N <= 0) return hipSuccess;
     const int64_t tiles = ((N + kQwTile - 1) / kQwTile) * ((K + kQwTile - 1) / kQwTile);
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;  // beyond 2^45 weights: not addressable in one grid
     dim3 grid((unsigned)tiles);
+    const int w_stream = weight_codes_stream(K, N);
     const bool vec = rows_aligned16(w, ld, bf16 ? 2 : 4);
     auto go = [&](auto tag, auto scaled, auto vecc) {
         using T = decltype(tag);
         hipLaunchKernelGGL((k_quant_weight<T, decltype(scaled)::value, decltype(vecc)::value>), grid, dim3(256), 0,
-                           st, static_cast<const T*>(w), K, N, ld, s, colmax, wq, w_scale);
+                           st, static_cast<const T*>(w), K, N, ld, s, colmax, wq, w_scale, w_stream);
     };
     using TT = std::true_type;
     using FF = std::false_type;
@@ -765,7 +773,7 @@ hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, c
     const bool keep = (uint64_t)M * (uint64_t)K <= (64ull << 20);
     auto go = [&](auto nv, auto kp) {
         hipLaunchKernelGGL((k_codes_both<decltype(nv)::value, decltype(kp)::value>), grid, dim3(256), 0, st, wb, K, N,
-                           ldw, s, colmax, wq, w_scale, tiles, xb, M, ldx, inv_s, xq, x_scale);
+                           ldw, s, colmax, wq, w_scale, tiles, xb, M, ldx, inv_s, xq, x_scale, weight_codes_stream(K, N));
     };
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
