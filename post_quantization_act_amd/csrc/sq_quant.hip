@@ -373,11 +373,13 @@ __global__ __launch_bounds__(256) void k_codes_both(const bf16_t* __restrict__ w
 // passes of dynamic per-tensor step 4): blocks walk token rows with a grid
 // stride, two rows' loads in flight, each thread keeps the inv_s of its
 // channel groups in registers and one running maximum; one atomicMax per
-// block on the fp32 bit pattern (*gmax starts at 0).
+// block on the fp32 bit pattern (*gmax starts at 0).  keep: plain loads, so
+// the codes pass that reads x again finds much of it in the caches (the
+// 256 MB memory-side cache above all); nontemporal loads otherwise.
 template <int NV>
 __global__ __launch_bounds__(256) void k_act_absmax_stream(const bf16_t* __restrict__ x, int64_t M, int64_t K,
                                                            int64_t ld, const float* __restrict__ inv_s,
-                                                           uint32_t* __restrict__ gmax) {
+                                                           uint32_t* __restrict__ gmax, int keep) {
     const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, t = threadIdx.x;
     const int64_t groups = K / 8;
     float is[NV][8];
@@ -403,7 +405,8 @@ __global__ __launch_bounds__(256) void k_act_absmax_stream(const bf16_t* __restr
 #pragma unroll
             for (int q = 0; q < NV; ++q) {
                 const int64_t rr = row + r * stride, g = t + (int64_t)q * 256;
-                u[r][q] = (rr < M && g < groups) ? ld16_stream(x + rr * ld + g * 8) : make_uint4(0, 0, 0, 0);
+                const bf16_t* p = x + rr * ld + g * 8;
+                u[r][q] = (rr < M && g < groups) ? (keep ? ld16(p) : ld16_stream(p)) : make_uint4(0, 0, 0, 0);
             }
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -718,15 +721,17 @@ static void launch_act_absmax_stream(const bf16_t* x, int64_t M, int64_t K, int6
         cus = 256;
     const int64_t grid = std::min<int64_t>(M, (int64_t)cus * 4);
     const dim3 g((unsigned)grid);
+    // x of up to 256 MB: 8 % off the two-pass per-tensor codes at 8192x12288
+    const int keep = (uint64_t)M * (uint64_t)ld * 2u <= (256ull << 20) ? 1 : 0;
     switch ((K / 8 + 255) / 256) {
-        case 1: hipLaunchKernelGGL((k_act_absmax_stream<1>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        case 2: hipLaunchKernelGGL((k_act_absmax_stream<2>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        case 3: hipLaunchKernelGGL((k_act_absmax_stream<3>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        case 4: hipLaunchKernelGGL((k_act_absmax_stream<4>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        case 5: hipLaunchKernelGGL((k_act_absmax_stream<5>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        case 6: hipLaunchKernelGGL((k_act_absmax_stream<6>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        case 7: hipLaunchKernelGGL((k_act_absmax_stream<7>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
-        default: hipLaunchKernelGGL((k_act_absmax_stream<8>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax); break;
+        case 1: hipLaunchKernelGGL((k_act_absmax_stream<1>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        case 2: hipLaunchKernelGGL((k_act_absmax_stream<2>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        case 3: hipLaunchKernelGGL((k_act_absmax_stream<3>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        case 4: hipLaunchKernelGGL((k_act_absmax_stream<4>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        case 5: hipLaunchKernelGGL((k_act_absmax_stream<5>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        case 6: hipLaunchKernelGGL((k_act_absmax_stream<6>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        case 7: hipLaunchKernelGGL((k_act_absmax_stream<7>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
+        default: hipLaunchKernelGGL((k_act_absmax_stream<8>), g, dim3(256), 0, st, x, M, K, ld, inv_s, gmax, keep); break;
     }
 }
 
