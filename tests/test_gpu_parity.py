@@ -425,3 +425,31 @@ def test_gemm_largest_k_extremes(M, N):
     for _ in range(2):
         r = rng.choice(np.array([-1, 1], dtype=np.int64), size=N)
         np.testing.assert_array_equal(C @ r, A @ (B.T @ r))
+
+
+def test_per_tensor_dynamic_large_x_streams():
+    """Dynamic per-tensor codes of an x above 256 MB (16400 x 8192 bf16): the max
+    pass takes its nontemporal-load branch (smaller x is read as plain loads).
+    The maximum is checked through the oracle's calibrated-maximum function on
+    all of x, the codes on sampled rows (static codes with that maximum equal
+    the dynamic ones, a CPU pin)."""
+    M, K = 16400, 8192
+    _say(f"per-tensor dynamic M={M} K={K}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    idx = torch.randperm(K, generator=g, device=DEV)[: K // 100]
+    fac = torch.full((idx.numel(),), 100.0, device=DEV)
+    x = synth.activations(M, K, "normal", idx, fac, torch.bfloat16, g, DEV)
+    inv_s = (torch.rand(K, generator=g, device=DEV) + 0.5).float()
+    xq = torch.empty(M, K, dtype=torch.int8, device=DEV)
+    xs = torch.empty(1, dtype=torch.float32, device=DEV)
+    nb = sq.sq_workspace_size(sq.SQ_OP_QUANT_ACT, M, 1, K, sq.SQ_PER_TENSOR)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=DEV)
+    sq.sq_quant_act(x, inv_s, sq.SQ_PER_TENSOR, xq, xs, ws)
+    torch.cuda.synchronize()
+    xn, isn = _np(x), _np(inv_s)
+    a = oracle.static_act_max(xn, isn)
+    rows = [0, 1, 4097, M // 2, M - 2, M - 1]
+    oq, os_ = oracle.quant_act_static(xn[rows], isn, a)
+    np.testing.assert_array_equal(_np(xs), os_)
+    np.testing.assert_array_equal(_np(xq[rows]), oq)
