@@ -74,6 +74,7 @@ CASES = [
     (1, 256, 64, 1.0, torch.bfloat16, torch.bfloat16, sq.SQ_PER_TOKEN),         # one token
     (4100, 512, 256, 0.5, torch.bfloat16, torch.bfloat16, sq.SQ_PER_TOKEN),     # more rows than row blocks
     (16400, 4096, 256, 0.5, torch.bfloat16, torch.bfloat16, sq.SQ_PER_TOKEN),  # codes above 64 MB: streaming stores
+    (64, 4096, 20000, 0.5, torch.bfloat16, torch.bfloat16, sq.SQ_PER_TOKEN),   # weight codes above 64 MB: streaming stores
     (64, 8192, 256, 0.5, torch.bfloat16, torch.bfloat16, sq.SQ_PER_TOKEN),      # K > 4096: two code launches
     (96, 512, 384, 0.5, torch.bfloat16, torch.bfloat16, sq.SQ_PER_TENSOR),      # the two calls
     (96, 512, 384, 0.5, torch.bfloat16, torch.float32, sq.SQ_PER_TOKEN),        # fp32 X: the two calls
