@@ -41,8 +41,10 @@
  *   - Every call is asynchronous on `stream` (NULL = the default stream of the
  *     current device) and returns after enqueueing.  Buffers must stay valid
  *     until the stream's work completes.  Calls on one stream are ordered.
- *   - The caller owns all memory.  The library allocates nothing and keeps no
- *     mutable global state except a per-thread error message.
+ *   - The caller owns all memory.  The library allocates nothing.  Its only
+ *     mutable global state is a per-thread error message and a per-device
+ *     cache of the compute-unit count (filled on first use, read and written
+ *     atomically; the GEMM's launch shape depends on it).
  *   - Arguments are validated before anything is enqueued; a failed check
  *     returns a negative sq_status, enqueues nothing and records a message for
  *     sq_last_error().  A launch failure returns SQ_ERR_HIP.
@@ -236,16 +238,25 @@ sq_status sq_prepare_and_quant_act(const float *amax_x, const void *w, sq_dtype 
  *   unused).  All [K] fp32 device vectors; outputs may alias the inputs.
  * sq_layernorm_quant: at run time, LayerNorm of each bf16 token row of
  *   x [M, K] with the folded gamma/beta, then per-token INT8 codes (step 4
- *   with the smoothing already inside gamma/beta):
- *     S1 = sum_j x_j, S2 = sum_j x_j^2 in fp64; mu = S1 / K;
- *     var = max(S2 / K - mu^2, 0); rstd = 1 / sqrt(var + eps) (fp64);
- *     z_j = fl(fl((float)((x_j - mu) * rstd) * gamma_j) + beta_j);
- *     x_scale[i] = fl(m_i / 127), codes clamp(rne(fl(z_j * fl(127 / m_i)))).
- *   The fp64 sums are exact (so the result does not depend on the order of
- *   summation) when a row's magnitudes span less than 2^29; results are
- *   specified under that condition.  x: bf16 only (SQ_ERR_UNSUPPORTED
- *   otherwise), 16-byte aligned rows; K <= 16384; gamma (and beta) 16-byte
- *   aligned; xq [M, K] and x_scale [M] as sq_quant_act per token.
+ *   with the smoothing already inside gamma/beta).  The page gives the
+ *   formula, not its arithmetic; the library computes, per row:
+ *     A = max_j |x_j|, with 2^(E-1) <= A < 2^E (E = 0 when A = 0);
+ *     S1 = sum_j trunc(x_j * 2^(39-E)) and S2 = sum_j trunc(x_j^2 * 2^(39-2E))
+ *       (truncation toward zero; integers below 2^39, summed exactly, so the
+ *       statistics do not depend on the order of summation);
+ *     mu = S1 * 2^(E-39) / K and var = max(S2 * 2^(2E-39) / K - mu^2, 0),
+ *       each in fp64 with single roundings (mu = var = 0 when A = 0);
+ *     mu32 = (float)mu, rstd32 = (float)(1 / sqrt(var + (double)eps))
+ *       (fp64 sqrt and divide, then one rounding to fp32);
+ *     n_j = fl(fl(x_j - mu32) * rstd32), z_j = fl(fl(n_j * gamma_j) + beta_j)
+ *       (z_j = fl(n_j * gamma_j) when beta is NULL);
+ *     m_i = max_j |z_j|, x_scale[i] = fl(m_i / 127) and
+ *       codes clamp(rne(fl(z_j * fl(127 / m_i))), -127, 127) (0 when m_i = 0).
+ *   The truncation moves mu by less than 2^(E-39) and the mean square by less
+ *   than 2^(2E-39) from the exact row statistics (biased variance, eps inside
+ *   the root).  x: bf16 only (SQ_ERR_UNSUPPORTED otherwise), 16-byte aligned
+ *   rows; K <= 16384; eps >= 0; gamma (and beta) 16-byte aligned; xq [M, K]
+ *   and x_scale [M] as sq_quant_act per token.
  */
 sq_status sq_fold_layernorm(const float *gamma, const float *beta, const float *inv_s, int64_t K, float *gamma_out,
                             float *beta_out, hipStream_t stream);

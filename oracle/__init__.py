@@ -201,8 +201,11 @@ def fold_layernorm(gamma: np.ndarray, beta: np.ndarray | None, inv_s: np.ndarray
 
 
 def layernorm_quant(x_bf16: np.ndarray, gamma: np.ndarray, beta: np.ndarray | None, eps: float):
-    """LayerNorm of each bf16 row (fp64 statistics) with gamma/beta, then per-token INT8:
-    (xq[M, K], x_scale[M])."""
+    """The library's arithmetic contract for LayerNorm + per-token INT8: the row
+    statistics on a fixed-point grid (order-free exact sums), then fp32
+    normalisation (see sqo_layernorm_quant in sq_oracle.c).  It is the bit-exact
+    reference of the kernel; layernorm_quant_plain is the definition it is
+    held to.  Returns (xq[M, K], x_scale[M])."""
     x = np.ascontiguousarray(x_bf16)
     if x.dtype != np.uint16:
         raise TypeError("layernorm_quant takes bf16 bit patterns (uint16)")
@@ -214,6 +217,47 @@ def layernorm_quant(x_bf16: np.ndarray, gamma: np.ndarray, beta: np.ndarray | No
     _check(lib().sqo_layernorm_quant(_p(x), M, K, K, _p(g), _p(b), ctypes.c_float(eps), _p(xq), K, _p(xs)),
            "layernorm_quant")
     return xq, xs
+
+
+def layernorm_quant_plain(x_bf16: np.ndarray, gamma: np.ndarray, beta: np.ndarray | None, eps: float):
+    """LayerNorm of each bf16 row, then per-token symmetric INT8, straight from
+    the definition in fp64 with no fp32 rounding anywhere (page "4.2 W8A8 量化与
+    SmoothQuant" section 6: LN(x)_j / s_j = (x_j - mu) / sigma * gamma_j / s_j +
+    beta_j / s_j; gamma and beta here are the folded gamma / s and beta / s):
+
+      mu = (sum_j x_j) / K,   var = (sum_j (x_j - mu)^2) / K   (biased),
+      sigma = sqrt(var + eps),  z_j = (x_j - mu) / sigma * gamma_j + beta_j,
+      m = max_j |z_j|,  scale = m / 127,  q_j = z_j * 127 / m,
+      code_j = clip(round_half_even(q_j), -127, 127)   (all 0 when m = 0).
+
+    The sums are taken with math.fsum (correctly rounded), so mu is the fp64
+    rounding of the exact mean.  eps enters as the fp64 value of the fp32 eps
+    the library takes.  Returns a dict: codes int8 [M, K], scale, mu, var, m
+    (fp64 [M]) and z, q (fp64 [M, K], the values before rounding)."""
+    import math
+
+    x = np.ascontiguousarray(x_bf16)
+    if x.dtype != np.uint16:
+        raise TypeError("layernorm_quant_plain takes bf16 bit patterns (uint16)")
+    M, K = x.shape
+    xf = bf16_to_f32(x).astype(np.float64)
+    g = np.asarray(gamma, dtype=np.float32).astype(np.float64)
+    b = None if beta is None else np.asarray(beta, dtype=np.float32).astype(np.float64)
+    e = float(np.float32(eps))
+    mu = np.empty(M)
+    var = np.empty(M)
+    for i in range(M):
+        mu[i] = math.fsum(xf[i].tolist()) / K
+        d = xf[i] - mu[i]
+        var[i] = math.fsum((d * d).tolist()) / K
+    z = (xf - mu[:, None]) / np.sqrt(var + e)[:, None] * g[None, :]
+    if b is not None:
+        z = z + b[None, :]
+    m = np.abs(z).max(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(m[:, None] > 0, z * (127.0 / np.where(m > 0, m, 1.0))[:, None], 0.0)
+    codes = np.clip(np.rint(q), -127, 127).astype(np.int8)
+    return dict(codes=codes, scale=m / 127.0, mu=mu, var=var, m=m, z=z, q=q)
 
 
 def gemm_i8(xq: np.ndarray, wq: np.ndarray, nthreads: int = 1) -> np.ndarray:

@@ -28,6 +28,7 @@
 // XCD walks a contiguous run of a grouped (m-major within groups of 8 tile
 // rows) raster and concurrent blocks on one XCD share operand panels in its L2.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <type_traits>
@@ -851,16 +852,20 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
     }
 }
 
+// Compute units of the current device, queried once per device.  The cache
+// is read and written atomically (relaxed: every thread that fills an entry
+// stores the same value), so concurrent first calls from several host threads
+// are safe.
 static int device_cu_count() {
-    static int cache[64] = {0};
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 static bool decode_ring_fits(int64_t M, int64_t N, int64_t K) {

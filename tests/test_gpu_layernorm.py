@@ -1,11 +1,14 @@
 """LayerNorm fold on the GPU: sq_fold_layernorm and the fused LayerNorm +
-per-token INT8 kernel equal the oracle bit for bit (every row layout of the
-kernel, ragged token counts, constant and all-zero rows, no bias), and the
-folded runtime path (fold -> LayerNorm codes -> GEMM) equals the oracle's."""
+per-token INT8 kernel equal the library's contract (the oracle's fixed-point
+statistics and fp32 normalisation) bit for bit, and stay within the derived
+bound of the plain fp64 LayerNorm definition (every row layout of the kernel,
+ragged token counts, constant and all-zero rows, no bias); the folded runtime
+path (fold -> LayerNorm codes -> GEMM) equals the oracle's."""
 import numpy as np
 import pytest
 import torch
 
+import ln_bound
 import oracle
 import post_quantization_act_amd as sq
 import synth
@@ -50,6 +53,30 @@ def test_layernorm_quant_matches_oracle(M, K, with_beta):
     xq_o, xs_o = oracle.layernorm_quant(_np(x), gamma.numpy(), None if b is None else b.numpy(), 1e-5)
     np.testing.assert_array_equal(_np(xs), xs_o)
     np.testing.assert_array_equal(_np(xq), xq_o)
+
+
+@pytest.mark.parametrize("M,K", [(130, 256), (13, 1024), (64, 2048), (37, 4096), (9, 8192), (40, 12288),
+                                 (5, 16384)])
+@pytest.mark.parametrize("with_beta", [True, False])
+def test_layernorm_quant_within_bound_of_definition(M, K, with_beta):
+    """The kernel against the plain fp64 LayerNorm (two-pass mean and biased
+    variance, eps inside the root, then per-token codes), not against its own
+    contract: scales within the derived bound, codes equal to the definition's
+    except within the bound of a rounding boundary, and there within one."""
+    print(f"layernorm vs definition M={M} K={K} beta={with_beta}", flush=True)
+    x, gamma, beta = _rows(M, K, M * 5 + K + 1)
+    x[0] = 1.5
+    if M > 2:
+        x[2] = 0.0
+    b = beta if with_beta else None
+    xq = torch.empty(M, K, dtype=torch.int8, device=DEV)
+    xs = torch.empty(M, dtype=torch.float32, device=DEV)
+    sq.sq_layernorm_quant(x.to(DEV), gamma.to(DEV), None if b is None else b.to(DEV), 1e-5, xq, xs)
+    torch.cuda.synchronize()
+    bn = None if b is None else b.numpy()
+    plain = oracle.layernorm_quant_plain(_np(x), gamma.numpy(), bn, 1e-5)
+    xf = oracle.bf16_to_f32(_np(x)).astype(np.float64)
+    ln_bound.check(_np(xq), _np(xs), xf, gamma.numpy(), bn, 1e-5, plain)
 
 
 def test_fold_layernorm_matches_oracle():

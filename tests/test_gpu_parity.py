@@ -120,6 +120,42 @@ def test_pipeline_matches_oracle(M, K, N, dtype, gran, alpha, T, y_dtype):
     _compare(b, o, alpha, y_dtype)
 
 
+# Shapes whose bf16 output takes the LDS-staged epilogue (N % 8 == 0, no int32
+# accumulator store) with ragged edges, one per tile launch: (M, K, N, the
+# kernel-name fragment the shape must select).
+DEPLOYED_EPILOGUE = [
+    (4100, 384, 16392, "k_gemm_ring<256,256,4,2,2> (256x256"),        # 256 x 256 tiles, ragged M
+    (500, 128, 66536, "on the remaining columns"),                   # column split, ragged M and last launch
+    (2100, 384, 3000, "k_gemm_ring<256,128,4,2,3> (256x128"),        # 256 x 128 tiles, ragged M and N
+    (33000, 256, 104, "k_gemm_ring<128,128,2,4,2>"),                 # 128 x 128 tiles, N < one tile
+]
+
+
+@pytest.mark.parametrize("M,K,N,dtype,gran,alpha,T", CASES)
+def test_deployed_epilogue_matches_oracle(M, K, N, dtype, gran, alpha, T):
+    """The call as deployed: bf16 output and no int32 accumulator store, so the
+    ring kernels take their LDS-staged bf16 epilogue wherever N % 8 == 0;
+    every output element against the oracle's."""
+    _say(f"deployed case M={M} K={K} N={N} {dtype} gran={gran} alpha={alpha} T={T}")
+    x, w, calib = _inputs(M, K, N, dtype, seed=M * 7 + K * 3 + N + 1, T=T)
+    b = _run_gpu(x.to(DEV), w.to(DEV), calib.to(DEV), alpha, gran, torch.bfloat16, with_acc=False)
+    o = oracle.w8a8_linear(_np(x), _np(w), alpha, gran, calib=_np(calib), nthreads=8)
+    _compare(b, o, alpha, torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,K,N,kernel", DEPLOYED_EPILOGUE)
+def test_deployed_epilogue_ragged_tiles(M, K, N, kernel):
+    """Ragged M and N with N % 8 == 0 on each tile launch of the GEMM, bf16
+    output, no accumulator store: the LDS-staged epilogue's edge handling,
+    compared element by element with the oracle."""
+    _say(f"deployed ragged M={M} K={K} N={N}")
+    assert kernel in sq.sq_gemm_kernel_name(M, N, K)
+    x, w, calib = _inputs(M, K, N, torch.bfloat16, seed=M + 11 * N + K, T=256)
+    b = _run_gpu(x.to(DEV), w.to(DEV), calib.to(DEV), 0.5, sq.SQ_PER_TOKEN, torch.bfloat16, with_acc=False)
+    o = oracle.w8a8_linear(_np(x), _np(w), 0.5, sq.SQ_PER_TOKEN, calib=_np(calib), nthreads=8)
+    _compare(b, o, 0.5, torch.bfloat16)
+
+
 @pytest.mark.parametrize("gran", [sq.SQ_PER_TOKEN, sq.SQ_PER_TENSOR])
 def test_unsmoothed_baseline_matches_oracle(gran):
     x, w, calib = _inputs(200, 320, 150, torch.bfloat16, seed=5)

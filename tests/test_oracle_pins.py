@@ -498,6 +498,90 @@ def test_layernorm_quant_constant_row_is_beta():
     np.testing.assert_array_equal(xs, s)
 
 
+def test_layernorm_plain_closed_form():
+    """The definition on x = [1, 2, 3, 4], gamma = 1, no beta, eps = 0:
+    z = (x - 2.5) / sqrt(1.25), codes [-127, -42, 42, 127], scale 1.5 / sqrt(1.25) / 127."""
+    r = oracle.layernorm_quant_plain(_bf16([[1, 2, 3, 4]]), np.ones(4, np.float32), None, 0.0)
+    assert r["codes"].tolist() == [[-127, -42, 42, 127]]
+    assert r["mu"][0] == 2.5 and r["var"][0] == 1.25
+    assert abs(r["scale"][0] - 1.5 / np.sqrt(1.25) / 127) < 1e-15
+
+
+def test_layernorm_plain_against_exact_rationals():
+    """Brute force on tiny rows: mean and biased variance in exact rationals
+    (fractions), the normalised values from them; the fp64 definition agrees
+    to fp64 rounding, and a constant row gives beta exactly."""
+    from fractions import Fraction
+    import math
+
+    rng = np.random.default_rng(24)
+    M, K = 5, 48
+    xf = (rng.standard_normal((M, K)) * 3.0 + 1.0).astype(np.float32)
+    xf[1] = 0.75
+    x = _bf16(xf)
+    gamma = (0.5 + rng.random(K)).astype(np.float32)
+    beta = (0.2 * rng.standard_normal(K)).astype(np.float32)
+    eps = np.float32(1e-5)
+    r = oracle.layernorm_quant_plain(x, gamma, beta, float(eps))
+    xv = oracle.bf16_to_f32(x)
+    for i in range(M):
+        row = [Fraction(float(v)) for v in xv[i]]
+        mu = sum(row) / K
+        var = sum((v - mu) ** 2 for v in row) / K
+        assert r["mu"][i] == float(mu) and abs(r["var"][i] - float(var)) <= 4e-16 * float(var)
+        sd = math.sqrt(float(var + Fraction(float(eps))))
+        z = [float(v - mu) / sd * float(gamma[j]) + float(beta[j]) for j, v in enumerate(row)]
+        np.testing.assert_allclose(r["z"][i], z, rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(r["z"][1], beta.astype(np.float64))
+
+
+@pytest.mark.parametrize("K,seed", [(256, 25), (2048, 26), (12288, 27)])
+@pytest.mark.parametrize("with_beta", [True, False])
+def test_layernorm_contract_within_bound_of_definition(K, seed, with_beta):
+    """The library's LayerNorm arithmetic (the contract oracle: grid statistics,
+    fp32 normalisation) against the plain fp64 definition, within the bound
+    derived from that arithmetic (tests/ln_bound.py): scales within it, codes
+    equal away from rounding boundaries and within one at them."""
+    import ln_bound
+
+    rng = np.random.default_rng(seed)
+    M = 24
+    out = rng.choice(K, max(1, K // 100), replace=False)
+    xf = rng.standard_normal((M, K)) + 0.25
+    xf[:, out] *= 50.0
+    xf[0] = 1.5
+    xf[2] = 0.0
+    x = _bf16(xf.astype(np.float32))
+    gamma = (0.5 + rng.random(K)).astype(np.float32)
+    gamma[out[0]] = 40.0
+    beta = (0.1 * rng.standard_normal(K)).astype(np.float32) if with_beta else None
+    xq, xs = oracle.layernorm_quant(x, gamma, beta, 1e-5)
+    plain = oracle.layernorm_quant_plain(x, gamma, beta, 1e-5)
+    ln_bound.check(xq, xs, oracle.bf16_to_f32(x).astype(np.float64), gamma, beta, 1e-5, plain)
+
+
+def test_layernorm_bound_rejects_a_wrong_variance():
+    """The bound has teeth: the contract's codes measured against a definition
+    with a planted mistake (unbiased variance, K - 1) fail the check."""
+    import ln_bound
+
+    rng = np.random.default_rng(28)
+    M, K = 16, 64
+    x = _bf16((rng.standard_normal((M, K)) * 2.0).astype(np.float32))
+    gamma = np.ones(K, np.float32)
+    xq, xs = oracle.layernorm_quant(x, gamma, None, 1e-5)
+    wrong = oracle.layernorm_quant_plain(x, gamma, None, 1e-5)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    wrong["var"] = wrong["var"] * K / (K - 1)
+    wrong["z"] = (xf - wrong["mu"][:, None]) / np.sqrt(wrong["var"] + np.float32(1e-5))[:, None]
+    wrong["m"] = np.abs(wrong["z"]).max(axis=1)
+    wrong["q"] = wrong["z"] * (127.0 / wrong["m"])[:, None]
+    wrong["codes"] = np.clip(np.rint(wrong["q"]), -127, 127).astype(np.int8)
+    wrong["scale"] = wrong["m"] / 127
+    with pytest.raises(AssertionError):
+        ln_bound.check(xq, xs, xf, gamma, None, 1e-5, wrong)
+
+
 def test_fold_is_layernorm_times_inverse_factor():
     """LN with (gamma / s, beta / s) is LN(x) diag(s)^-1: against the fp64
     LayerNorm divided by s, codes agree within 1 and scales to fp32 rounding."""
@@ -697,21 +781,24 @@ def test_llm_int8_keeps_accuracy_on_outlier_data(cfg):
     assert e_mixed < 2.0 * e_smooth
 
 
-def test_explainer_demo_shape_smoke():
-    """The explainer page "SmoothQuant大模型平滑量化技术" demonstrates the method on 4 channels x 8
-    tokens of N(3, 1) activations with one value of 200 and N(1, 0.3) weights, at alpha = 0.5, and
-    prints no numbers: a smoke check only (parity unpinned).  Token-major here: X [8 tokens, 4
-    channels], W [4 channels, 4 outputs].  Smoothing brings the activation maximum far below 200,
-    the outlier channel gets the largest factor, and the per-tensor W8A8 product error drops."""
-    rng = np.random.default_rng(42)
-    X = rng.normal(3.0, 1.0, (8, 4)).astype(np.float32)
-    X[3, 2] = 200.0
-    W = rng.normal(1.0, 0.3, (4, 4)).astype(np.float32)
-    ax = oracle.calib_absmax(X)
-    s, inv_s = oracle.smooth_factors(ax, oracle.weight_rowmax(W), 0.5)
-    assert int(np.argmax(s)) == 2
-    Xs = X * inv_s[None, :]
-    assert np.abs(Xs).max() < 200.0 / 4
+def test_outlier_channel_takes_the_largest_factor():
+    """The effect the explainer page "SmoothQuant大模型平滑量化技术" describes, on
+    data of this test's own making: one input channel carries values about 60x
+    the others on every token.  At alpha = 0.5 that channel gets the largest
+    smoothing factor, its smoothed maximum falls to the geometric mean of the
+    two maxima (far below the raw one), and the per-tensor W8A8 error of the
+    product drops.  Direction only: the page prints no values."""
+    rng = np.random.default_rng(7)
+    T, K, N = 32, 12, 6
+    X = rng.standard_normal((T, K)).astype(np.float32)
+    X[:, 5] *= 60.0
+    W = (0.1 * rng.standard_normal((K, N))).astype(np.float32)
+    ax, aw = oracle.calib_absmax(X), oracle.weight_rowmax(W)
+    s, inv_s = oracle.smooth_factors(ax, aw, 0.5)
+    assert int(np.argmax(s)) == 5
+    smoothed_max = np.abs(X * inv_s[None, :]).max(axis=0)
+    np.testing.assert_allclose(smoothed_max, np.sqrt(ax.astype(np.float64) * aw), rtol=1e-6)
+    assert smoothed_max[5] < ax[5] / 10
     y = oracle.matmul_f64(X, W)
     plain = oracle.rel_fro(oracle.w8a8_linear(X, W, None, oracle.PER_TENSOR)["y32"], y)
     smooth = oracle.rel_fro(oracle.w8a8_linear(X, W, 0.5, oracle.PER_TENSOR, calib=X)["y32"], y)
