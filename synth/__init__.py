@@ -165,6 +165,20 @@ def make(cfg: Config | str, device="cpu", M=None, K=None, N=None, calib_chunks=N
     return Inputs(cfg, x, w, calib, out_idx, out_fac)
 
 
+def make_x(cfg: Config | str, device="cpu", variant=0, rows=None, with_outliers=True) -> torch.Tensor:
+    """One more runtime batch x [rows (default M), K] of a configuration, with
+    its outlier channels, from its own stream (``variant`` >= 1 gives batches
+    independent of the one ``make`` draws); no weights, no calibration set."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rows = cfg.M if rows is None else rows
+    out_idx, out_fac = outlier_set(cfg.K, cfg.n_out, cfg.out_lo, cfg.out_hi, (cfg.seed_tag, cfg.K), device)
+    if not with_outliers:
+        out_idx = out_fac = None
+    return activations(rows, cfg.K, cfg.body, out_idx, out_fac, cfg.torch_dtype,
+                       _gen(device, cfg.seed_tag, rows, "extra-x", variant), device)
+
+
 def to_numpy(t: torch.Tensor):
     """Host numpy view for the oracle: fp32 stays fp32, bf16 becomes uint16 bits."""
     t = t.detach().to("cpu").contiguous()
