@@ -42,9 +42,11 @@
  *     current device) and returns after enqueueing.  Buffers must stay valid
  *     until the stream's work completes.  Calls on one stream are ordered.
  *   - The caller owns all memory.  The library allocates nothing.  Its only
- *     mutable global state is a per-thread error message and a per-device
- *     cache of the compute-unit count (filled on first use, read and written
- *     atomically; the GEMM's launch shape depends on it).
+ *     mutable global state is a per-thread error message, a per-device cache
+ *     of the compute-unit count (filled on first use, read and written
+ *     atomically; the GEMM's launch shape depends on it), and the static
+ *     scratch array of sq_quant_weight_noalloc with its per-device address
+ *     cache (see there).
  *   - Arguments are validated before anything is enqueued; a failed check
  *     returns a negative sq_status, enqueues nothing and records a message for
  *     sq_last_error().  A launch failure returns SQ_ERR_HIP.
@@ -155,6 +157,27 @@ sq_status sq_smooth_factors(const float *amax_x, const void *w, sq_dtype wt, int
 sq_status sq_quant_weight(const void *w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
                           const float *s, int8_t *wq, float *w_scale, void *ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/*
+ * sq_quant_weight without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the per-column maxima live in a static scratch array
+ * of the library instead of `ws`.  Same arguments (less ws) and the same
+ * results as sq_quant_weight.
+ *
+ *   Limit: N <= 65536 output channels (the scratch holds 65536 maxima, 256 KB
+ *   per GPU, kept until the process ends); larger N returns SQ_ERR_WORKSPACE
+ *   and enqueues nothing.
+ *   The scratch is one array per device, shared by every call on that device
+ *   and cleared at the start of each call by a fill kernel (no memset, no
+ *   allocation): calls that overlap on one device race, so serialize them (one
+ *   stream, or events between streams).  `stream` must belong to the current
+ *   device (SQ_ERR_INVALID_ARG otherwise).  The first call on a device looks up
+ *   the scratch's device address (hipGetSymbolAddress, no allocation) and
+ *   caches it; a failure there returns SQ_ERR_HIP.
+ */
+sq_status sq_quant_weight_noalloc(const void *w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw, const float *s,
+                                  int8_t *wq, float *w_scale, hipStream_t stream);
 
 /*
  * Steps 2 and 3 in one call -- the offline weight preparation (page "4.2 W8A8

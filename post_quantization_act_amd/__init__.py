@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "SqError", "SQ_F32", "SQ_BF16", "SQ_PER_TOKEN", "SQ_PER_TENSOR",
     "SQ_OP_CALIB_ABSMAX", "SQ_OP_SMOOTH_FACTORS", "SQ_OP_QUANT_WEIGHT", "SQ_OP_QUANT_ACT", "SQ_OP_GEMM_W8A8",
-    "lib", "lib_path", "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act",
+    "lib", "lib_path", "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight",
+    "sq_quant_weight_noalloc", "sq_quant_act",
     "sq_gemm_w8a8", "sq_prepare_weights", "sq_prepare_and_quant_act", "SQ_OP_PREPARE_WEIGHTS",
     "SQ_OP_PREPARE_AND_QUANT_ACT", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
     "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier",
@@ -36,8 +37,8 @@ SQ_PER_TOKEN, SQ_PER_TENSOR = 0, 1
  SQ_OP_PREPARE_AND_QUANT_ACT) = range(7)
 
 EXPORTED_SYMBOLS = (
-    "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
-    "sq_prepare_weights", "sq_prepare_and_quant_act", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
+    "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight", "sq_quant_weight_noalloc",
+    "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights", "sq_prepare_and_quant_act", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
     "sq_gather_outliers", "sq_gemm_w8a8_outlier", "sq_workspace_size", "sq_status_str", "sq_last_error",
     "sq_version", "sq_gemm_kernel_name", "sq_gemm_outlier_kernel_name",
 )
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
     L.sq_calib_reset.argtypes = [vp, i64, vp]
     L.sq_smooth_factors.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp]
     L.sq_quant_weight.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, sz, vp]
+    L.sq_quant_weight_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp]
     L.sq_quant_act.argtypes = [vp, i32, i64, i64, i64, vp, i32, vp, vp, vp, sz, vp]
     L.sq_gemm_w8a8.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, i32, vp, vp, sz, vp]
     L.sq_prepare_weights.argtypes = [vp, vp, i32, i64, i64, i64, f32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -82,7 +84,8 @@ def lib() -> ctypes.CDLL:
     L.sq_outlier_columns.argtypes = [vp, i64, f32, vp, vp, vp, vp]
     L.sq_gather_outliers.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp, i64, vp, vp, vp]
     L.sq_gemm_w8a8_outlier.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, vp, vp, i32, vp]
-    for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_act", "sq_gemm_w8a8",
+    for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_weight_noalloc", "sq_quant_act",
+              "sq_gemm_w8a8",
               "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
               "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier"):
         getattr(L, f).restype = ctypes.c_int
@@ -233,6 +236,19 @@ def sq_quant_weight(w: torch.Tensor, s: torch.Tensor | None, wq: torch.Tensor, w
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().sq_quant_weight(_ptr(w), _dtype(w), K, N, ld, _ptr(s), _ptr(wq), _ptr(w_scale), _ptr(ws), nbytes,
                                  _stream(_dev(w), stream)))
+
+
+def sq_quant_weight_noalloc(w: torch.Tensor, s: torch.Tensor | None, wq: torch.Tensor, w_scale: torch.Tensor,
+                            stream=None) -> None:
+    """sq_quant_weight with the library's static scratch instead of a workspace (N <= 65536; calls on one
+    device must not overlap)."""
+    K, N, ld = _rows(w)
+    _dense(wq, "wq", (N, K), torch.int8)
+    _dense(w_scale, "w_scale", (N,), torch.float32)
+    if s is not None:
+        _dense(s, "s", (K,), torch.float32)
+    _check(lib().sq_quant_weight_noalloc(_ptr(w), _dtype(w), K, N, ld, _ptr(s), _ptr(wq), _ptr(w_scale),
+                                         _stream(_dev(w), stream)))
 
 
 def sq_prepare_weights(amax_x: torch.Tensor, w: torch.Tensor, alpha: float, s: torch.Tensor, inv_s: torch.Tensor,

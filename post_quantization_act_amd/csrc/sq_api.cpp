@@ -196,6 +196,47 @@ sq_status sq_quant_weight(const void* w, sq_dtype wt, int64_t K, int64_t N, int6
     return hip_result(e, fn);
 }
 
+sq_status sq_quant_weight_noalloc(const void* w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw, const float* s,
+                                  int8_t* wq, float* w_scale, hipStream_t stream) {
+    const char* fn = "sq_quant_weight_noalloc";
+    SQ_TRY(check_k(fn, K));
+    if (N > sqk::noalloc_scratch_cols())
+        return fail(SQ_ERR_WORKSPACE, "%s: N = %lld output channels exceed the %lld of the library's static scratch",
+                    fn, (long long)N, (long long)sqk::noalloc_scratch_cols());
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
+    if (s) SQ_TRY(check_vec(fn, "s", s, K));
+    SQ_TRY(check_vec(fn, "w_scale", w_scale, N, true));
+    if (K > 0 && N > 0) {
+        if (!wq) return fail(SQ_ERR_INVALID_ARG, "%s: wq is NULL", fn);
+        if (!aligned16(wq)) return fail(SQ_ERR_INVALID_ARG, "%s: wq is not 16-byte aligned", fn);
+    }
+    if (N == 0) return ok();
+    if (K == 0)  // no input channels: every column max is 0, so every scale is 0
+        return hip_result(sqk::launch_fill_u32(reinterpret_cast<uint32_t*>(w_scale), N, 0u, stream), fn);
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_result(e, fn);
+    if (stream) {
+        int sdev = 0;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return hip_result(e, fn);
+        if (sdev != dev)
+            return fail(SQ_ERR_INVALID_ARG, "%s: the stream belongs to device %d, the current device is %d", fn, sdev,
+                        dev);
+    }
+    void* scratch = nullptr;
+    e = sqk::noalloc_scratch(dev, &scratch);
+    if (e != hipSuccess) return fail(SQ_ERR_HIP, "%s: no device address of the static scratch: %s", fn,
+                                     hipGetErrorString(e));
+    // the same three launches as sq_quant_weight, with the static scratch as
+    // the column maxima (cleared first: it keeps the previous call's values)
+    uint32_t* colmax = static_cast<uint32_t*>(scratch);
+    e = sqk::launch_fill_u32(colmax, N, 0u, stream);
+    if (e == hipSuccess) e = sqk::launch_col_absmax(w, wt == SQ_BF16, K, N, ldw, s, colmax, stream);
+    if (e == hipSuccess) e = sqk::launch_quant_weight(w, wt == SQ_BF16, K, N, ldw, s, colmax, wq, w_scale, stream);
+    return hip_result(e, fn);
+}
+
 sq_status sq_prepare_weights(const float* amax_x, const void* w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
                              float alpha, float* s, float* inv_s, float* amax_w, int8_t* wq, float* w_scale, void* ws,
                              size_t ws_bytes, hipStream_t stream) {

@@ -74,6 +74,13 @@ hipError_t launch_gemm_w8a8_outlier(const int8_t* xq, const float* x_scale, cons
                                     int64_t M, int64_t N, int64_t K, const uint16_t* x_o, const uint16_t* w_ot,
                                     int64_t kp, const int32_t* count, void* y, bool y_bf16, hipStream_t st);
 
+// The static scratch of sq_quant_weight_noalloc: room for noalloc_scratch_cols()
+// column maxima; noalloc_scratch() gives its device address on `device`, which
+// must be the current device (taken with hipGetSymbolAddress on the first call
+// per device, then cached).
+int64_t noalloc_scratch_cols();
+hipError_t noalloc_scratch(int device, void** out);
+
 // Static description of the GEMM kernel launch_gemm_w8a8 (outl: the outlier
 // variant) runs for this shape.
 const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl = false);

@@ -144,6 +144,17 @@ def test_quant_weight_rejects():
     _expect(L.sq_quant_weight(FAKE, sq.SQ_BF16, 33, 64, 64, FAKE, FAKE, FAKE, FAKE, 4096, None), -1, "K = 33")
 
 
+def test_quant_weight_noalloc_rejects():
+    """Beyond the 65536 columns of the static scratch, and the usual argument
+    checks, all before the scratch's device address is looked up."""
+    L = _L()
+    _expect(L.sq_quant_weight_noalloc(FAKE, sq.SQ_BF16, 32, 65537, 65537, FAKE, FAKE, FAKE, None), -3,
+            "static scratch")
+    _expect(L.sq_quant_weight_noalloc(FAKE, sq.SQ_BF16, 32, 64, 64, FAKE, MISALIGNED, FAKE, None), -1, "wq")
+    _expect(L.sq_quant_weight_noalloc(FAKE, sq.SQ_BF16, 33, 64, 64, FAKE, FAKE, FAKE, None), -1, "K = 33")
+    _expect(L.sq_quant_weight_noalloc(None, sq.SQ_BF16, 32, 64, 64, FAKE, FAKE, FAKE, None), -1, "w is NULL")
+
+
 def test_quant_act_rejects():
     L = _L()
     _expect(L.sq_quant_act(FAKE, sq.SQ_BF16, 4, 32, 32, FAKE, 5, FAKE, FAKE, None, 0, None), -2, "granularity")
