@@ -134,7 +134,15 @@ def _tops(us, ops, **extra):
 
 class _Timer:
     """Per-call durations from HIP events recorded on the current stream (the
-    stream the library launches on); returns the median in microseconds."""
+    stream the library launches on); returns the median in microseconds.
+
+    The timed calls are enqueued behind a spin kernel of about 20 ms, so the
+    host has queued them all before the GPU reaches them: each event interval
+    is then the call's device time (its kernels and the gaps between them),
+    not the host's launch overhead, which exceeds the device time of the short
+    calls."""
+
+    SPIN_CYCLES = 40_000_000
 
     def __init__(self, torch, runs):
         self.torch = torch
@@ -148,6 +156,7 @@ class _Timer:
         torch.cuda.synchronize()
         s = torch.cuda.current_stream()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+        torch.cuda._sleep(self.SPIN_CYCLES)
         for i, (a, b) in enumerate(evs):
             a.record(s)
             fn(warm + i)
