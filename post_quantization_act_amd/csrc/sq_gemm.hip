@@ -52,9 +52,9 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1)
 
 // Output tile renumbering: blocks are dealt round-robin to the 8 XCDs, so give
 // each XCD a contiguous run of virtual tile ids, then walk them in groups of
-// `group_m` tile rows (m-major inside a group).
-__device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int group_m, int& tn, int& tm) {
-    const int b = blockIdx.x, nb = gridDim.x;
+// `group_m` tile rows (m-major inside a group).  tile_of: the tile of block b
+// in a launch of nb blocks (one tile per block).
+__device__ __forceinline__ void tile_of(int b, int nb, int tiles_n, int tiles_m, int group_m, int& tn, int& tm) {
     const int xcd = b % 8, l = b / 8, per = nb / 8, rem = nb % 8;
     const int v = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + l;
     const int group = group_m * tiles_n;
@@ -63,6 +63,9 @@ __device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int grou
     const int r = v % group;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+__device__ __forceinline__ void tile_of_block(int tiles_n, int tiles_m, int group_m, int& tn, int& tm) {
+    tile_of(blockIdx.x, gridDim.x, tiles_n, tiles_m, group_m, tn, tm);
 }
 
 // The 16-bit half of the LLM.int8()-style product (page "4.2 W8A8 量化与
@@ -451,6 +454,207 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_ring(const int8_t* __re
     }
     epilogue<TN, TM, kOut, kAcc, kO>(acc, n0 + wn * WN, m0 + wm * WM, lane, x_scale, xs_step, w_scale, M, N, ldy, y,
                                      acc_out, op);
+}
+
+// ---- persistent ring kernel: tiles walked per block, epilogue overlapped ----------
+//
+// The deployed product (bf16 output through the LDS epilogue, N % 8 == 0, no
+// accumulator store, K % (128 NS) == 0) over many rounds of tiles.  The grid is
+// one block per CU (a multiple of 8, so block p stays on XCD p % 8); block p
+// computes the tiles blocks p, p + G, p + 2G, ... of the one-tile-per-block
+// launch would, in that order.  Within a tile the main loop is k_gemm_ring's.
+// Between tiles the next tile's first stage and its scales are copied while the
+// current tile finishes: its stage 0 goes into the ring buffer freed two stages
+// before the end (in the last two iterations, as a regular stage would), its
+// scales into the other half of a double-buffered scale area; the epilogue
+// stages its outputs in the buffer of the last stage (free once every
+// wavefront passed the last iteration's barrier); after a barrier the next
+// tile's stage 1 follows.  So the CU streams the next tile's operands while it
+// dequantizes and stores, instead of waiting for them at the start of every
+// tile.
+template <int BN, int BM, int WGN, int WGM, int NS>
+__global__ __launch_bounds__(64 * WGN * WGM) void k_gemm_persist(
+    const int8_t* __restrict__ xq, const float* __restrict__ x_scale, int xs_step, const int8_t* __restrict__ wq,
+    const float* __restrict__ w_scale, int M, int N, int K, uint16_t* __restrict__ y, int ldy, int tiles_n,
+    int tiles_m, int group_m, int ntiles) {
+    constexpr int NW = WGN * WGM;
+    constexpr int WN = BN / WGN, WM = BM / WGM, TN = WN / 32, TM = WM / 32;
+    constexpr int ROWS = BN + BM, STAGE = ROWS * 8, COPIES = ROWS / 8, L = COPIES / NW;
+    constexpr int NMF = TN * TM, NRD = TN + TM;
+    constexpr int DR = (NRD + NMF - 1) / NMF, DD = (L + NMF - 1) / NMF;
+    constexpr int PARTS = (NS >= 3 && L % 3 == 0) ? 3 : (L % 2 == 0 ? 2 : 1);
+    constexpr int LP = L / PARTS;
+    constexpr int SC = BN + BM;  // scales per tile
+    static_assert(COPIES % NW == 0 && WN % 32 == 0 && WM % 32 == 0, "tile");
+    static_assert(BN % 64 == 0 && BM % 64 == 0 && (SC / 64) % NW == 0 || SC / 64 < NW, "scale staging");
+    static_assert(NS * STAGE * 16 + 2 * SC * 4 <= 160 * 1024, "LDS");
+    static_assert(NW * 32 * (WN + 8) * 2 <= STAGE * 16, "the epilogue's staging fits one ring buffer");
+    __shared__ uint4 lds[NS * STAGE];
+    __shared__ __align__(16) float scl[2 * SC];
+
+    const int lane = threadIdx.x % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int wn = wave % WGN, wm = wave / WGN;
+    const int fr = lane % 32, fh = lane / 32;
+    const int nk = K / kBK;
+    const int G = gridDim.x;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char*)lds;
+    const uint32_t scl0 = (uint32_t)(uintptr_t)(lds_char*)scl;
+
+    // Copy j of a stage fills rows 8i .. 8i+7 (i = wave + NW j): lane -> row
+    // 8i + lane/8 = r0 + 8 NW j, LDS chunk lane%8 holding logical chunk
+    // (lane%8) ^ ((row>>1)&7), which is the same for every j (8 NW j is a
+    // multiple of 16).  Source offsets are formed per copy from r0 and that
+    // chunk; rows past the edge are clamped (read, never stored).
+    static_assert((8 * NW) % 16 == 0, "one chunk swizzle per wavefront");
+    const int r0 = 8 * wave + lane / 8;
+    const uint32_t cb = (uint32_t)(((lane % 8) ^ ((r0 >> 1) & 7)) * 16);
+    auto copy_from = [&](int tn0, int tm0, int st, int j) {  // stage st of the tile at (tn0, tm0), copy j
+        const int i = wave + NW * j;
+        const int r = r0 + 8 * NW * j;
+        const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + ((st % NS) * STAGE + i * 64) * 16);
+        const uint32_t row = 8 * i < BN ? (uint32_t)min(tn0 + r, N - 1) : (uint32_t)min(tm0 + r - BN, M - 1);
+        copy16_to_lds(8 * i < BN ? wq : xq, row * (uint32_t)K + cb + (uint32_t)st * kBK, la);
+    };
+    // The tile's w_scale rows then x_scale rows into scale buffer `half`.
+    auto copy_scales = [&](int n0, int m0, int half) {
+#pragma unroll
+        for (int c0 = 0; c0 < SC / 64; c0 += NW) {
+            const int c = c0 + wave;  // 64 scales per copy
+            if (c < SC / 64) {
+                const int r = c * 64 + lane;
+                const uint32_t la = __builtin_amdgcn_readfirstlane(scl0 + (half * SC + c * 64) * 4);
+                if (c * 64 < BN)
+                    copy4_to_lds(w_scale, (uint32_t)min(n0 + r, N - 1) * 4u, la);
+                else
+                    copy4_to_lds(x_scale, (uint32_t)(min(m0 + r - BN, M - 1) * xs_step) * 4u, la);
+            }
+        }
+    };
+
+    int tn, tm;
+    int vb = blockIdx.x;
+    tile_of(vb, ntiles, tiles_n, tiles_m, group_m, tn, tm);
+    int n0 = tn * BN, m0 = tm * BM;
+    int n0n = 0, m0n = 0;
+
+    v16i acc[TN][TM];
+    v4i fa[2][TN], fb[2][TM];
+    auto read_frag = [&](int buf, int ks, int q, int sl) {
+        const uint4* base = lds + buf * STAGE;
+        const int c = 2 * ks + fh;
+        if (q < TN) {
+            const uint4 u = base[swz(wn * WN + q * 32 + fr, c)];
+            fa[sl][q] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+        } else {
+            const uint4 u = base[swz(BN + wm * WM + (q - TN) * 32 + fr, c)];
+            fb[sl][q - TN] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+        }
+    };
+    // Copy j of "stage" st of the ring: st < nk is this tile's stage st, st == nk
+    // the next tile's stage 0 (when there is one); later ones are issued after
+    // the epilogue.
+    bool has_next = false;
+    auto copy = [&](int st, int j) {
+        if (st < nk) copy_from(n0, m0, st, j);
+        else if (st == nk && has_next) copy_from(n0n, m0n, 0, j);
+    };
+    auto kstep = [&](int sl, bool rd, int rbuf, int rks, int rsl, bool cp, int ckt, int c_lo, int c_hi) {
+        const int cn = c_hi - c_lo, cper = (cn + NMF - 1) / NMF;
+#pragma unroll
+        for (int j = 0; j < NMF; ++j) {
+            const int a = j / TM, b = j % TM;
+            acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[sl][a], fb[sl][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < DR; ++u)
+                if (rd && j * DR + u < NRD) read_frag(rbuf, rks, j * DR + u, rsl);
+#pragma unroll
+            for (int u = 0; u < DD; ++u)
+                if (cp && u < cper && j * cper + u < cn) copy(ckt, c_lo + j * cper + u);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // Prologue of the first tile: its scales and stages 0 .. NS-1.
+    copy_scales(n0, m0, 0);
+#pragma unroll
+    for (int st = 0; st < NS; ++st)
+#pragma unroll
+        for (int j = 0; j < L; ++j) copy_from(n0, m0, st, j);
+    wait_vmcnt<L*(NS - 1)>();
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < NRD; ++q) read_frag(0, 0, q, 0);
+
+    for (int it = 0;; ++it) {
+        const int vbn = vb + G;
+        has_next = vbn < ntiles;
+        if (has_next) {
+            int tnn, tmn;
+            tile_of(vbn, ntiles, tiles_n, tiles_m, group_m, tnn, tmn);
+            n0n = tnn * BN;
+            m0n = tmn * BM;
+        }
+#pragma unroll
+        for (int a = 0; a < TN; ++a)
+#pragma unroll
+            for (int b = 0; b < TM; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[a][b][e] = 0;
+
+        // The ring position restarts at buffer 0 with every tile (nk % NS == 0).
+        int kt = 0, buf = 0;
+        for (; kt + NS < nk; ++kt) {
+            const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+            const bool late = kt > 0;
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(0, true, buf, 1, 1, late && PARTS > 1, kt - 1 + NS, LP, 2 * LP);
+            kstep(1, true, buf, 2, 0, late && PARTS > 2, kt - 1 + NS, 2 * LP, 3 * LP);
+            kstep(0, true, buf, 3, 1, false, 0, 0, 0);
+            wait_vmcnt<L*(NS - 2)>();
+            lds_barrier();
+            kstep(1, true, nbuf, 0, 0, true, kt + NS, 0, LP);
+            buf = nbuf;
+        }
+        // The last NS iterations: the stages after the last one are the next
+        // tile's stage 0 (copied here) and its stage 1 .. (after the epilogue).
+        for (; kt < nk; ++kt) {
+            const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+            const bool late = kt > 0;
+            __builtin_amdgcn_sched_barrier(0);
+            kstep(0, true, buf, 1, 1, late && PARTS > 1, kt - 1 + NS, LP, 2 * LP);
+            kstep(1, true, buf, 2, 0, late && PARTS > 2, kt - 1 + NS, 2 * LP, 3 * LP);
+            kstep(0, true, buf, 3, 1, false, 0, 0, 0);
+            if (kt + 1 < nk) wait_vmcnt<0>();  // the tile's last stage has landed (nothing newer is in flight)
+            lds_barrier();                        // in the last iteration: every read of the last buffer is done
+            if (kt + NS == nk && has_next) copy_scales(n0n, m0n, (it + 1) & 1);
+            kstep(1, kt + 1 < nk, nbuf, 0, 0, kt + NS == nk, kt + NS, 0, LP);
+            buf = nbuf;
+        }
+        // Epilogue: outputs staged in the buffer of the last stage, scales from
+        // this tile's half of the scale area.
+        {
+            uint16_t* ldsw = reinterpret_cast<uint16_t*>(lds + ((nk - 1) % NS) * STAGE) + wave * 32 * (WN + 8);
+            const float* sc = scl + (it & 1) * SC;
+            epilogue_bf16_lds<TN, TM>(acc, n0 + wn * WN, m0 + wm * WM, lane, sc + BN + wm * WM, sc + wn * WN, M, N,
+                                      ldy, y, ldsw);
+        }
+        if (!has_next) break;
+        // Every wavefront is done with its staging region: the next tile's
+        // stages 1 .. NS-1 may overwrite the ring.
+        lds_barrier();
+#pragma unroll
+        for (int st = 1; st < NS; ++st)
+#pragma unroll
+            for (int j = 0; j < L; ++j) copy_from(n0n, m0n, st, j);
+        wait_vmcnt<L*(NS - 1)>();  // stage 0 and the scales of the next tile (and the stores before them)
+        lds_barrier();
+        vb = vbn;
+        n0 = n0n;
+        m0 = m0n;
+#pragma unroll
+        for (int q = 0; q < NRD; ++q) read_frag(0, 0, q, 0);
+    }
 }
 
 // ---- generic kernel: any K % 16 == 0 -------------------------------------------
@@ -979,6 +1183,24 @@ static void launch_ring(const int8_t* xq, const float* x_scale, bool per_tensor,
     });
 }
 
+// The 256 x 256 product through the persistent kernel when the call is the
+// deployed one (bf16 output, no accumulator store, no outlier addend, N and
+// the output stride multiples of 8, K a multiple of 256); returns false (and
+// launches nothing) otherwise.  Columns [n0, n0 + N) as launch_ring.
+static bool launch_persist256(const int8_t* xq, const float* x_scale, bool per_tensor, const int8_t* wq,
+                              const float* w_scale, int M, int N, int K, void* y, bool y_bf16, int32_t* acc_out,
+                              const OutlierOps* op, int group_m, hipStream_t st, int n0 = 0, int ldy = -1) {
+    if (ldy < 0) ldy = N;
+    if (!y_bf16 || acc_out || op || N % 8 != 0 || ldy % 8 != 0 || K % 256 != 0 || K < 256) return false;
+    const int tiles_n = (N + 255) / 256, tiles_m = (M + 255) / 256, ntiles = tiles_n * tiles_m;
+    const int cus = (int)std::max<int64_t>(8, device_cu_count() / 8 * 8);
+    const int grid = std::min(ntiles, cus);
+    hipLaunchKernelGGL((k_gemm_persist<256, 256, 4, 2, 2>), dim3((unsigned)grid), dim3(512), 0, st, xq, x_scale,
+                       per_tensor ? 0 : 1, wq + (int64_t)n0 * K, w_scale + n0, M, N, K,
+                       static_cast<uint16_t*>(y) + n0, ldy, tiles_n, tiles_m, group_m, ntiles);
+    return true;
+}
+
 // Which kernel a product of this shape runs (the one rule both the launcher
 // and gemm_kernel_name use).
 enum class GemmPath { kNone, kDecodeRing, kDecode, kRing256, kRing256Split, kRing256x128, kRing128, kGeneric };
@@ -1055,13 +1277,15 @@ static hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool per_t
             launch_decode(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, st);
             break;
         case GemmPath::kRing256:
-            launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 4,
-                                           st);
+            if (!launch_persist256(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 4, st))
+                launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op,
+                                               4, st);
             break;
         case GemmPath::kRing256Split: {
             const int n1 = (int)ring256_split_cols(M64, N64, device_cu_count());
-            launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, n1, K, y, y_bf16, acc_out, op, 4,
-                                           st, 0, N);
+            if (!launch_persist256(xq, x_scale, per_tensor, wq, w_scale, M, n1, K, y, y_bf16, acc_out, op, 4, st, 0, N))
+                launch_ring<256, 256, 4, 2, 2>(xq, x_scale, per_tensor, wq, w_scale, M, n1, K, y, y_bf16, acc_out, op,
+                                               4, st, 0, N);
             launch_ring<256, 128, 4, 2, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N - n1, K, y, y_bf16, acc_out, op,
                                            8, st, n1, N);
             break;
