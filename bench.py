@@ -395,8 +395,8 @@ def _judged_decode(torch, sq, synth, pipeline, dev, tm):
         sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, wqs[i % n], b.w_scale, b.y)
 
     out["quant_act_then_gemm"] = _rate(tm(both), stream_bytes + 2 * M * K + 4 * K,
-                                       note="steps 4 + 5 of one decode token batch (two calls), the weight-stream "
-                                            "rate of the pair")
+                                       note="steps 4 + 5 of one decode token batch as two calls (sq_quant_act, "
+                                            "sq_gemm_w8a8), the weight-stream rate of the pair")
     del wqs, inp, b
     torch.cuda.empty_cache()
     return out

@@ -900,18 +900,20 @@ __global__ __launch_bounds__(256) void k_gemm_decode(const int8_t* __restrict__ 
 // the SPW = K / 2048 chunks of 128 k-bytes that start at byte 2048 sp + 128 w,
 // sp < SPW (so at stage sp the 16 wavefronts read one contiguous 2 KB of every
 // row of the group), and keeps the token operand of those chunks in registers
-// for the whole kernel.  Work items
-// are groups of 16 output channels, dealt round-robin to the blocks.  A stage
-// is 16 weight rows x 128 bytes, copied by two global_load_lds_dwordx4 (8 rows
-// x 128 bytes each, nontemporal: the stream is read once) into the
-// wavefront's own three-stage LDS ring; chunk c of row r sits at slot
-// 8 r + (c ^ ((r >> 1) & 7)), so the MFMA fragment reads are conflict-free.
-// No workgroup barrier guards the rings (each is private to a wavefront);
-// only explicit vmcnt waits do, and no other vector-memory instruction runs
-// during the stream: scales are staged in LDS first, the 16 partial tiles of
-// a group are summed through LDS and kept there as int32, and the epilogue
-// and all stores run after the last stage.
+// for the whole kernel.  Work items are groups of 16 output channels, dealt
+// round-robin to the blocks.  A stage is 16 weight rows x 128 bytes, copied by
+// two global_load_lds_dwordx4 (8 rows x 128 bytes each, nontemporal: the
+// stream is read once) into the wavefront's own NST-stage LDS ring; chunk c of
+// row r sits at slot 8 r + (c ^ ((r >> 1) & 7)), so the MFMA fragment reads
+// are conflict-free.  No workgroup barrier guards the rings (each is private
+// to a wavefront); only explicit vmcnt waits do, and no other vector-memory
+// instruction runs during the stream: scales are staged in LDS first, the 16
+// partial tiles of a group are summed through LDS by one wavefront, which
+// keeps the int32 sum in registers, and the epilogue and all stores run after
+// the last stage.
+
 constexpr int kDrWaves = 16, kDrStages = 3, kDrStageBytes = 128, kDrMaxGroups = 24;
+constexpr int kDrSums = (kDrMaxGroups + kDrWaves - 1) / kDrWaves;  // groups summed per wavefront
 
 __device__ __forceinline__ void copy16_to_lds_nt(const int8_t* base, uint32_t voff, uint32_t lds_off) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
@@ -933,7 +935,6 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
     constexpr int KS = SB / 64;      // MFMA k-steps per stage
     __shared__ uint4 ring_all[NW * NST * SLOTS];
     __shared__ v4i part[NW * 64];
-    __shared__ v4i sums[kDrMaxGroups * 64];
     __shared__ __align__(16) float wsl[kDrMaxGroups * 16];
     __shared__ float xsl[16];
     auto h = [](int r) { return (r >> 1) & 7; };
@@ -944,30 +945,6 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
     // k-chunks of this wavefront: stage sp covers bytes sp * NW * SB + wave * SB .. + SB of the rows, so
     // at each stage the 16 wavefronts read one contiguous NW * SB bytes of every row of the group
     auto kofs = [&](int sp) { return sp * (NW * SB) + wave * SB; };
-
-    // token operand: lane l holds token l % 16, 16-byte chunk l / 16 of each 64-byte k-step
-    v4i xb[SPW][KS];
-    {
-        const int8_t* xr = xq + (int64_t)min(lane % 16, M - 1) * K + 16 * (lane / 16);
-#pragma unroll
-        for (int sp = 0; sp < SPW; ++sp)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const uint4 u = ld16(xr + kofs(sp) + s * 64);
-                xb[sp][s] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
-            }
-        // consume them here so the compiler's own waits for these loads come
-        // before the stream and never inside it
-#pragma unroll
-        for (int sp = 0; sp < SPW; ++sp)
-#pragma unroll
-            for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(xb[sp][s]));
-    }
-    for (int i = threadIdx.x; i < ngroups * 16; i += 64 * NW) {
-        const int g = (int)blockIdx.x + (i / 16) * (int)gridDim.x;
-        wsl[i] = w_scale[min(16 * g + i % 16, N - 1)];
-    }
-    if (threadIdx.x < 16) xsl[threadIdx.x] = x_scale[min((int)threadIdx.x, M - 1) * xs_step];
 
     const uint32_t ring = (uint32_t)(uintptr_t)(lds_char*)(ring_all + wave * NST * SLOTS);
     const int rr = lane / CPR, cl = lane % CPR;
@@ -984,12 +961,41 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
             copy16_to_lds_nt(wq, off, la + i * 1024);
         }
     };
+    // the weight stream starts first; the token operand loads while its first stages are in flight
 #pragma unroll
     for (int t = 0; t < NST - 1; ++t)
         if (t < T) issue(t);
+
+    // token operand: lane l holds token l % 16, 16-byte chunk l / 16 of each 64-byte k-step
+    v4i xb[SPW][KS];
+    {
+        const int8_t* xr = xq + (int64_t)min(lane % 16, M - 1) * K + 16 * (lane / 16);
+#pragma unroll
+        for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint4 u = ld16(xr + kofs(sp) + s * 64);
+                xb[sp][s] = v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w};
+            }
+        if (threadIdx.x < 16) xsl[threadIdx.x] = x_scale[min((int)threadIdx.x, M - 1) * xs_step];
+    }
+    // consume the operand here so the compiler's own waits for these loads come
+    // before the stream and never inside it
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(xb[sp][s]));
+    for (int i = threadIdx.x; i < ngroups * 16; i += 64 * NW) {
+        const int g = (int)blockIdx.x + (i / 16) * (int)gridDim.x;
+        wsl[i] = w_scale[min(16 * g + i % 16, N - 1)];
+    }
     wait_vmcnt<0>();
+    __syncthreads();  // the staged scales
 
     v4i acc = {0, 0, 0, 0};
+    v4i sums[kDrSums];
+#pragma unroll
+    for (int q = 0; q < kDrSums; ++q) sums[q] = v4i{0, 0, 0, 0};
     const int fr = lane % 16, fc = lane / 16;
     for (int gi = 0; gi < ngroups; ++gi) {
 #pragma unroll
@@ -1011,7 +1017,7 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
 #pragma unroll
             for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[s], xb[sp][s], acc, 0, 0, 0);
         }
-        // group done: the 16 partial tiles are summed by one wavefront
+        // group done: the 16 partial tiles are summed by wavefront gi % NW
         part[wave * 64 + lane] = acc;
         acc = v4i{0, 0, 0, 0};
         lds_barrier();
@@ -1019,20 +1025,25 @@ __global__ __launch_bounds__(64 * kDrWaves) void k_gemm_decode_ring(
             v4i sum = part[lane];
 #pragma unroll
             for (int w = 1; w < NW; ++w) sum += part[w * 64 + lane];
-            sums[gi * 64 + lane] = sum;
+#pragma unroll
+            for (int q = 0; q < kDrSums; ++q)
+                if (gi / NW == q) sums[q] = sum;
         }
         lds_barrier();  // part is reused by the next group
     }
 
-    // epilogue: 16x16 accumulator layout, lane l holds channels 4 (l / 16) + e of token l % 16
-    for (int idx = threadIdx.x; idx < ngroups * 64; idx += 64 * NW) {
-        const int gi = idx / 64, l = idx % 64;
+    // epilogue: wavefront w stores the groups gi = w + NW q; 16x16 accumulator
+    // layout, lane l holds channels 4 (l / 16) + e of token l % 16
+#pragma unroll
+    for (int q = 0; q < kDrSums; ++q) {
+        const int gi = wave + NW * q;
+        if (gi >= ngroups) break;
         const int g = (int)blockIdx.x + gi * (int)gridDim.x;
-        const int m = l % 16, n = 16 * g + 4 * (l / 16);
+        const int m = lane % 16, n = 16 * g + 4 * (lane / 16);
         if (m >= M || n >= N) continue;
-        const v4i sum = sums[idx];
+        const v4i sum = sums[q];
         const float xs = xsl[m];
-        const float* ws = wsl + gi * 16 + 4 * (l / 16);
+        const float* ws = wsl + gi * 16 + 4 * (lane / 16);
         const int64_t off = (int64_t)m * N + n;
         if (n + 3 < N && N % 4 == 0) {
             const float y0 = ((float)sum[0] * xs) * ws[0], y1 = ((float)sum[1] * xs) * ws[1];
