@@ -187,8 +187,7 @@ sq_status sq_quant_weight_noalloc(const void *w, sq_dtype wt, int64_t K, int64_t
  * Computes exactly what sq_smooth_factors(amax_x, w, ..., alpha, s, inv_s,
  * amax_w) followed by sq_quant_weight(w, ..., s, wq, w_scale, ...) compute,
  * with the same arguments and results.  For a bf16 W with 16-byte aligned
- * rows, N % 8 == 0, N <= 49152 when alpha is 0, 1/2 or 1 and N <= 32768
- * otherwise, it reads W once less: one pass over W
+ * rows, N % 8 == 0 and N <= 49152, it reads W once less: one pass over W
  * yields the row maxima, the factors and the column maxima of diag(s) W, and
  * a second pass writes the codes.  Other inputs take the two-call sequence
  * internally.

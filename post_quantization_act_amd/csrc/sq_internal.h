@@ -19,7 +19,7 @@ hipError_t launch_row_absmax_factors(const void* w, bool bf16, int64_t K, int64_
                                      hipStream_t st);
 
 // Steps 2 + 3a in one read of W (bf16, 16-byte aligned rows, N % 8 == 0,
-// N <= 49152 for alpha in {0, 1/2, 1}, N <= 32768 otherwise): amax_w (optional), s, inv_s and the column maxima of diag(s) W
+// N <= 49152): amax_w (optional), s, inv_s and the column maxima of diag(s) W
 // into colmax (fp32 bits), through per-block partial maxima
 // partial[prep_blocks(K)][N].  hipErrorNotSupported (nothing enqueued) when
 // prep_fused_supported() is false.

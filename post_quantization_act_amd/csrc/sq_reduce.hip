@@ -154,8 +154,9 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // column maxima of diag(s) W ------------------------------------------------
 //
 // A block of NT threads (1024 for exact alpha on rows of more than 256
-// 8-column groups, else 512) streams the rows [r0, r1) of W (bf16, 16-byte
-// aligned rows, N % 8 == 0).
+// 8-column groups, else 512: the fp64 pow of a general alpha needs the
+// registers) streams the rows [r0, r1) of W (bf16, 16-byte aligned rows,
+// N % 8 == 0, N <= 49152).
 // Each iteration takes RB rows: row slot t / TPR (TPR = NT / RB threads per
 // row); thread t % TPR of a slot owns the 8-column groups q = t % TPR + TPR i,
 // i < GPT, and keeps their running column maxima in registers (GR groups) or
@@ -453,9 +454,8 @@ int prep_blocks(int64_t K) {
 }
 
 bool prep_fused_supported(const void* w, bool bf16, int64_t N, int64_t ld, float alpha) {
-    const bool exact = alpha == 0.0f || alpha == 0.5f || alpha == 1.0f;
-    const int64_t max_groups = exact ? 1024 * 6 : (int64_t)kPrepThreads * 8;
-    return bf16 && N > 0 && N % 8 == 0 && N / 8 <= max_groups && rows_aligned16(w, ld, 2);
+    (void)alpha;  // every alpha takes the one-read pass up to 6144 groups of 8 columns
+    return bf16 && N > 0 && N % 8 == 0 && N / 8 <= 6144 && rows_aligned16(w, ld, 2);
 }
 
 hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* amax_x,
@@ -493,7 +493,8 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
         else if (groups <= 1024) SQ_PREP(4, 8, 0, true);
         else if (groups <= 2048) SQ_PREP(2, 8, 0, true);
         else if (groups <= 3072) SQ_PREP(1, 6, 0, true);
-        else SQ_PREP(1, 8, 0, true);
+        else if (groups <= 4096) SQ_PREP(1, 8, 0, true);
+        else SQ_PREP(1, 4, 8, true);  // up to 6144 groups: 4 in registers, 8 in LDS (128 KB)
     } else {
         // beyond 256 groups: 1024 threads (16 wavefronts per CU stream the
         // rows 3-8 % faster than 8), half the groups per thread
