@@ -34,11 +34,14 @@ Besides the headline line, the JSON carries:
                 output (fp32) against X W (fp64) per alpha on a 256-token sample;
   llm_int8_comparator   the LLM.int8()-style mixed-precision route against
                 SmoothQuant on the attention-projection workload;
+  hbm_probe     torch's bf16 -> int8 conversion, bf16 copy and bf16 max on
+                1 GB pools: what generic kernels reach on this GPU for the
+                quantizers' read + write pattern and for a read stream;
   cpu_baseline  the CPU oracle as it stands, on the host cores, over bounded
                 samples of the step's stages, scaled to the whole step.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
-                    [--sections step,judged,attn_proj,alpha,comparator]
+                    [--sections step,judged,attn_proj,alpha,comparator,probe]
 """
 from __future__ import annotations
 
@@ -61,7 +64,7 @@ INT8_PEAK_TOPS = 5000.0    # MI355X dense INT8 MFMA, TOPS (5.0 POP/s)
 METRIC = "W8A8 GEMM TOPS (% INT8 MFMA peak); quant-kernel HBM GB/s (% peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_large_8192x12288x49152_traffic.json")
 GEMM_SOURCES = [os.path.join(ROOT, "post_quantization_act_amd", "csrc", f) for f in ("sq_gemm.hip", "sq_device.h")]
-SECTIONS = ("step", "judged", "attn_proj", "alpha", "comparator")
+SECTIONS = ("step", "judged", "attn_proj", "alpha", "comparator", "probe")
 RUNS = 50          # HIP-event timed calls per judged row (median reported)
 POOL_BYTES = 1e9   # rotate inputs over at least this many bytes
 CPU_THREADS_MAX = 16
@@ -555,6 +558,29 @@ def _comparator(torch, sq, synth, pipeline, dev, tm):
     return out
 
 
+def _hbm_probe(torch, dev, tm):
+    """Reference points for the quantizers' access pattern on this GPU, from
+    torch's own kernels over rotating 1 GB pools: a bf16 -> int8 conversion
+    (reads 2 B and writes 1 B per element, the pattern of every code kernel
+    here), a bf16 copy (2 + 2 B) and a bf16 max reduction (a read stream)."""
+    n = 1 << 27  # 128 Mi elements: 256 MB of bf16
+    src = [torch.empty(n, dtype=torch.bfloat16, device=dev).normal_() for _ in range(4)]
+    dst8 = [torch.empty(n, dtype=torch.int8, device=dev) for _ in range(4)]
+    dst16 = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    out = {
+        "bf16_to_int8_copy": _rate(tm(lambda i: dst8[i % 4].copy_(src[i % 4])), 3 * n,
+                                   note="torch elementwise conversion: read 2 B, write 1 B per element"),
+        "bf16_copy": _rate(tm(lambda i: dst16[i % 4].copy_(src[i % 4])), 4 * n,
+                           note="torch copy: read 2 B, write 2 B per element"),
+        "bf16_amax": _rate(tm(lambda i: torch.amax(src[i % 4])), 2 * n,
+                           note="torch max reduction: read 2 B per element"),
+        "elements": n,
+    }
+    del src, dst8, dst16
+    torch.cuda.empty_cache()
+    return out
+
+
 # ---- CPU baseline ----------------------------------------------------------------------------
 
 def _cpu_baseline(target_s: float):
@@ -707,6 +733,8 @@ def main():
         out["attn_proj_step"] = _attn_proj_step(torch, sq, synth, pipeline, dev, tm)
     if "comparator" in sections:
         out["llm_int8_comparator"] = _comparator(torch, sq, synth, pipeline, dev, tm)
+    if "probe" in sections:
+        out["hbm_probe"] = _hbm_probe(torch, dev, tm)
     if not args.no_cpu:
         out["cpu_baseline"] = _cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
