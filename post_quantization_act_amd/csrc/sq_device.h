@@ -41,6 +41,25 @@ __device__ __forceinline__ uint4 ld16_stream(const void* p) {
     return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Buffer descriptor of `bytes` bytes at p (raw buffer, no stride): loads at
+// offsets at or past `bytes` return zero and do not access memory.  The
+// fourth dword is the gfx9-family default for 32-bit raw accesses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// 16-byte buffer load at byte offset off with the nontemporal hint (zero when
+// off is out of the descriptor's range).
+__device__ __forceinline__ uint4 ld16_buf_stream(__amdgpu_buffer_rsrc_t rs, int off) {
+    const v4u_t t = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 2);
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
+// 4-byte buffer load at byte offset off (zero out of range).
+__device__ __forceinline__ float ld4_buf(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+
 // Streaming stores (nontemporal hint) for outputs written once.
 __device__ __forceinline__ void st16_stream(void* p, uint4 v) {
     __builtin_nontemporal_store(v4u_t{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u_t*>(p));

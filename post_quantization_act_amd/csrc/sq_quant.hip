@@ -43,6 +43,82 @@ __device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restri
     const int64_t k0 = (grp * kQwGroup + rem / tj) * kQwTile;
     const int64_t j0 = (rem % tj) * kQwTile;
     const int t = threadIdx.x;
+    const int wave = t / kWave, lane = t % kWave;
+    const int cg = (lane % 8) + 8 * (wave % 2);
+    const int rg = (lane / 8) + 8 * (wave / 2);
+    const int64_t kc = k0 + cg * 8;
+    const int64_t ncol = N - kc;
+
+    // The thread's 8 rows (and their s) are loaded before anything waits: with
+    // 16-byte rows (kVec) as buffer loads over the tile's rows below K, so
+    // rows past K, and groups of a lane whose 8 columns are not all inside N,
+    // read zeros without a branch (the latter then load element-wise).
+    float v[8][8];
+    float sv[8];
+    if constexpr (kVec) {
+        const int rows = (int)min<int64_t>(kQwTile, K - j0);
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(w + j0 * ld, (int)(rows * ld * (int64_t)sizeof(T)));
+        const bool full = ncol >= 8;
+        constexpr int kLd = 8 * (int)sizeof(T) / 16;  // 16-byte loads per row
+        uint4 raw[8][kLd];
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+            for (int h = 0; h < kLd; ++h) {
+                const int off = (int)(((rg * 8 + rr) * ld + kc) * (int64_t)sizeof(T)) + 16 * h;
+                raw[rr][h] = ld16_buf_stream(rs, full ? off : 0x7FFFFFF0);
+            }
+        if constexpr (kScaled) {
+            const __amdgpu_buffer_rsrc_t rsj = row_rsrc(s + j0, rows * 4);
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) sv[rr] = ld4_buf(rsj, (rg * 8 + rr) * 4);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t u[4] = {raw[rr][0].x, raw[rr][0].y, raw[rr][0].z, raw[rr][0].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    v[rr][2 * h] = bf16_lo(u[h]);
+                    v[rr][2 * h + 1] = bf16_hi(u[h]);
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    v[rr][4 * h] = __uint_as_float(raw[rr][h].x);
+                    v[rr][4 * h + 1] = __uint_as_float(raw[rr][h].y);
+                    v[rr][4 * h + 2] = __uint_as_float(raw[rr][h].z);
+                    v[rr][4 * h + 3] = __uint_as_float(raw[rr][h].w);
+                }
+            }
+        }
+        if (!full && ncol > 0) {
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const int64_t j = j0 + rg * 8 + rr;
+                if (j < K) load8_tail(w + j * ld + kc, ncol, v[rr]);
+            }
+        }
+    } else {
+        if (ncol > 0) {
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                const int64_t j = j0 + rg * 8 + rr;
+                if (j < K) {
+                    load8_tail(w + j * ld + kc, ncol, v[rr]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[rr][i] = 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) {
+            const int64_t j = j0 + rg * 8 + rr;
+            sv[rr] = (kScaled && j < K) ? s[j] : 1.0f;
+        }
+    }
+
     if (t < kQwTile) {
         const int64_t k = k0 + t;
         float scale = 0.0f, r = 0.0f;
@@ -54,28 +130,11 @@ __device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restri
     }
     __syncthreads();
 
-    const int wave = t / kWave, lane = t % kWave;
-    const int cg = (lane % 8) + 8 * (wave % 2);
-    const int rg = (lane / 8) + 8 * (wave / 2);
-    const int64_t kc = k0 + cg * 8;
-    const int64_t ncol = N - kc;
-
     uint32_t lo[8], hi[8];  // per column cc: codes of rows 0..3 (lo) and 4..7 (hi)
 #pragma unroll
     for (int cc = 0; cc < 8; ++cc) lo[cc] = hi[cc] = 0u;
 
     if (ncol > 0) {
-        float v[8][8];
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int64_t j = j0 + rg * 8 + rr;
-            if (j < K) {
-                load8_any<kVec>(w + j * ld + kc, ncol, v[rr]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) v[rr][i] = 0.0f;
-            }
-        }
         float rr_[8];
         bool finite = true;
 #pragma unroll
@@ -86,11 +145,9 @@ __device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restri
         auto code_all = [&](auto fast) {
 #pragma unroll
             for (int rr = 0; rr < 8; ++rr) {
-                const int64_t j = j0 + rg * 8 + rr;
-                const float sj = (kScaled && j < K) ? s[j] : 1.0f;
 #pragma unroll
                 for (int cc = 0; cc < 8; ++cc) {
-                    const float wp = kScaled ? sj * v[rr][cc] : v[rr][cc];
+                    const float wp = kScaled ? sv[rr] * v[rr][cc] : v[rr][cc];
                     if constexpr (decltype(fast)::value) {
                         // code + 128 is an integer in [1, 255]: one byte insert
                         // (the 0x80 flip below turns it into the int8 code)
@@ -247,6 +304,22 @@ __global__ __launch_bounds__(256) void k_quant_act(const T* __restrict__ x, int6
     else code_row(std::false_type{});
 }
 
+// One row's groups g = t + TPB q (q < NV) of bf16 x, 16 bytes each, as
+// buffer loads over a descriptor of the row: offsets at or past the row's
+// groups * 16 bytes (groups past the row end) and every offset of a row at or
+// past M (the descriptor then holds 0 bytes) read as zero without touching
+// memory.  So the loads carry no branch, and the compiler can wait for the
+// current row alone (vmcnt(NV)) while the next row's loads stay in flight;
+// loads under a per-lane branch would each end in a full wait.
+template <int NV, int TPB>
+__device__ __forceinline__ void load_row_groups(const bf16_t* __restrict__ x, int64_t row, int64_t M, int64_t ld,
+                                                int groups, int t, uint4 (&d)[NV]) {
+    const bool in = row < M;
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(x + (in ? row : 0) * ld, in ? groups * 16 : 0);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) d[q] = ld16_buf_stream(rs, (t + q * TPB) * 16);
+}
+
 // bf16 rows with per-token scales (mode 0) or a fixed per-tensor maximum
 // (mode 2), K <= 16384: a block of 4 wavefronts walks rows blockIdx.x,
 // blockIdx.x + gridDim.x, ...  Each thread owns the NV 8-channel groups
@@ -282,23 +355,14 @@ __device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk,
         if (bid == 0 && t == 0) x_scale[0] = scale;
     }
     __shared__ float red[2][4];
-    uint4 cur[NV], nxt[NV];
-    auto load = [&](int64_t row, uint4 (&d)[NV]) {
-#pragma unroll
-        for (int q = 0; q < NV; ++q) {
-            const int64_t g = t + (int64_t)q * 256;
-            d[q] = (row < M && g < groups) ? ld16_stream(x + row * ld + g * 8) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    int64_t row = bid;
-    load(row, cur);
-    for (int it = 0; row < M; ++it, row += nblk) {
-        load(row + nblk, nxt);
+    // one row of codes from its loaded groups d; `slot` picks the LDS slots
+    // (alternating between consecutive rows of the block)
+    auto row_codes = [&](int64_t row, const uint4 (&d)[NV], int slot) {
         float v[NV][8];
         float m = 0.0f;
 #pragma unroll
         for (int q = 0; q < NV; ++q) {
-            const uint32_t u[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+            const uint32_t u[4] = {d[q].x, d[q].y, d[q].z, d[q].w};
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 v[q][2 * h] = bf16_lo(u[h]) * is[q][2 * h];
@@ -311,9 +375,9 @@ __device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk,
         }
         if constexpr (!kStatic) {
             m = wave_max(m);
-            if (lane == 0) red[it & 1][wave] = m;
+            if (lane == 0) red[slot][wave] = m;
             __syncthreads();
-            m = fmaxf(fmaxf(red[it & 1][0], red[it & 1][1]), fmaxf(red[it & 1][2], red[it & 1][3]));
+            m = fmaxf(fmaxf(red[slot][0], red[slot][1]), fmaxf(red[slot][2], red[slot][3]));
             group_scale(m, scale, r);
             if (t == 0) x_scale[row] = scale;
         }
@@ -334,8 +398,19 @@ __device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk,
         };
         if (r <= 3.402823466e38f) code_row(std::true_type{});
         else code_row(std::false_type{});
-#pragma unroll
-        for (int q = 0; q < NV; ++q) cur[q] = nxt[q];
+    };
+    // two rows per iteration with two load buffers: the loads of one row are
+    // in flight while the other is coded, and no register copy between
+    // iterations waits for them
+    uint4 da[NV], db[NV];
+    int64_t row = bid;
+    if (row < M) load_row_groups<NV, 256>(x, row, M, ld, (int)groups, t, da);
+    for (; row < M; row += 2 * nblk) {
+        load_row_groups<NV, 256>(x, row + nblk, M, ld, (int)groups, t, db);
+        row_codes(row, da, 0);
+        if (row + nblk >= M) break;
+        load_row_groups<NV, 256>(x, row + 2 * nblk, M, ld, (int)groups, t, da);
+        row_codes(row + nblk, db, 1);
     }
 }
 
@@ -484,6 +559,12 @@ __global__ __launch_bounds__(256) void k_quant_act_long(const T* __restrict__ x,
 
 // ---- launchers -----------------------------------------------------------------
 
+// A weight tile's 128 rows of stride ld fit the 31-bit byte range of one
+// buffer descriptor.
+static bool qw_rows_addressable(int64_t ld, int64_t elem_bytes) {
+    return ld > 0 && (int64_t)kQwTile * ld * elem_bytes < ((int64_t)1 << 31) - 64;
+}
+
 // Weight codes beyond 64 MB leave as nontemporal stores; smaller ones stay
 // cacheable for the GEMM that reads them next.
 static int weight_codes_stream(int64_t K, int64_t N) { return (uint64_t)K * (uint64_t)N > (64ull << 20) ? 1 : 0; }
@@ -495,7 +576,9 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;  // beyond 2^45 weights: not addressable in one grid
     dim3 grid((unsigned)tiles);
     const int w_stream = weight_codes_stream(K, N);
-    const bool vec = rows_aligned16(w, ld, bf16 ? 2 : 4);
+    // the 16-byte path addresses a tile's 128 rows through one buffer
+    // descriptor (32-bit byte offsets)
+    const bool vec = rows_aligned16(w, ld, bf16 ? 2 : 4) && qw_rows_addressable(ld, bf16 ? 2 : 4);
     auto go = [&](auto tag, auto scaled, auto vecc) {
         using T = decltype(tag);
         hipLaunchKernelGGL((k_quant_weight<T, decltype(scaled)::value, decltype(vecc)::value>), grid, dim3(256), 0,
@@ -515,157 +598,171 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
 
 // ---- fused LayerNorm + per-token codes (the runtime half of the LN fold) ----------
 //
-// Same row layout as k_quant_act (WPR wavefronts per bf16 token row, NV groups
-// of 8 channels per thread, the row in registers).  The statistics use a
-// fixed-point grid so no reduction order can change them: with 2^E the power
-// of two just above the row's largest magnitude, x_j is truncated toward zero
-// to a multiple of 2^(E-39) and x_j^2 to a multiple of 2^(2E-39); the
-// truncated values are integers in units of the grid, and with K <= 16384 every
-// partial sum stays below 2^53, so fp64 adds them exactly in any order.  Then
-// mu = S1 2^(E-39) / K, var = max(S2 2^(2E-39) / K - mu^2, 0),
-// rstd = 1 / sqrt(var + eps) in fp64, each rounded once to fp32; element j in
-// fp32: n = fl(fl(x_j - mu) rstd), z = fl(fl(n g_j) + b_j) with the folded
-// LayerNorm weight g and bias b; then the row's max |z|, scale and codes as
-// in step 4.  The grid terms are formed in fp32 (for bf16 x, x 2^(39-E) and
-// (x 2^-E)^2 2^39 are exact in fp32, and terms too small to be exact truncate
-// to 0 either way); only their sums run in fp64.
+// The statistics use a fixed-point grid so no reduction order can change
+// them: with 2^E the power of two just above the row's largest magnitude,
+// x_j is truncated toward zero to a multiple of 2^(E-39) and x_j^2 to a
+// multiple of 2^(2E-39); the truncated values are integers in units of the
+// grid, and with K <= 16384 every partial sum stays below 2^53, so fp64 adds
+// them exactly in any order.  Then mu = S1 2^(E-39) / K,
+// var = max(S2 2^(2E-39) / K - mu^2, 0), rstd = 1 / sqrt(var + eps) in fp64,
+// each rounded once to fp32; element j in fp32: n = fl(fl(x_j - mu) rstd),
+// z = fl(fl(n g_j) + b_j) with the folded LayerNorm weight g and bias b; then
+// the row's max |z|, scale and codes as in step 4.
+//
+// The grid terms are formed in fp32: a = x 2^(39-E) is exact, and so is
+// p = a (x 2^-E) = x^2 2^(39-2E) whenever p >= 1 (both factors are then
+// normal and the product has at most 16 significant bits); a smaller p
+// truncates to 0 whatever its rounding.  Only the sums run in fp64.
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
     return v;
 }
 
-template <int NV, int WPR>
-__global__ __launch_bounds__(256) void k_ln_quant(const bf16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld,
+// One token row per TPB threads (TPB / 64 wavefronts), rows walked with a
+// grid stride.  Thread t owns the 8-channel groups t + TPB q (q < NV) of
+// every row and keeps their folded gamma (and beta) in registers for all its
+// rows; the next row's loads are in flight while the current row is reduced,
+// normalised and coded.  Three reductions per row (max |x|, the two grid
+// sums, max |z|) cross the wavefronts through LDS slots that alternate
+// between rows, so each costs one barrier.
+template <int NV, int TPB, bool kBeta>
+__global__ __launch_bounds__(TPB) void k_ln_quant(const bf16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld,
                                                   const float* __restrict__ gamma, const float* __restrict__ beta,
                                                   float eps, int8_t* __restrict__ xq, float* __restrict__ x_scale) {
-    constexpr int kRowsPerBlock = 4 / WPR;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-    const int row_in_block = wave / WPR;
-    const int t = (wave % WPR) * kWave + lane;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + row_in_block;
-    const bool valid = row < M;
-    const int64_t groups = K / 8;
-
-    float v[NV][8];
-    float xm = 0.0f;
+    constexpr int W = TPB / kWave;
+    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, t = threadIdx.x;
+    const int groups = (int)(K / 8);
+    // groups past the row end (last q only) take the last group's gamma/beta;
+    // their x is zero and they are left out of the max and the stores
+    float gw[NV][8], bw[NV][8];
 #pragma unroll
     for (int q = 0; q < NV; ++q) {
-        const int64_t g = t + (int64_t)q * (WPR * kWave);
-        if (valid && g < groups) {
-            load8(x + row * ld + g * 8, v[q]);
+        const int g = t + q * TPB;
+        const int64_t gc = (q < NV - 1 || g < groups) ? g : groups - 1;
+        const float4 a = *reinterpret_cast<const float4*>(gamma + gc * 8);
+        const float4 b = *reinterpret_cast<const float4*>(gamma + gc * 8 + 4);
+        gw[q][0] = a.x; gw[q][1] = a.y; gw[q][2] = a.z; gw[q][3] = a.w;
+        gw[q][4] = b.x; gw[q][5] = b.y; gw[q][6] = b.z; gw[q][7] = b.w;
+        if constexpr (kBeta) {
+            const float4 c = *reinterpret_cast<const float4*>(beta + gc * 8);
+            const float4 d = *reinterpret_cast<const float4*>(beta + gc * 8 + 4);
+            bw[q][0] = c.x; bw[q][1] = c.y; bw[q][2] = c.z; bw[q][3] = c.w;
+            bw[q][4] = d.x; bw[q][5] = d.y; bw[q][6] = d.z; bw[q][7] = d.w;
+        }
+    }
+    __shared__ float red_x[2][W], red_z[2][W];
+    __shared__ double red_1[2][W], red_2[2][W];
+    const int64_t nblk = gridDim.x;
+    auto row_codes = [&](int64_t row, const uint4 (&cur)[NV], int b) {
+        float v[NV][8];
+        float xm = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const uint32_t u[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[q][2 * h] = bf16_lo(u[h]);
+                v[q][2 * h + 1] = bf16_hi(u[h]);
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) xm = fmaxf(xm, fabsf(v[q][i]));
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[q][i] = 0.0f;
         }
-    }
-    __shared__ float redm[4];
-    __shared__ double red1[4], red2[4];
-    xm = wave_max(xm);
-    if constexpr (WPR > 1) {
-        if (lane == 0) redm[wave] = xm;
-        __syncthreads();
-        const int w0 = row_in_block * WPR;
-        xm = redm[w0];
+        xm = wave_max(xm);
+        if constexpr (W > 1) {
+            if (lane == 0) red_x[b][wave] = xm;
+            __syncthreads();
+            xm = red_x[b][0];
 #pragma unroll
-        for (int i = 1; i < WPR; ++i) xm = fmaxf(xm, redm[w0 + i]);
-        __syncthreads();  // redm is reused below
-    }
-    int E = 0;
-    frexpf(xm, &E);
-    // ldexpf scales exactly over the whole range (a constant 2^(39-E) could overflow)
-    double s1 = 0.0, s2 = 0.0;
-#pragma unroll
-    for (int q = 0; q < NV; ++q)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float y = ldexpf(v[q][i], -E);
-            s1 += (double)truncf(ldexpf(v[q][i], 39 - E));
-            s2 += (double)truncf(ldexpf(y * y, 39));
+            for (int i = 1; i < W; ++i) xm = fmaxf(xm, red_x[b][i]);
         }
-    // convert again below rather than keeping 8 doubles per group alive
+        int E = 0;
+        frexpf(xm, &E);
+        // ldexpf scales exactly over the whole range (a constant 2^(39-E) could overflow)
+        double s1 = 0.0, s2 = 0.0;
 #pragma unroll
-    for (int q = 0; q < NV; ++q)
+        for (int q = 0; q < NV; ++q)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[q][i]));
-    s1 = wave_sum_f64(s1);
-    s2 = wave_sum_f64(s2);
-    if constexpr (WPR > 1) {
-        if (lane == 0) {
-            red1[wave] = s1;
-            red2[wave] = s2;
-        }
-        __syncthreads();
-        const int w0 = row_in_block * WPR;
-        s1 = red1[w0];
-        s2 = red2[w0];
-#pragma unroll
-        for (int i = 1; i < WPR; ++i) {
-            s1 += red1[w0 + i];
-            s2 += red2[w0 + i];
-        }
-    }
-    double mu = 0.0, var = 0.0;
-    if (xm > 0.0f) {
-        mu = ldexp(s1, E - 39) / (double)K;
-        var = ldexp(s2, 2 * E - 39) / (double)K - mu * mu;
-        if (var < 0.0) var = 0.0;
-    }
-    const float mu32 = (float)mu, rstd32 = (float)(1.0 / sqrt(var + (double)eps));
-
-    float m = 0.0f;
-#pragma unroll
-    for (int q = 0; q < NV; ++q) {
-        const int64_t g = t + (int64_t)q * (WPR * kWave);
-        if (valid && g < groups) {
-            const float4 ga = *reinterpret_cast<const float4*>(gamma + g * 8);
-            const float4 gb = *reinterpret_cast<const float4*>(gamma + g * 8 + 4);
-            const float gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-            float bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if (beta) {
-                const float4 ba = *reinterpret_cast<const float4*>(beta + g * 8);
-                const float4 bb = *reinterpret_cast<const float4*>(beta + g * 8 + 4);
-                bw[0] = ba.x; bw[1] = ba.y; bw[2] = ba.z; bw[3] = ba.w;
-                bw[4] = bb.x; bw[5] = bb.y; bw[6] = bb.z; bw[7] = bb.w;
+            for (int i = 0; i < 8; ++i) {
+                const float a = ldexpf(v[q][i], 39 - E);
+                s1 += (double)truncf(a);
+                s2 += (double)truncf(a * ldexpf(v[q][i], -E));
             }
+        s1 = wave_sum_f64(s1);
+        s2 = wave_sum_f64(s2);
+        if constexpr (W > 1) {
+            if (lane == 0) {
+                red_1[b][wave] = s1;
+                red_2[b][wave] = s2;
+            }
+            __syncthreads();
+            s1 = red_1[b][0];
+            s2 = red_2[b][0];
+#pragma unroll
+            for (int i = 1; i < W; ++i) {
+                s1 += red_1[b][i];
+                s2 += red_2[b][i];
+            }
+        }
+        double mu = 0.0, var = 0.0;
+        if (xm > 0.0f) {
+            mu = ldexp(s1, E - 39) / (double)K;
+            var = ldexp(s2, 2 * E - 39) / (double)K - mu * mu;
+            if (var < 0.0) var = 0.0;
+        }
+        const float mu32 = (float)mu, rstd32 = (float)(1.0 / sqrt(var + (double)eps));
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const bool in = q < NV - 1 || t + q * TPB < groups;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float n = (v[q][i] - mu32) * rstd32;
-                const float tt = n * gw[i];
-                v[q][i] = beta ? tt + bw[i] : tt;
-                m = fmaxf(m, fabsf(v[q][i]));
+                const float tt = n * gw[q][i];
+                v[q][i] = kBeta ? tt + bw[q][i] : tt;
+                m = fmaxf(m, in ? fabsf(v[q][i]) : 0.0f);
             }
         }
-    }
-    m = wave_max(m);
-    if constexpr (WPR > 1) {
-        if (lane == 0) redm[wave] = m;
-        __syncthreads();
-        const int w0 = row_in_block * WPR;
-        m = redm[w0];
+        m = wave_max(m);
+        if constexpr (W > 1) {
+            if (lane == 0) red_z[b][wave] = m;
+            __syncthreads();
+            m = red_z[b][0];
 #pragma unroll
-        for (int i = 1; i < WPR; ++i) m = fmaxf(m, redm[w0 + i]);
-    }
-    float scale, r;
-    group_scale(m, scale, r);
-    if (!valid) return;
-    if (t == 0) x_scale[row] = scale;
-    auto code_row = [&](auto fast) {
-#pragma unroll
-        for (int q = 0; q < NV; ++q) {
-            const int64_t g = t + (int64_t)q * (WPR * kWave);
-            if (g < groups) {
-                int c[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
-                st8_stream(xq + row * K + g * 8, make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
-            }
+            for (int i = 1; i < W; ++i) m = fmaxf(m, red_z[b][i]);
         }
+        float scale, r;
+        group_scale(m, scale, r);
+        if (t == 0) x_scale[row] = scale;
+        auto code_row = [&](auto fast) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const int g = t + q * TPB;
+                if (q < NV - 1 || g < groups) {
+                    int c[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
+                    st8_stream(xq + row * K + (int64_t)g * 8,
+                               make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+                }
+            }
+        };
+        if (r <= 3.402823466e38f) code_row(std::true_type{});
+        else code_row(std::false_type{});
     };
-    if (r <= 3.402823466e38f) code_row(std::true_type{});
-    else code_row(std::false_type{});
+    // two rows per iteration with two load buffers (no register copy between
+    // iterations that would wait for the loads in flight)
+    uint4 da[NV], db[NV];
+    int64_t row = blockIdx.x;
+    if (row < M) load_row_groups<NV, TPB>(x, row, M, ld, groups, t, da);
+    for (; row < M; row += 2 * nblk) {
+        load_row_groups<NV, TPB>(x, row + nblk, M, ld, groups, t, db);
+        row_codes(row, da, 0);
+        if (row + nblk >= M) break;
+        load_row_groups<NV, TPB>(x, row + 2 * nblk, M, ld, groups, t, da);
+        row_codes(row + nblk, db, 1);
+    }
 }
 
 template <typename T, int NV, int WPR>
@@ -761,7 +858,8 @@ hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, c
                              int8_t* xq, float* x_scale, hipStream_t st) {
     if (K <= 0 || N <= 0 || M <= 0 || !s || !inv_s) return hipErrorNotSupported;
     const int64_t groups = K / 8;
-    if (K % 8 != 0 || groups > 2 * 256 || !rows_aligned16(w, ldw, 2) || !rows_aligned16(x, ldx, 2))
+    if (K % 8 != 0 || groups > 2 * 256 || !rows_aligned16(w, ldw, 2) || !rows_aligned16(x, ldx, 2) ||
+        !qw_rows_addressable(ldw, 2))
         return hipErrorNotSupported;
     const int64_t tiles = ((N + kQwTile - 1) / kQwTile) * ((K + kQwTile - 1) / kQwTile);
     int cus = 0, dev = 0;
@@ -787,29 +885,55 @@ hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, c
     return hipGetLastError();
 }
 
-template <int NV, int WPR>
-static void launch_ln_rows(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* gamma, const float* beta,
-                           float eps, int8_t* xq, float* x_scale, hipStream_t st) {
-    constexpr int rpb = 4 / WPR;
-    const int64_t blocks = (M + rpb - 1) / rpb;
-    hipLaunchKernelGGL((k_ln_quant<NV, WPR>), dim3((unsigned)blocks), dim3(256), 0, st, x, M, K, ld, gamma, beta, eps,
-                       xq, x_scale);
+// Blocks per CU of k_ln_quant<NV, TPB, *>: what its register footprint lets
+// reside at once (the grid walks all rows with that many blocks).
+static int ln_blocks_per_cu(int nv, int tpb) {
+    const int waves_per_simd = nv <= 1 ? 8 : nv <= 2 ? 5 : nv <= 4 ? 3 : 2;
+    return std::max(1, waves_per_simd * 4 / (tpb / kWave));
 }
 
+template <int NV, int TPB>
+static hipError_t launch_ln_rows(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* gamma,
+                                 const float* beta, float eps, int8_t* xq, float* x_scale, hipStream_t st) {
+    // the kernel reads groups t + TPB q unchecked for q < NV - 1
+    const int64_t groups = K / 8;
+    if (groups <= (int64_t)(NV - 1) * TPB || groups > (int64_t)NV * TPB) return hipErrorInvalidValue;
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    const dim3 grid((unsigned)std::min<int64_t>(M, (int64_t)cus * ln_blocks_per_cu(NV, TPB)));
+    if (beta)
+        hipLaunchKernelGGL((k_ln_quant<NV, TPB, true>), grid, dim3(TPB), 0, st, x, M, K, ld, gamma, beta, eps, xq,
+                           x_scale);
+    else
+        hipLaunchKernelGGL((k_ln_quant<NV, TPB, false>), grid, dim3(TPB), 0, st, x, M, K, ld, gamma, beta, eps, xq,
+                           x_scale);
+    return hipGetLastError();
+}
+
+// Threads per row grow with K so that each thread keeps at most 6 groups
+// (48 channels, with their gamma and beta) in registers; NV is always
+// ceil(groups / TPB).
 hipError_t launch_ln_quant(const void* x, int64_t M, int64_t K, int64_t ld, const float* gamma, const float* beta,
                            float eps, int8_t* xq, float* x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const int64_t groups = K / 8;
-    if (groups <= 1 * kWave) launch_ln_rows<1, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else if (groups <= 2 * kWave) launch_ln_rows<2, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else if (groups <= 4 * kWave) launch_ln_rows<4, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else if (groups <= 8 * kWave) launch_ln_rows<8, 1>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else if (groups <= 4 * 4 * kWave) launch_ln_rows<4, 4>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else if (groups <= 6 * 4 * kWave) launch_ln_rows<6, 4>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else if (groups <= 8 * 4 * kWave) launch_ln_rows<8, 4>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st);
-    else return hipErrorNotSupported;
-    return hipGetLastError();
+#define SQ_LN(NV, TPB) return launch_ln_rows<NV, TPB>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st)
+    if (groups <= 64) SQ_LN(1, 64);
+    if (groups <= 128) SQ_LN(2, 64);
+    if (groups <= 192) SQ_LN(3, 64);
+    if (groups <= 256) SQ_LN(4, 64);
+    if (groups <= 384) SQ_LN(3, 128);
+    if (groups <= 512) SQ_LN(4, 128);
+    if (groups <= 768) SQ_LN(3, 256);
+    if (groups <= 1024) SQ_LN(4, 256);
+    if (groups <= 1280) SQ_LN(5, 256);
+    if (groups <= 1536) SQ_LN(6, 256);
+    if (groups <= 2048) SQ_LN(4, 512);
+#undef SQ_LN
+    return hipErrorNotSupported;
 }
 
 // gamma_out[j] = fl(gamma[j] * inv_s[j]); beta_out likewise when beta is given.

@@ -284,6 +284,19 @@ def test_strided_inputs():
     _compare(b, o, 0.5, torch.bfloat16)
 
 
+@pytest.mark.parametrize("dtype,N,pad", [(torch.bfloat16, 100, 4), (torch.float32, 101, 3), (torch.bfloat16, 8, 0)])
+def test_strided_weight_ragged_columns(dtype, N, pad):
+    """16-byte aligned weight rows with N % 8 != 0 (the last 8-column group of a
+    row is partly past N) and K not a multiple of the 128-row weight tile."""
+    K = 208
+    x, w, calib = _inputs(70, K, N, dtype, seed=13, T=90)
+    ww = torch.zeros(K, N + pad, dtype=dtype)
+    ww[:, :N] = w
+    b = _run_gpu(x.to(DEV), ww.to(DEV)[:, :N], calib.to(DEV), 0.5, sq.SQ_PER_TOKEN)
+    o = oracle.w8a8_linear(_np(x), _np(w), 0.5, oracle.PER_TOKEN, calib=_np(calib))
+    _compare(b, o, 0.5, torch.bfloat16)
+
+
 def test_zero_rows_and_columns():
     x, w, calib = _inputs(40, 128, 70, torch.bfloat16, seed=4, T=40)
     x[3] = 0
