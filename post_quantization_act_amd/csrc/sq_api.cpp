@@ -110,6 +110,13 @@ const char* sq_status_str(sq_status s) {
     return "SQ_UNKNOWN_STATUS";
 }
 
+// The power tables of the one-read weight pass: after the column maxima and
+// the per-block partial maxima in the SQ_OP_PREPARE_WEIGHTS workspace.
+static double* prep_tables(void* ws, int64_t N, int64_t K) {
+    return reinterpret_cast<double*>(static_cast<char*>(ws) + round256((size_t)N * sizeof(uint32_t)) +
+                                     round256((size_t)sqk::prep_blocks(K) * (size_t)N * sizeof(float)));
+}
+
 size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran g) {
     (void)M;
     (void)K;
@@ -117,7 +124,8 @@ size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran 
         case SQ_OP_QUANT_WEIGHT: return N > 0 ? round256((size_t)N * sizeof(uint32_t)) : 0;
         case SQ_OP_PREPARE_WEIGHTS:
             return N > 0 && K > 0 ? round256((size_t)N * sizeof(uint32_t)) +
-                                        round256((size_t)sqk::prep_blocks(K) * (size_t)N * sizeof(float))
+                                        round256((size_t)sqk::prep_blocks(K) * (size_t)N * sizeof(float)) +
+                                        round256((size_t)sqk::prep_table_entries(K) * sizeof(double))
                                   : 0;
         case SQ_OP_QUANT_ACT: return g == SQ_PER_TENSOR ? 256 : 0;
         case SQ_OP_PREPARE_AND_QUANT_ACT:
@@ -265,11 +273,13 @@ sq_status sq_prepare_weights(const float* amax_x, const void* w, sq_dtype wt, in
     const bool bf16 = wt == SQ_BF16;
     uint32_t* colmax = static_cast<uint32_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)N * sizeof(uint32_t)));
+    double* tab = prep_tables(ws, N, K);
     hipError_t e;
     // The one-read pass (row maxima, factors and column maxima together) is
     // faster than the separate passes at every size it supports.
     if (sqk::prep_fused_supported(w, bf16, N, ldw, alpha)) {
-        e = sqk::launch_prepare_weights(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, partial, colmax, stream);
+        e = sqk::launch_prepare_weights(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, partial, colmax, tab,
+                                        stream);
     } else {
         e = sqk::launch_row_absmax_factors(w, bf16, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, stream);
         if (e == hipSuccess) e = sqk::launch_fill_u32(colmax, N, 0u, stream);
@@ -353,7 +363,7 @@ sq_status sq_prepare_and_quant_act(const float* amax_x, const void* w, sq_dtype 
     uint32_t* colmax = static_cast<uint32_t*>(ws);
     float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) + round256((size_t)N * sizeof(uint32_t)));
     hipError_t e = sqk::launch_prepare_weights(w, true, K, N, ldw, amax_x, alpha, s, inv_s, amax_w, partial, colmax,
-                                               stream);
+                                               prep_tables(ws, N, K), stream);
     if (e != hipSuccess) return hip_result(e, fn);
     e = sqk::launch_codes_both(w, K, N, ldw, s, colmax, wq, w_scale, x, M, ldx, inv_s, xq, x_scale, stream);
     if (e == hipErrorNotSupported) {  // K > 4096 or X rows not 16-byte aligned: the two code launches

@@ -23,11 +23,15 @@ hipError_t launch_row_absmax_factors(const void* w, bool bf16, int64_t K, int64_
 // into colmax (fp32 bits), through per-block partial maxima
 // partial[prep_blocks(K)][N].  hipErrorNotSupported (nothing enqueued) when
 // prep_fused_supported() is false.
+// For alpha outside {0, 1/2, 1} the powers of s come from tables of
+// prep_table_entries(K) doubles at tab (built by the call; tab must not be
+// NULL).
 int prep_blocks(int64_t K);
+int64_t prep_table_entries(int64_t K);
 bool prep_fused_supported(const void* w, bool bf16, int64_t N, int64_t ld, float alpha);
 hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* amax_x,
                                   float alpha, float* s, float* inv_s, float* amax_w, float* partial,
-                                  uint32_t* colmax, hipStream_t st);
+                                  uint32_t* colmax, double* tab, hipStream_t st);
 
 // out[0] = max_j fl(amax_x[j] * inv_s[j]) (inv_s may be NULL).
 hipError_t launch_static_max(const float* amax_x, const float* inv_s, int64_t K, float* out, hipStream_t st);

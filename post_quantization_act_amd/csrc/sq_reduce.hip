@@ -153,16 +153,22 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // ---- steps 2 + 3a fused: one read of W gives amax_w, s, inv_s and the
 // column maxima of diag(s) W ------------------------------------------------
 //
-// A block of NT threads (1024 for exact alpha on rows of more than 256
-// 8-column groups, else 512: the fp64 pow of a general alpha needs the
-// registers) streams the rows [r0, r1) of W (bf16, 16-byte aligned rows,
+// A block of NT threads (1024 on rows of more than 256 8-column groups, else
+// 512) streams the rows [r0, r1) of W (bf16, 16-byte aligned rows,
 // N % 8 == 0, N <= 49152).
 // Each iteration takes RB rows: row slot t / TPR (TPR = NT / RB threads per
 // row); thread t % TPR of a slot owns the 8-column groups q = t % TPR + TPR i,
 // i < GPT, and keeps their running column maxima in registers (GR groups) or
 // LDS (GL more).  Per row: max |w| over the slot (shuffles, then LDS across
 // its wavefronts behind one barrier), s_j by the same fp64 rule as
-// k_row_absmax_factors, then the running maxima take |fl(s_j w)|.  The next
+// k_row_absmax_factors, then the running maxima take |fl(s_j w)|.  For alpha
+// in {0, 1/2, 1} the two powers are exact forms computed in place; for any
+// other alpha (kTab) they come from tables of pow_cases built before the pass
+// (k_pow_tables): the numerator per row of W, the denominator per bf16 value
+// of the row maximum, which is always one of the row's bf16 elements.  The
+// tables hold the fp64 values the in-place rule would compute, so s_j is the
+// same; the pass keeps the registers of the exact-alpha form instead of the
+// fp64 pow's.  The next
 // row's loads are issued at the top of the iteration and stay in flight
 // through the reduction, the factor and the update; the barrier waits on LDS
 // only, and nothing else touches global memory in the loop: amax_x is staged
@@ -173,17 +179,37 @@ __global__ __launch_bounds__(256) void k_row_absmax_factors(const T* __restrict_
 // codes read again right after this pass.
 constexpr int kPrepThreads = 512;
 constexpr int kPrepMaxRows = 256;  // rows per block (LDS staging of per-row values)
+constexpr int kPowTabB = 32768;    // denominator table: bf16 patterns 0 .. 0x7FFF, then the floor
+
+// tab[i] = pow_cases(bf16 value of pattern i, 1 - alpha) for i < kPowTabB,
+// tab[kPowTabB] = pow_cases(1e-5f, 1 - alpha), then
+// tab[kPowTabB + 1 + j] = pow_cases(max(amax_x[j], 1e-5f), alpha), j < K.
+__global__ __launch_bounds__(256) void k_pow_tables(const float* __restrict__ amax_x, int64_t K, float alpha,
+                                                    double* __restrict__ tab) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const float fl = 1e-5f;
+    const double ea = (double)alpha, eb = 1.0 - ea;
+    if (i < kPowTabB) {
+        tab[i] = pow_cases((double)__uint_as_float((uint32_t)i << 16), eb);
+    } else if (i == kPowTabB) {
+        tab[i] = pow_cases((double)fl, eb);
+    } else if (i <= kPowTabB + K) {
+        const float a = amax_x[i - kPowTabB - 1];
+        tab[i] = pow_cases((double)(a > fl ? a : fl), ea);
+    }
+}
 
 __device__ __forceinline__ void lds_only_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int RB, int GR, int GL, bool kGeneral, int NT = kPrepThreads, bool kKeep = false>
+template <int RB, int GR, int GL, bool kTab, int NT = kPrepThreads, bool kKeep = false>
 __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, int64_t K, int64_t N,
                                                             int64_t ld, const float* __restrict__ amax_x,
-                                                            float alpha, float* __restrict__ s,
-                                                            float* __restrict__ inv_s, float* __restrict__ amax_w,
-                                                            float* __restrict__ partial, int rows_per_block) {
+                                                            float alpha, const double* __restrict__ tab,
+                                                            float* __restrict__ s, float* __restrict__ inv_s,
+                                                            float* __restrict__ amax_w, float* __restrict__ partial,
+                                                            int rows_per_block) {
     // GR groups keep their running maxima in registers, GL more in LDS
     // (thread-major, so each access is conflict-free)
     constexpr int GPT = GR + GL;
@@ -191,12 +217,16 @@ __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, 
     static_assert(RB == 1 || GL == 0, "LDS-held maxima only with one row per iteration");
     __shared__ float red[2][NT / kWave];
     __shared__ float axl[kPrepMaxRows], srow[kPrepMaxRows], irow[kPrepMaxRows], arow[kPrepMaxRows];
+    __shared__ double pal[kTab ? kPrepMaxRows : 1];  // numerators of the rows (kTab)
     __shared__ float comb[RB > 1 ? (RB - 1) * TPR * 8 * GPT : 1];
     __shared__ float cml[GL > 0 ? GL * 8 * NT : 1];
     const int t = threadIdx.x, slot = t / TPR, ts = t % TPR, wave = t / kWave, lane = t % kWave;
     const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
     const int nrows = (int)min((int64_t)rows_per_block, K - r0);
-    for (int i = t; i < nrows; i += NT) axl[i] = amax_x[r0 + i];
+    for (int i = t; i < nrows; i += NT) {
+        if constexpr (kTab) pal[i] = tab[kPowTabB + 1 + r0 + i];
+        else axl[i] = amax_x[r0 + i];
+    }
 #pragma unroll
     for (int i = 0; i < GL * 8; ++i) cml[i * NT + t] = 0.0f;
     const int iters = (nrows + RB - 1) / RB;
@@ -243,7 +273,17 @@ __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, 
 #pragma unroll
             for (int v = 0; v < WPR; ++v) rm = fmaxf(rm, red[it & 1][slot * WPR + v]);
             float sj = 0.0f, ij = 0.0f;
-            if (lane == 0) smooth_factor<kGeneral>(axl[rl], rm, alpha, sj, ij);
+            if (lane == 0) {
+                if constexpr (kTab) {
+                    // the floored maximum rm > 1e-5f is a bf16 value: its pattern indexes the table
+                    const float fl = 1e-5f;
+                    const double pb = tab[rm > fl ? (int)(__float_as_uint(rm) >> 16) : kPowTabB];
+                    sj = (float)(pal[rl] / pb);
+                    ij = 1.0f / sj;
+                } else {
+                    smooth_factor<false>(axl[rl], rm, alpha, sj, ij);
+                }
+            }
             sj = __shfl(sj, 0);
             if (ts == 0) {
                 srow[rl] = sj;
@@ -458,11 +498,13 @@ bool prep_fused_supported(const void* w, bool bf16, int64_t N, int64_t ld, float
     return bf16 && N > 0 && N % 8 == 0 && N / 8 <= 6144 && rows_aligned16(w, ld, 2);
 }
 
+int64_t prep_table_entries(int64_t K) { return K > 0 ? kPowTabB + 1 + K : 0; }
+
 hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N, int64_t ld, const float* amax_x,
                                   float alpha, float* s, float* inv_s, float* amax_w, float* partial,
-                                  uint32_t* colmax, hipStream_t st) {
+                                  uint32_t* colmax, double* tab, hipStream_t st) {
     if (K <= 0 || N <= 0) return hipSuccess;
-    if (!prep_fused_supported(w, bf16, N, ld, alpha)) return hipErrorNotSupported;
+    if (!prep_fused_supported(w, bf16, N, ld, alpha) || !tab) return hipErrorNotSupported;
     const int nb = prep_blocks(K);
     const int rpb = (int)((K + nb - 1) / nb);
     const int64_t groups = N / 8;
@@ -474,7 +516,7 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
     const bool keep = (uint64_t)K * (uint64_t)ld * 2u <= (128ull << 20);
 #define SQ_PREP_KEEP(RB, GR, GL, G, NT, KEEP)                                                                     \
     hipLaunchKernelGGL((k_prep_rows<RB, GR, GL, G, NT, KEEP>), dim3((unsigned)nb), dim3(NT), 0, st, wb, K, N, ld,     \
-                       amax_x, alpha, s, inv_s, amax_w, partial, rpb)
+                       amax_x, alpha, tab, s, inv_s, amax_w, partial, rpb)
 #define SQ_PREP_NT(RB, GR, GL, G, NT)                                                                             \
     do {                                                                                                          \
         if (keep) SQ_PREP_KEEP(RB, GR, GL, G, NT, true);                                                          \
@@ -483,30 +525,28 @@ hipError_t launch_prepare_weights(const void* w, bool bf16, int64_t K, int64_t N
 #define SQ_PREP(RB, GR, GL, G) SQ_PREP_NT(RB, GR, GL, G, kPrepThreads)
     // Rows per iteration so that each thread has 4-8 loads of 16 bytes in
     // flight per row set (several rows at once for narrow W: with one row per
-    // iteration a 4096-column row is one 16-byte load per thread).  alpha in
-    // {0, 1/2, 1} needs no fp64 pow: fewer registers, wider rows.
+    // iteration a 4096-column row is one 16-byte load per thread).  alpha
+    // outside {0, 1/2, 1}: the powers from tables built first.
     const bool general = !(alpha == 0.0f || alpha == 0.5f || alpha == 1.0f);
     if (general) {
-        if (groups <= 128) SQ_PREP(4, 1, 0, true);
-        else if (groups <= 256) SQ_PREP(4, 2, 0, true);
-        else if (groups <= 512) SQ_PREP(4, 4, 0, true);
-        else if (groups <= 1024) SQ_PREP(4, 8, 0, true);
-        else if (groups <= 2048) SQ_PREP(2, 8, 0, true);
-        else if (groups <= 3072) SQ_PREP(1, 6, 0, true);
-        else if (groups <= 4096) SQ_PREP(1, 8, 0, true);
-        else SQ_PREP(1, 4, 8, true);  // up to 6144 groups: 4 in registers, 8 in LDS (128 KB)
-    } else {
+        const int64_t n = prep_table_entries(K);
+        hipLaunchKernelGGL(k_pow_tables, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, amax_x, K, alpha, tab);
+    }
+    auto go = [&](auto g) {
+        constexpr bool G = decltype(g)::value;
         // beyond 256 groups: 1024 threads (16 wavefronts per CU stream the
         // rows 3-8 % faster than 8), half the groups per thread
-        if (groups <= 128) SQ_PREP(4, 1, 0, false);
-        else if (groups <= 256) SQ_PREP(4, 2, 0, false);
-        else if (groups <= 512) SQ_PREP_NT(4, 2, 0, false, 1024);
-        else if (groups <= 1024) SQ_PREP_NT(4, 4, 0, false, 1024);
-        else if (groups <= 2048) SQ_PREP_NT(2, 4, 0, false, 1024);
-        else if (groups <= 3072) SQ_PREP_NT(1, 3, 0, false, 1024);
-        else if (groups <= 4096) SQ_PREP_NT(1, 4, 0, false, 1024);
-        else SQ_PREP_NT(1, 5, 1, false, 1024);  // up to 6144 groups: 5 in registers, 1 in LDS
-    }
+        if (groups <= 128) SQ_PREP(4, 1, 0, G);
+        else if (groups <= 256) SQ_PREP(4, 2, 0, G);
+        else if (groups <= 512) SQ_PREP_NT(4, 2, 0, G, 1024);
+        else if (groups <= 1024) SQ_PREP_NT(4, 4, 0, G, 1024);
+        else if (groups <= 2048) SQ_PREP_NT(2, 4, 0, G, 1024);
+        else if (groups <= 3072) SQ_PREP_NT(1, 3, 0, G, 1024);
+        else if (groups <= 4096) SQ_PREP_NT(1, 4, 0, G, 1024);
+        else SQ_PREP_NT(1, 5, 1, G, 1024);  // up to 6144 groups: 5 in registers, 1 in LDS
+    };
+    if (general) go(std::true_type{});
+    else go(std::false_type{});
 #undef SQ_PREP
 #undef SQ_PREP_NT
 #undef SQ_PREP_KEEP

@@ -75,6 +75,9 @@ def test_workspace_sizes():
     assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 100) >= 4096 * 4 + 100 * 4096 * 4
     assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 300) < 4096 * 4 + 256 * 4096 * 4  # 150 blocks
     assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 0, 4096) == 0
+    # plus the power tables of a general alpha: 32768 + 1 + K doubles
+    assert sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 0, 4096, 4096) >= (
+        4096 * 4 + 256 * 4096 * 4 + (32769 + 4096) * 8)
     # prepare_and_quant_act: prepare_weights' workspace, then (256-byte aligned) quant_act's
     for g in (sq.SQ_PER_TOKEN, sq.SQ_PER_TENSOR):
         p = sq.sq_workspace_size(sq.SQ_OP_PREPARE_WEIGHTS, 2048, 4096, 4096, g)

@@ -99,6 +99,10 @@ CASES = [
     (16, 2048, 1001, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     # ring decode: one token, K = 16384 (eight stages per wavefront), per-tensor
     (1, 16384, 300, torch.bfloat16, sq.SQ_PER_TENSOR, 0.5, 16),
+    # ring decode: 7 channel groups per block, ragged last group
+    (16, 4096, 28000, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
+    # ring decode: 10 channel groups per block, 13 tokens
+    (13, 2048, 37000, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     # ring decode: 513 groups, so one block takes three; K = 6144
     (12, 6144, 8200, torch.bfloat16, sq.SQ_PER_TOKEN, 0.5, 64),
     # K a multiple of 16 but not of 128: register-staged GEMM path with a K tail
