@@ -197,7 +197,10 @@ sq_status sq_quant_weight_noalloc(const void *w, sq_dtype wt, int64_t K, int64_t
  *   wq, w_scale     as sq_quant_weight;
  *   ws              workspace of sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, 0, N,
  *                   K, 0) bytes, 16-byte aligned (column maxima and per-block
- *                   partial maxima, about 1 KB per output channel).
+ *                   partial maxima, about 1 KB per output channel, then
+ *                   (32769 + K) doubles: for alpha outside {0, 1/2, 1} the
+ *                   fp64 powers of the factor rule are tabulated first, per
+ *                   row of W and per bf16 value of a row maximum).
  */
 sq_status sq_prepare_weights(const float *amax_x, const void *w, sq_dtype wt, int64_t K, int64_t N, int64_t ldw,
                              float alpha, float *s, float *inv_s, float *amax_w, int8_t *wq, float *w_scale,
