@@ -1263,8 +1263,15 @@ const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl) {
         case GemmPath::kDecodeRing:
             return "k_gemm_decode_ring (one block of 16 wavefronts per CU, per-wavefront LDS rings of 128-byte stages)";
         case GemmPath::kDecode: return "k_gemm_decode (32 output channels per block, K split over 4 wavefronts)";
-        case GemmPath::kRing256: return "k_gemm_ring<256,256,4,2,2> (256x256 tile, 8 wavefronts of 64x128, 2 stages)";
+        case GemmPath::kRing256:
+            if (!outl && K % 256 == 0)
+                return "k_gemm_persist<256,256,4,2,2> (one block per CU walking 256x256 tiles, 8 wavefronts of 64x128, "
+                       "2 stages) for bf16 output without accumulator store and N % 8 == 0, else k_gemm_ring<256,256,4,2,2>";
+            return "k_gemm_ring<256,256,4,2,2> (256x256 tile, 8 wavefronts of 64x128, 2 stages)";
         case GemmPath::kRing256Split:
+            if (!outl && K % 256 == 0)
+                return "k_gemm_persist<256,256,4,2,2> (or k_gemm_ring<256,256,4,2,2>) on whole rounds of columns + "
+                       "k_gemm_ring<256,128,4,2,3> on the remaining columns (one round)";
             return "k_gemm_ring<256,256,4,2,2> on whole rounds of columns + k_gemm_ring<256,128,4,2,3> on the "
                    "remaining columns (one round)";
         case GemmPath::kRing256x128:

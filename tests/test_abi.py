@@ -51,11 +51,12 @@ def test_gemm_kernel_choice():
     assert sq.sq_gemm_kernel_name(16, 100, 1040).startswith("k_gemm_decode (")
     assert sq.sq_gemm_kernel_name(2048, 4096, 4096).startswith("k_gemm_ring<256,128")
     assert sq.sq_gemm_kernel_name(33000, 100, 384).startswith("k_gemm_ring<128,128")
-    assert sq.sq_gemm_kernel_name(4096, 14336, 4096).startswith("k_gemm_ring<256,256")
-    assert sq.sq_gemm_kernel_name(4096, 4096, 4096).startswith("k_gemm_ring<256,256")  # one full round
+    assert sq.sq_gemm_kernel_name(4096, 14336, 4096).startswith("k_gemm_persist<256,256")
+    assert sq.sq_gemm_kernel_name(4096, 4096, 4096).startswith("k_gemm_persist<256,256")  # one full round
+    assert sq.sq_gemm_kernel_name(4096, 4096, 384).startswith("k_gemm_ring<256,256")  # K % 256 != 0
     assert sq.sq_gemm_kernel_name(2400, 8000, 4096).startswith("k_gemm_ring<256,128")   # 320 tiles: 2 rounds
-    assert sq.sq_gemm_kernel_name(3072, 4096, 4096).startswith("k_gemm_ring<256,256")   # 192 tiles, 1 round
-    assert sq.sq_gemm_kernel_name(8192, 49152, 12288).startswith("k_gemm_ring<256,256")
+    assert sq.sq_gemm_kernel_name(3072, 4096, 4096).startswith("k_gemm_persist<256,256")   # 192 tiles, 1 round
+    assert sq.sq_gemm_kernel_name(8192, 49152, 12288).startswith("k_gemm_persist<256,256")
     assert sq.sq_gemm_kernel_name(300, 520, 1040).startswith("k_gemm_generic")
     # 896 tiles of 256 x 256 (3.5 rounds): 3 rounds of them, then the last 2048 columns as 256 x 128 tiles
     assert "whole rounds" in sq.sq_gemm_kernel_name(4096, 14336, 4096)

@@ -129,6 +129,7 @@ def test_pipeline_matches_oracle(M, K, N, dtype, gran, alpha, T, y_dtype):
 # kernel-name fragment the shape must select).
 DEPLOYED_EPILOGUE = [
     (4100, 384, 16392, "k_gemm_ring<256,256,4,2,2> (256x256"),        # 256 x 256 tiles, ragged M
+    (4100, 512, 8200, "k_gemm_persist<256,256,4,2,2>"),               # persistent 256 x 256, ragged M and N
     (500, 128, 66536, "on the remaining columns"),                   # column split, ragged M and last launch
     (2100, 384, 3000, "k_gemm_ring<256,128,4,2,3> (256x128"),        # 256 x 128 tiles, ragged M and N
     (33000, 256, 104, "k_gemm_ring<128,128,2,4,2>"),                 # 128 x 128 tiles, N < one tile
