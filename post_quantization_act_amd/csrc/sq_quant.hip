@@ -765,6 +765,153 @@ __global__ __launch_bounds__(TPB) void k_ln_quant(const bf16_t* __restrict__ x, 
     }
 }
 
+// The same LayerNorm + codes with TEAMS rows in flight per block: TEAMS teams
+// of TPB threads each walk their own token rows (the team's first row is
+// blockIdx.x * TEAMS + team, its stride gridDim.x * TEAMS), and the folded
+// gamma (and beta) sit in LDS once for the whole block instead of in every
+// thread's registers, so 3-4 wavefronts per SIMD hide each other's latency
+// where k_ln_quant has 2.  The LDS copies are split into two planes of float4
+// per 8-channel group (channels 0-3, then 4-7): a wavefront's reads of
+// consecutive groups are consecutive 16-byte slots.  The teams take the
+// block's barriers together, so every team runs the same number of rows; a
+// team whose row lies past M computes on zeros and stores nothing.
+// Arithmetic as k_ln_quant.
+template <int NV, int TPB, int TEAMS, bool kBeta>
+__global__ __launch_bounds__(TPB * TEAMS) void k_ln_quant_teams(const bf16_t* __restrict__ x, int64_t M, int64_t K,
+                                                                int64_t ld, const float* __restrict__ gamma,
+                                                                const float* __restrict__ beta, float eps,
+                                                                int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+    constexpr int W = TPB / kWave, NT = TPB * TEAMS;
+    constexpr int CAP = NV * TPB;  // groups the LDS planes hold
+    __shared__ float4 gl[2 * CAP];
+    __shared__ float4 bl[kBeta ? 2 * CAP : 1];
+    __shared__ float red_x[2][TEAMS * W], red_z[2][TEAMS * W];
+    __shared__ double red_1[2][TEAMS * W], red_2[2][TEAMS * W];
+    const int team = threadIdx.x / TPB, t = threadIdx.x % TPB;
+    const int wave = t / kWave, lane = t % kWave, w0 = team * W;
+    const int groups = (int)(K / 8);
+    for (int i = threadIdx.x; i < 2 * groups; i += NT) {
+        gl[(i & 1) * CAP + (i >> 1)] = reinterpret_cast<const float4*>(gamma)[i];  // channels 8g + 4h .. + 3
+        if constexpr (kBeta) bl[(i & 1) * CAP + (i >> 1)] = reinterpret_cast<const float4*>(beta)[i];
+    }
+    __syncthreads();
+    auto row_codes = [&](int64_t row, const uint4 (&cur)[NV], int b) {
+        float v[NV][8];
+        float xm = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const uint32_t u[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                v[q][2 * h] = bf16_lo(u[h]);
+                v[q][2 * h + 1] = bf16_hi(u[h]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xm = fmaxf(xm, fabsf(v[q][i]));
+        }
+        xm = wave_max(xm);
+        if (lane == 0) red_x[b][w0 + wave] = xm;
+        __syncthreads();
+        xm = red_x[b][w0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) xm = fmaxf(xm, red_x[b][w0 + i]);
+        int E = 0;
+        frexpf(xm, &E);
+        double s1 = 0.0, s2 = 0.0;
+#pragma unroll
+        for (int q = 0; q < NV; ++q)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float a = ldexpf(v[q][i], 39 - E);
+                s1 += (double)truncf(a);
+                s2 += (double)truncf(a * ldexpf(v[q][i], -E));
+            }
+        s1 = wave_sum_f64(s1);
+        s2 = wave_sum_f64(s2);
+        if (lane == 0) {
+            red_1[b][w0 + wave] = s1;
+            red_2[b][w0 + wave] = s2;
+        }
+        __syncthreads();
+        s1 = red_1[b][w0];
+        s2 = red_2[b][w0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) {
+            s1 += red_1[b][w0 + i];
+            s2 += red_2[b][w0 + i];
+        }
+        double mu = 0.0, var = 0.0;
+        if (xm > 0.0f) {
+            mu = ldexp(s1, E - 39) / (double)K;
+            var = ldexp(s2, 2 * E - 39) / (double)K - mu * mu;
+            if (var < 0.0) var = 0.0;
+        }
+        const float mu32 = (float)mu, rstd32 = (float)(1.0 / sqrt(var + (double)eps));
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NV; ++q) {
+            const int g = t + q * TPB;
+            const bool in = q < NV - 1 || g < groups;
+            const int gc = in ? g : groups - 1;
+            const float4 ga = gl[gc], gb = gl[CAP + gc];
+            const float gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+            float bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if constexpr (kBeta) {
+                const float4 ba = bl[gc], bb = bl[CAP + gc];
+                bw[0] = ba.x; bw[1] = ba.y; bw[2] = ba.z; bw[3] = ba.w;
+                bw[4] = bb.x; bw[5] = bb.y; bw[6] = bb.z; bw[7] = bb.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float n = (v[q][i] - mu32) * rstd32;
+                const float tt = n * gw[i];
+                v[q][i] = kBeta ? tt + bw[i] : tt;
+                m = fmaxf(m, in ? fabsf(v[q][i]) : 0.0f);
+            }
+        }
+        m = wave_max(m);
+        if (lane == 0) red_z[b][w0 + wave] = m;
+        __syncthreads();
+        m = red_z[b][w0];
+#pragma unroll
+        for (int i = 1; i < W; ++i) m = fmaxf(m, red_z[b][w0 + i]);
+        if (row >= M) return;  // a team past the last row: nothing to store
+        float scale, r;
+        group_scale(m, scale, r);
+        if (t == 0) x_scale[row] = scale;
+        auto code_row = [&](auto fast) {
+#pragma unroll
+            for (int q = 0; q < NV; ++q) {
+                const int g = t + q * TPB;
+                if (q < NV - 1 || g < groups) {
+                    int c[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
+                    st8_stream(xq + row * K + (int64_t)g * 8,
+                               make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+                }
+            }
+        };
+        if (r <= 3.402823466e38f) code_row(std::true_type{});
+        else code_row(std::false_type{});
+    };
+    // rows base + team, base stepping by the block's share; two rows per
+    // iteration with two load buffers, as k_ln_quant; the loop bounds are the
+    // same for every team (barriers)
+    const int64_t stride = (int64_t)gridDim.x * TEAMS;
+    uint4 da[NV], db[NV];
+    int64_t base = (int64_t)blockIdx.x * TEAMS;
+    if (base < M) load_row_groups<NV, TPB>(x, base + team, M, ld, groups, t, da);
+    for (; base < M; base += 2 * stride) {
+        load_row_groups<NV, TPB>(x, base + stride + team, M, ld, groups, t, db);
+        row_codes(base + team, da, 0);
+        if (base + stride >= M) break;
+        load_row_groups<NV, TPB>(x, base + 2 * stride + team, M, ld, groups, t, da);
+        row_codes(base + stride + team, db, 1);
+    }
+}
+
 template <typename T, int NV, int WPR>
 static void launch_act_rows(const T* x, int64_t M, int64_t K, int64_t ld, const float* inv_s, int mode, int8_t* xq,
                             float* x_scale, uint32_t* gmax, hipStream_t st) {
@@ -912,9 +1059,30 @@ static hipError_t launch_ln_rows(const bf16_t* x, int64_t M, int64_t K, int64_t 
     return hipGetLastError();
 }
 
+// k_ln_quant_teams: one block per CU (its LDS holds gamma and beta), at most
+// ceil(M / TEAMS) blocks.
+template <int NV, int TPB, int TEAMS>
+static hipError_t launch_ln_teams(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* gamma,
+                                  const float* beta, float eps, int8_t* xq, float* x_scale, hipStream_t st) {
+    const int64_t groups = K / 8;
+    if (groups <= (int64_t)(NV - 1) * TPB || groups > (int64_t)NV * TPB) return hipErrorInvalidValue;
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+        cus = 256;
+    const dim3 grid((unsigned)std::min<int64_t>((M + TEAMS - 1) / TEAMS, cus));
+    if (beta)
+        hipLaunchKernelGGL((k_ln_quant_teams<NV, TPB, TEAMS, true>), grid, dim3(TPB * TEAMS), 0, st, x, M, K, ld, gamma,
+                           beta, eps, xq, x_scale);
+    else
+        hipLaunchKernelGGL((k_ln_quant_teams<NV, TPB, TEAMS, false>), grid, dim3(TPB * TEAMS), 0, st, x, M, K, ld,
+                           gamma, beta, eps, xq, x_scale);
+    return hipGetLastError();
+}
+
 // Threads per row grow with K so that each thread keeps at most 6 groups
-// (48 channels, with their gamma and beta) in registers; NV is always
-// ceil(groups / TPB).
+// (48 channels, with their gamma and beta) in registers up to 12288
+// channels; NV is always ceil(groups / TPB).
 hipError_t launch_ln_quant(const void* x, int64_t M, int64_t K, int64_t ld, const float* gamma, const float* beta,
                            float eps, int8_t* xq, float* x_scale, hipStream_t st) {
     if (M <= 0) return hipSuccess;
@@ -929,10 +1097,16 @@ hipError_t launch_ln_quant(const void* x, int64_t M, int64_t K, int64_t ld, cons
     if (groups <= 512) SQ_LN(4, 128);
     if (groups <= 768) SQ_LN(3, 256);
     if (groups <= 1024) SQ_LN(4, 256);
+#define SQ_LNT(NV, TPB, TEAMS) \
+    return launch_ln_teams<NV, TPB, TEAMS>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st)
     if (groups <= 1280) SQ_LN(5, 256);
     if (groups <= 1536) SQ_LN(6, 256);
-    if (groups <= 2048) SQ_LN(4, 512);
+    // beyond 12288 channels two teams of 512 threads share gamma/beta in LDS
+    // (4 wavefronts per SIMD): 141 vs 155 us at 8192x16384; below, the teams
+    // form was slower (103 vs 96 us at 8192x12288 with three teams of 256)
+    if (groups <= 2048) SQ_LNT(4, 512, 2);
 #undef SQ_LN
+#undef SQ_LNT
     return hipErrorNotSupported;
 }
 

@@ -37,7 +37,11 @@ def _rows(M, K, seed):
 
 
 @pytest.mark.parametrize("M,K", [(130, 256), (13, 1024), (64, 2048), (37, 4096), (9, 8192), (40, 12288),
-                                 (5, 16384)])
+                                 (5, 16384),
+                                 # rows shared by teams of one block: more rows than teams in the grid, a last
+                                 # pass where most teams are past M, fewer rows than one block's teams, ragged
+                                 # channel groups
+                                 (800, 12288), (770, 10256), (517, 16384), (3, 12288), (1000, 9232)])
 @pytest.mark.parametrize("with_beta", [True, False])
 def test_layernorm_quant_matches_oracle(M, K, with_beta):
     print(f"layernorm M={M} K={K} beta={with_beta}", flush=True)
