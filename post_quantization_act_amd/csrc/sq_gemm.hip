@@ -1309,7 +1309,7 @@ static hipError_t launch_gemm(const int8_t* xq, const float* x_scale, bool per_t
             break;
         }
         case GemmPath::kRing256x128:
-            launch_ring<256, 128, 4, 2, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 8,
+            launch_ring<256, 128, 4, 2, 3>(xq, x_scale, per_tensor, wq, w_scale, M, N, K, y, y_bf16, acc_out, op, 4,
                                            st);
             break;
         case GemmPath::kRing128:

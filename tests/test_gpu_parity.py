@@ -124,6 +124,37 @@ def test_pipeline_matches_oracle(M, K, N, dtype, gran, alpha, T, y_dtype):
     _compare(b, o, alpha, y_dtype)
 
 
+def _random_cases(n, seed):
+    """n seeded draws over the path's shape space: M in [1, 700], K a multiple
+    of 16 in [16, 3072], N in [1, 1200] (a third of them multiples of 8),
+    bf16 or fp32 inputs, either granularity, alpha from a grid, the deployed
+    or the accumulator-storing epilogue."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(r.integers(1, 701))
+        K = 16 * int(r.integers(1, 193))
+        N = int(r.integers(1, 1201))
+        if i % 3 == 0:
+            N = 8 * max(1, N // 8)
+        dtype = torch.bfloat16 if r.random() < 0.75 else torch.float32
+        gran = sq.SQ_PER_TOKEN if r.random() < 0.7 else sq.SQ_PER_TENSOR
+        alpha = float(r.choice([0.0, 0.25, 0.4, 0.5, 0.6, 0.75, 0.85, 1.0]))
+        T = int(r.integers(1, 400))
+        out.append((M, K, N, dtype, gran, alpha, T, bool(r.random() < 0.5)))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,dtype,gran,alpha,T,with_acc", _random_cases(16, 20261203))
+def test_random_shapes_match_oracle(M, K, N, dtype, gran, alpha, T, with_acc):
+    """Seeded random shapes, every output compared with the oracle's."""
+    _say(f"random M={M} K={K} N={N} {dtype} gran={gran} alpha={alpha} T={T} acc={with_acc}")
+    x, w, calib = _inputs(M, K, N, dtype, seed=M + 13 * K + 7 * N, T=T)
+    b = _run_gpu(x.to(DEV), w.to(DEV), calib.to(DEV), alpha, gran, torch.bfloat16, with_acc=with_acc)
+    o = oracle.w8a8_linear(_np(x), _np(w), alpha, gran, calib=_np(calib), nthreads=8)
+    _compare(b, o, alpha, torch.bfloat16)
+
+
 # Shapes whose bf16 output takes the LDS-staged epilogue (N % 8 == 0, no int32
 # accumulator store) with ragged edges, one per tile launch: (M, K, N, the
 # kernel-name fragment the shape must select).
