@@ -620,40 +620,63 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 }
 
 // One token row per TPB threads (TPB / 64 wavefronts), rows walked with a
-// grid stride.  Thread t owns the 8-channel groups t + TPB q (q < NV) of
-// every row and keeps their folded gamma (and beta) in registers for all its
-// rows; the next row's loads are in flight while the current row is reduced,
-// normalised and coded.  Three reductions per row (max |x|, the two grid
-// sums, max |z|) cross the wavefronts through LDS slots that alternate
-// between rows, so each costs one barrier.
-template <int NV, int TPB, bool kBeta>
-__global__ __launch_bounds__(TPB) void k_ln_quant(const bf16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld,
-                                                  const float* __restrict__ gamma, const float* __restrict__ beta,
-                                                  float eps, int8_t* __restrict__ xq, float* __restrict__ x_scale) {
-    constexpr int W = TPB / kWave;
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave, t = threadIdx.x;
+// grid stride; TEAMS teams of TPB threads per block each take their own rows
+// (the team's first row is blockIdx.x * TEAMS + team, its stride
+// gridDim.x * TEAMS).  Thread t of a team owns the 8-channel groups
+// t + TPB q (q < NV) of every row.  The folded gamma (and beta) of those
+// groups stay in the thread's registers for all its rows when TEAMS == 1;
+// with TEAMS > 1 they sit in LDS once for the whole block (two planes of
+// float4 per group, channels 0-3 then 4-7, so a wavefront's reads of
+// consecutive groups are consecutive 16-byte slots) and the registers they
+// free let more wavefronts per SIMD hide each other's latency.  Rows go
+// through two load buffers, so one row's loads are in flight while the other
+// is reduced, normalised and coded.  Three reductions per row (max |x|, the
+// two grid sums, max |z|) cross the team's wavefronts through LDS slots that
+// alternate between rows, one barrier each; the teams take those barriers
+// together, so every team runs the same number of rows and a team whose row
+// lies past M computes on zeros and stores nothing.
+template <int NV, int TPB, int TEAMS, bool kBeta>
+__global__ __launch_bounds__(TPB * TEAMS) void k_ln_quant(const bf16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          int64_t ld, const float* __restrict__ gamma,
+                                                          const float* __restrict__ beta, float eps,
+                                                          int8_t* __restrict__ xq, float* __restrict__ x_scale) {
+    constexpr int W = TPB / kWave, NT = TPB * TEAMS;
+    constexpr bool kLdsGB = TEAMS > 1;
+    constexpr int CAP = NV * TPB;  // groups the LDS planes hold
+    const int team = TEAMS > 1 ? (int)threadIdx.x / TPB : 0;
+    const int t = TEAMS > 1 ? (int)threadIdx.x % TPB : (int)threadIdx.x;
+    const int wave = t / kWave, lane = t % kWave, w0 = team * W;
     const int groups = (int)(K / 8);
+    __shared__ float4 gl[kLdsGB ? 2 * CAP : 1];
+    __shared__ float4 bl[kLdsGB && kBeta ? 2 * CAP : 1];
+    __shared__ float red_x[2][TEAMS * W], red_z[2][TEAMS * W];
+    __shared__ double red_1[2][TEAMS * W], red_2[2][TEAMS * W];
     // groups past the row end (last q only) take the last group's gamma/beta;
     // their x is zero and they are left out of the max and the stores
-    float gw[NV][8], bw[NV][8];
+    float gr[kLdsGB ? 1 : NV][8], br[kLdsGB ? 1 : NV][8];
+    if constexpr (kLdsGB) {
+        for (int i = threadIdx.x; i < 2 * groups; i += NT) {
+            gl[(i & 1) * CAP + (i >> 1)] = reinterpret_cast<const float4*>(gamma)[i];  // channels 8g + 4h .. + 3
+            if constexpr (kBeta) bl[(i & 1) * CAP + (i >> 1)] = reinterpret_cast<const float4*>(beta)[i];
+        }
+        __syncthreads();
+    } else {
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-        const int g = t + q * TPB;
-        const int64_t gc = (q < NV - 1 || g < groups) ? g : groups - 1;
-        const float4 a = *reinterpret_cast<const float4*>(gamma + gc * 8);
-        const float4 b = *reinterpret_cast<const float4*>(gamma + gc * 8 + 4);
-        gw[q][0] = a.x; gw[q][1] = a.y; gw[q][2] = a.z; gw[q][3] = a.w;
-        gw[q][4] = b.x; gw[q][5] = b.y; gw[q][6] = b.z; gw[q][7] = b.w;
-        if constexpr (kBeta) {
-            const float4 c = *reinterpret_cast<const float4*>(beta + gc * 8);
-            const float4 d = *reinterpret_cast<const float4*>(beta + gc * 8 + 4);
-            bw[q][0] = c.x; bw[q][1] = c.y; bw[q][2] = c.z; bw[q][3] = c.w;
-            bw[q][4] = d.x; bw[q][5] = d.y; bw[q][6] = d.z; bw[q][7] = d.w;
+        for (int q = 0; q < NV; ++q) {
+            const int g = t + q * TPB;
+            const int64_t gc = (q < NV - 1 || g < groups) ? g : groups - 1;
+            const float4 a = *reinterpret_cast<const float4*>(gamma + gc * 8);
+            const float4 b = *reinterpret_cast<const float4*>(gamma + gc * 8 + 4);
+            gr[q][0] = a.x; gr[q][1] = a.y; gr[q][2] = a.z; gr[q][3] = a.w;
+            gr[q][4] = b.x; gr[q][5] = b.y; gr[q][6] = b.z; gr[q][7] = b.w;
+            if constexpr (kBeta) {
+                const float4 c = *reinterpret_cast<const float4*>(beta + gc * 8);
+                const float4 d = *reinterpret_cast<const float4*>(beta + gc * 8 + 4);
+                br[q][0] = c.x; br[q][1] = c.y; br[q][2] = c.z; br[q][3] = c.w;
+                br[q][4] = d.x; br[q][5] = d.y; br[q][6] = d.z; br[q][7] = d.w;
+            }
         }
     }
-    __shared__ float red_x[2][W], red_z[2][W];
-    __shared__ double red_1[2][W], red_2[2][W];
-    const int64_t nblk = gridDim.x;
     auto row_codes = [&](int64_t row, const uint4 (&cur)[NV], int b) {
         float v[NV][8];
         float xm = 0.0f;
@@ -669,12 +692,12 @@ __global__ __launch_bounds__(TPB) void k_ln_quant(const bf16_t* __restrict__ x, 
             for (int i = 0; i < 8; ++i) xm = fmaxf(xm, fabsf(v[q][i]));
         }
         xm = wave_max(xm);
-        if constexpr (W > 1) {
-            if (lane == 0) red_x[b][wave] = xm;
+        if constexpr (W > 1 || TEAMS > 1) {
+            if (lane == 0) red_x[b][w0 + wave] = xm;
             __syncthreads();
-            xm = red_x[b][0];
+            xm = red_x[b][w0];
 #pragma unroll
-            for (int i = 1; i < W; ++i) xm = fmaxf(xm, red_x[b][i]);
+            for (int i = 1; i < W; ++i) xm = fmaxf(xm, red_x[b][w0 + i]);
         }
         int E = 0;
         frexpf(xm, &E);
@@ -690,155 +713,19 @@ __global__ __launch_bounds__(TPB) void k_ln_quant(const bf16_t* __restrict__ x, 
             }
         s1 = wave_sum_f64(s1);
         s2 = wave_sum_f64(s2);
-        if constexpr (W > 1) {
+        if constexpr (W > 1 || TEAMS > 1) {
             if (lane == 0) {
-                red_1[b][wave] = s1;
-                red_2[b][wave] = s2;
+                red_1[b][w0 + wave] = s1;
+                red_2[b][w0 + wave] = s2;
             }
             __syncthreads();
-            s1 = red_1[b][0];
-            s2 = red_2[b][0];
+            s1 = red_1[b][w0];
+            s2 = red_2[b][w0];
 #pragma unroll
             for (int i = 1; i < W; ++i) {
-                s1 += red_1[b][i];
-                s2 += red_2[b][i];
+                s1 += red_1[b][w0 + i];
+                s2 += red_2[b][w0 + i];
             }
-        }
-        double mu = 0.0, var = 0.0;
-        if (xm > 0.0f) {
-            mu = ldexp(s1, E - 39) / (double)K;
-            var = ldexp(s2, 2 * E - 39) / (double)K - mu * mu;
-            if (var < 0.0) var = 0.0;
-        }
-        const float mu32 = (float)mu, rstd32 = (float)(1.0 / sqrt(var + (double)eps));
-        float m = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NV; ++q) {
-            const bool in = q < NV - 1 || t + q * TPB < groups;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float n = (v[q][i] - mu32) * rstd32;
-                const float tt = n * gw[q][i];
-                v[q][i] = kBeta ? tt + bw[q][i] : tt;
-                m = fmaxf(m, in ? fabsf(v[q][i]) : 0.0f);
-            }
-        }
-        m = wave_max(m);
-        if constexpr (W > 1) {
-            if (lane == 0) red_z[b][wave] = m;
-            __syncthreads();
-            m = red_z[b][0];
-#pragma unroll
-            for (int i = 1; i < W; ++i) m = fmaxf(m, red_z[b][i]);
-        }
-        float scale, r;
-        group_scale(m, scale, r);
-        if (t == 0) x_scale[row] = scale;
-        auto code_row = [&](auto fast) {
-#pragma unroll
-            for (int q = 0; q < NV; ++q) {
-                const int g = t + q * TPB;
-                if (q < NV - 1 || g < groups) {
-                    int c[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
-                    st8_stream(xq + row * K + (int64_t)g * 8,
-                               make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
-                }
-            }
-        };
-        if (r <= 3.402823466e38f) code_row(std::true_type{});
-        else code_row(std::false_type{});
-    };
-    // two rows per iteration with two load buffers (no register copy between
-    // iterations that would wait for the loads in flight)
-    uint4 da[NV], db[NV];
-    int64_t row = blockIdx.x;
-    if (row < M) load_row_groups<NV, TPB>(x, row, M, ld, groups, t, da);
-    for (; row < M; row += 2 * nblk) {
-        load_row_groups<NV, TPB>(x, row + nblk, M, ld, groups, t, db);
-        row_codes(row, da, 0);
-        if (row + nblk >= M) break;
-        load_row_groups<NV, TPB>(x, row + 2 * nblk, M, ld, groups, t, da);
-        row_codes(row + nblk, db, 1);
-    }
-}
-
-// The same LayerNorm + codes with TEAMS rows in flight per block: TEAMS teams
-// of TPB threads each walk their own token rows (the team's first row is
-// blockIdx.x * TEAMS + team, its stride gridDim.x * TEAMS), and the folded
-// gamma (and beta) sit in LDS once for the whole block instead of in every
-// thread's registers, so 3-4 wavefronts per SIMD hide each other's latency
-// where k_ln_quant has 2.  The LDS copies are split into two planes of float4
-// per 8-channel group (channels 0-3, then 4-7): a wavefront's reads of
-// consecutive groups are consecutive 16-byte slots.  The teams take the
-// block's barriers together, so every team runs the same number of rows; a
-// team whose row lies past M computes on zeros and stores nothing.
-// Arithmetic as k_ln_quant.
-template <int NV, int TPB, int TEAMS, bool kBeta>
-__global__ __launch_bounds__(TPB * TEAMS) void k_ln_quant_teams(const bf16_t* __restrict__ x, int64_t M, int64_t K,
-                                                                int64_t ld, const float* __restrict__ gamma,
-                                                                const float* __restrict__ beta, float eps,
-                                                                int8_t* __restrict__ xq, float* __restrict__ x_scale) {
-    constexpr int W = TPB / kWave, NT = TPB * TEAMS;
-    constexpr int CAP = NV * TPB;  // groups the LDS planes hold
-    __shared__ float4 gl[2 * CAP];
-    __shared__ float4 bl[kBeta ? 2 * CAP : 1];
-    __shared__ float red_x[2][TEAMS * W], red_z[2][TEAMS * W];
-    __shared__ double red_1[2][TEAMS * W], red_2[2][TEAMS * W];
-    const int team = threadIdx.x / TPB, t = threadIdx.x % TPB;
-    const int wave = t / kWave, lane = t % kWave, w0 = team * W;
-    const int groups = (int)(K / 8);
-    for (int i = threadIdx.x; i < 2 * groups; i += NT) {
-        gl[(i & 1) * CAP + (i >> 1)] = reinterpret_cast<const float4*>(gamma)[i];  // channels 8g + 4h .. + 3
-        if constexpr (kBeta) bl[(i & 1) * CAP + (i >> 1)] = reinterpret_cast<const float4*>(beta)[i];
-    }
-    __syncthreads();
-    auto row_codes = [&](int64_t row, const uint4 (&cur)[NV], int b) {
-        float v[NV][8];
-        float xm = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NV; ++q) {
-            const uint32_t u[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                v[q][2 * h] = bf16_lo(u[h]);
-                v[q][2 * h + 1] = bf16_hi(u[h]);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xm = fmaxf(xm, fabsf(v[q][i]));
-        }
-        xm = wave_max(xm);
-        if (lane == 0) red_x[b][w0 + wave] = xm;
-        __syncthreads();
-        xm = red_x[b][w0];
-#pragma unroll
-        for (int i = 1; i < W; ++i) xm = fmaxf(xm, red_x[b][w0 + i]);
-        int E = 0;
-        frexpf(xm, &E);
-        double s1 = 0.0, s2 = 0.0;
-#pragma unroll
-        for (int q = 0; q < NV; ++q)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float a = ldexpf(v[q][i], 39 - E);
-                s1 += (double)truncf(a);
-                s2 += (double)truncf(a * ldexpf(v[q][i], -E));
-            }
-        s1 = wave_sum_f64(s1);
-        s2 = wave_sum_f64(s2);
-        if (lane == 0) {
-            red_1[b][w0 + wave] = s1;
-            red_2[b][w0 + wave] = s2;
-        }
-        __syncthreads();
-        s1 = red_1[b][w0];
-        s2 = red_2[b][w0];
-#pragma unroll
-        for (int i = 1; i < W; ++i) {
-            s1 += red_1[b][w0 + i];
-            s2 += red_2[b][w0 + i];
         }
         double mu = 0.0, var = 0.0;
         if (xm > 0.0f) {
@@ -852,30 +739,35 @@ __global__ __launch_bounds__(TPB * TEAMS) void k_ln_quant_teams(const bf16_t* __
         for (int q = 0; q < NV; ++q) {
             const int g = t + q * TPB;
             const bool in = q < NV - 1 || g < groups;
-            const int gc = in ? g : groups - 1;
-            const float4 ga = gl[gc], gb = gl[CAP + gc];
-            const float gw[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-            float bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-            if constexpr (kBeta) {
-                const float4 ba = bl[gc], bb = bl[CAP + gc];
-                bw[0] = ba.x; bw[1] = ba.y; bw[2] = ba.z; bw[3] = ba.w;
-                bw[4] = bb.x; bw[5] = bb.y; bw[6] = bb.z; bw[7] = bb.w;
+            float gw[8] = {0, 0, 0, 0, 0, 0, 0, 0}, bw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if constexpr (kLdsGB) {
+                const int gc = in ? g : groups - 1;
+                const float4 ga = gl[gc], gb = gl[CAP + gc];
+                gw[0] = ga.x; gw[1] = ga.y; gw[2] = ga.z; gw[3] = ga.w;
+                gw[4] = gb.x; gw[5] = gb.y; gw[6] = gb.z; gw[7] = gb.w;
+                if constexpr (kBeta) {
+                    const float4 ba = bl[gc], bb = bl[CAP + gc];
+                    bw[0] = ba.x; bw[1] = ba.y; bw[2] = ba.z; bw[3] = ba.w;
+                    bw[4] = bb.x; bw[5] = bb.y; bw[6] = bb.z; bw[7] = bb.w;
+                }
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float n = (v[q][i] - mu32) * rstd32;
-                const float tt = n * gw[i];
-                v[q][i] = kBeta ? tt + bw[i] : tt;
+                const float tt = n * (kLdsGB ? gw[i] : gr[kLdsGB ? 0 : q][i]);
+                v[q][i] = kBeta ? tt + (kLdsGB ? bw[i] : br[kLdsGB ? 0 : q][i]) : tt;
                 m = fmaxf(m, in ? fabsf(v[q][i]) : 0.0f);
             }
         }
         m = wave_max(m);
-        if (lane == 0) red_z[b][w0 + wave] = m;
-        __syncthreads();
-        m = red_z[b][w0];
+        if constexpr (W > 1 || TEAMS > 1) {
+            if (lane == 0) red_z[b][w0 + wave] = m;
+            __syncthreads();
+            m = red_z[b][w0];
 #pragma unroll
-        for (int i = 1; i < W; ++i) m = fmaxf(m, red_z[b][w0 + i]);
-        if (row >= M) return;  // a team past the last row: nothing to store
+            for (int i = 1; i < W; ++i) m = fmaxf(m, red_z[b][w0 + i]);
+        }
+        if (TEAMS > 1 && row >= M) return;  // a team past the last row: nothing to store
         float scale, r;
         group_scale(m, scale, r);
         if (t == 0) x_scale[row] = scale;
@@ -896,9 +788,10 @@ __global__ __launch_bounds__(TPB * TEAMS) void k_ln_quant_teams(const bf16_t* __
         if (r <= 3.402823466e38f) code_row(std::true_type{});
         else code_row(std::false_type{});
     };
-    // rows base + team, base stepping by the block's share; two rows per
-    // iteration with two load buffers, as k_ln_quant; the loop bounds are the
-    // same for every team (barriers)
+    // rows base + team, base stepping by the grid's share; two rows per
+    // iteration with two load buffers (no register copy between iterations
+    // that would wait for the loads in flight); the loop bounds are the same
+    // for every team
     const int64_t stride = (int64_t)gridDim.x * TEAMS;
     uint4 da[NV], db[NV];
     int64_t base = (int64_t)blockIdx.x * TEAMS;
@@ -1032,14 +925,16 @@ hipError_t launch_codes_both(const void* w, int64_t K, int64_t N, int64_t ldw, c
     return hipGetLastError();
 }
 
-// Blocks per CU of k_ln_quant<NV, TPB, *>: what its register footprint lets
-// reside at once (the grid walks all rows with that many blocks).
+// Blocks per CU of k_ln_quant<NV, TPB, 1, *>: what its register footprint
+// lets reside at once (the grid walks all rows with that many blocks).
 static int ln_blocks_per_cu(int nv, int tpb) {
     const int waves_per_simd = nv <= 1 ? 8 : nv <= 2 ? 5 : nv <= 4 ? 3 : 2;
     return std::max(1, waves_per_simd * 4 / (tpb / kWave));
 }
 
-template <int NV, int TPB>
+// TEAMS == 1: the resident blocks per CU; TEAMS > 1: one block per CU (its
+// LDS holds gamma and beta), at most ceil(M / TEAMS) blocks.
+template <int NV, int TPB, int TEAMS>
 static hipError_t launch_ln_rows(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* gamma,
                                  const float* beta, float eps, int8_t* xq, float* x_scale, hipStream_t st) {
     // the kernel reads groups t + TPB q unchecked for q < NV - 1
@@ -1049,34 +944,14 @@ static hipError_t launch_ln_rows(const bf16_t* x, int64_t M, int64_t K, int64_t 
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                  hipSuccess || cus <= 0)
         cus = 256;
-    const dim3 grid((unsigned)std::min<int64_t>(M, (int64_t)cus * ln_blocks_per_cu(NV, TPB)));
+    const int64_t per_cu = TEAMS > 1 ? 1 : ln_blocks_per_cu(NV, TPB);
+    const dim3 grid((unsigned)std::min<int64_t>((M + TEAMS - 1) / TEAMS, (int64_t)cus * per_cu));
     if (beta)
-        hipLaunchKernelGGL((k_ln_quant<NV, TPB, true>), grid, dim3(TPB), 0, st, x, M, K, ld, gamma, beta, eps, xq,
-                           x_scale);
-    else
-        hipLaunchKernelGGL((k_ln_quant<NV, TPB, false>), grid, dim3(TPB), 0, st, x, M, K, ld, gamma, beta, eps, xq,
-                           x_scale);
-    return hipGetLastError();
-}
-
-// k_ln_quant_teams: one block per CU (its LDS holds gamma and beta), at most
-// ceil(M / TEAMS) blocks.
-template <int NV, int TPB, int TEAMS>
-static hipError_t launch_ln_teams(const bf16_t* x, int64_t M, int64_t K, int64_t ld, const float* gamma,
-                                  const float* beta, float eps, int8_t* xq, float* x_scale, hipStream_t st) {
-    const int64_t groups = K / 8;
-    if (groups <= (int64_t)(NV - 1) * TPB || groups > (int64_t)NV * TPB) return hipErrorInvalidValue;
-    int cus = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                 hipSuccess || cus <= 0)
-        cus = 256;
-    const dim3 grid((unsigned)std::min<int64_t>((M + TEAMS - 1) / TEAMS, cus));
-    if (beta)
-        hipLaunchKernelGGL((k_ln_quant_teams<NV, TPB, TEAMS, true>), grid, dim3(TPB * TEAMS), 0, st, x, M, K, ld, gamma,
+        hipLaunchKernelGGL((k_ln_quant<NV, TPB, TEAMS, true>), grid, dim3(TPB * TEAMS), 0, st, x, M, K, ld, gamma,
                            beta, eps, xq, x_scale);
     else
-        hipLaunchKernelGGL((k_ln_quant_teams<NV, TPB, TEAMS, false>), grid, dim3(TPB * TEAMS), 0, st, x, M, K, ld,
-                           gamma, beta, eps, xq, x_scale);
+        hipLaunchKernelGGL((k_ln_quant<NV, TPB, TEAMS, false>), grid, dim3(TPB * TEAMS), 0, st, x, M, K, ld, gamma,
+                           beta, eps, xq, x_scale);
     return hipGetLastError();
 }
 
@@ -1088,25 +963,23 @@ hipError_t launch_ln_quant(const void* x, int64_t M, int64_t K, int64_t ld, cons
     if (M <= 0) return hipSuccess;
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const int64_t groups = K / 8;
-#define SQ_LN(NV, TPB) return launch_ln_rows<NV, TPB>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st)
-    if (groups <= 64) SQ_LN(1, 64);
-    if (groups <= 128) SQ_LN(2, 64);
-    if (groups <= 192) SQ_LN(3, 64);
-    if (groups <= 256) SQ_LN(4, 64);
-    if (groups <= 384) SQ_LN(3, 128);
-    if (groups <= 512) SQ_LN(4, 128);
-    if (groups <= 768) SQ_LN(3, 256);
-    if (groups <= 1024) SQ_LN(4, 256);
-#define SQ_LNT(NV, TPB, TEAMS) \
-    return launch_ln_teams<NV, TPB, TEAMS>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st)
-    if (groups <= 1280) SQ_LN(5, 256);
-    if (groups <= 1536) SQ_LN(6, 256);
+#define SQ_LN(NV, TPB, TEAMS) \
+    return launch_ln_rows<NV, TPB, TEAMS>(xb, M, K, ld, gamma, beta, eps, xq, x_scale, st)
+    if (groups <= 64) SQ_LN(1, 64, 1);
+    if (groups <= 128) SQ_LN(2, 64, 1);
+    if (groups <= 192) SQ_LN(3, 64, 1);
+    if (groups <= 256) SQ_LN(4, 64, 1);
+    if (groups <= 384) SQ_LN(3, 128, 1);
+    if (groups <= 512) SQ_LN(4, 128, 1);
+    if (groups <= 768) SQ_LN(3, 256, 1);
+    if (groups <= 1024) SQ_LN(4, 256, 1);
+    if (groups <= 1280) SQ_LN(5, 256, 1);
+    if (groups <= 1536) SQ_LN(6, 256, 1);
     // beyond 12288 channels two teams of 512 threads share gamma/beta in LDS
     // (4 wavefronts per SIMD): 141 vs 155 us at 8192x16384; below, the teams
     // form was slower (103 vs 96 us at 8192x12288 with three teams of 256)
-    if (groups <= 2048) SQ_LNT(4, 512, 2);
+    if (groups <= 2048) SQ_LN(4, 512, 2);
 #undef SQ_LN
-#undef SQ_LNT
     return hipErrorNotSupported;
 }
 
