@@ -450,6 +450,17 @@ def _attn_proj_step(torch, sq, synth, pipeline, dev, tm):
     return r
 
 
+def _rel_error(torch, sq, dev, y_ref):
+    """||y - y_ref||_F / ||y_ref||_F of an fp32 y against an fp64 y_ref, by the library."""
+    ws = torch.empty(sq.sq_workspace_size(sq.SQ_OP_REL_ERROR, *y_ref.shape, 0), dtype=torch.uint8, device=dev)
+    err = torch.empty(1, dtype=torch.float64, device=dev)
+
+    def rel(y):
+        sq.sq_rel_error(y, y_ref, err, ws)
+        return float(err.item())
+    return rel
+
+
 def _alpha_sweep(torch, sq, pipeline, dev, st):
     cfg, inp, b = st["cfg"], st["inp"], st["b"]
     M, K, N = cfg.M, cfg.K, cfg.N
@@ -457,8 +468,15 @@ def _alpha_sweep(torch, sq, pipeline, dev, st):
     pipeline.calibrate(inp.calib, b.amax_x)
     rows = torch.arange(0, M, M // 256, device=dev)[:256]
     xs_ = inp.x[rows].contiguous()
-    y_ref = xs_.double() @ inp.w.double()
-    ref_norm = float(torch.linalg.norm(y_ref))
+    y_ref = torch.empty(256, N, dtype=torch.float64, device=dev)
+    sq.sq_matmul_f64(xs_, inp.w, y_ref)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    sq.sq_matmul_f64(xs_, inp.w, y_ref)
+    e1.record()
+    torch.cuda.synchronize()
+    ref_us = e0.elapsed_time(e1) * 1e3
+    rel = _rel_error(torch, sq, dev, y_ref)
     bs = pipeline.W8A8Buffers.allocate(256, N, K, sq.SQ_PER_TOKEN, dev, y_dtype=torch.float32)
     bs.amax_x.copy_(b.amax_x)
     sweep = {}
@@ -467,14 +485,14 @@ def _alpha_sweep(torch, sq, pipeline, dev, st):
         sq.sq_smooth_factors(bs.amax_x, None, a, bs.s, bs.inv_s, bs.amax_w)
         sq.sq_quant_weight(inp.w, bs.s, bs.wq, bs.w_scale, bs.ws_w)
         pipeline.forward(xs_, sq.SQ_PER_TOKEN, bs, smoothed=True)
-        sweep[str(a)] = round(float(torch.linalg.norm(bs.y.double() - y_ref)) / ref_norm, 6)
+        sweep[str(a)] = round(rel(bs.y), 6)
     sq.sq_quant_weight(inp.w, None, bs.wq, bs.w_scale, bs.ws_w)
     pipeline.forward(xs_, sq.SQ_PER_TOKEN, bs, smoothed=False)
-    base_tok = float(torch.linalg.norm(bs.y.double() - y_ref)) / ref_norm
+    base_tok = rel(bs.y)
     bt = pipeline.W8A8Buffers.allocate(256, N, K, sq.SQ_PER_TENSOR, dev, y_dtype=torch.float32)
     sq.sq_quant_weight(inp.w, None, bt.wq, bt.w_scale, bt.ws_w)
     pipeline.forward(xs_, sq.SQ_PER_TENSOR, bt, smoothed=False)
-    base_ten = float(torch.linalg.norm(bt.y.double() - y_ref)) / ref_norm
+    base_ten = rel(bt.y)
     grid = [round(0.05 * i, 2) for i in range(21)]
     t0 = time.perf_counter()
     best, errs = pipeline.search_alpha(xs_, inp.w, b.amax_x, grid)
@@ -484,6 +502,8 @@ def _alpha_sweep(torch, sq, pipeline, dev, st):
               "errors": {f"{a:.2f}": round(e, 6) for a, e in errs.items()}}
     r = {"workload": cfg.name, "sample_tokens": 256, "output": "fp32", "reference": "X W in fp64",
          "search": search, "metric": "relative Frobenius error", "smoothed_per_token": sweep,
+         "reference_product": {"us": round(ref_us, 1),
+                               "fp64_TFLOPs": round(2.0 * 256 * N * K / (ref_us * 1e-6) / 1e12, 2)},
          "unsmoothed_per_token": round(base_tok, 6), "unsmoothed_per_tensor": round(base_ten, 6)}
     del bs, bt, y_ref
     torch.cuda.empty_cache()
@@ -520,11 +540,12 @@ def _comparator(torch, sq, synth, pipeline, dev, tm):
     ops = 2.0 * M * N * K
     inp = sets[0]
     rows = torch.arange(0, M, M // 256, device=dev)[:256]
-    y_ref = inp.x[rows].double() @ inp.w.double()
-    nrm = float(torch.linalg.norm(y_ref))
+    y_ref = torch.empty(256, N, dtype=torch.float64, device=dev)
+    sq.sq_matmul_f64(inp.x[rows].contiguous(), inp.w, y_ref)
+    rel = _rel_error(torch, sq, dev, y_ref)
 
     def err(y):
-        return round(float(torch.linalg.norm(y[rows].double() - y_ref)) / nrm, 6)
+        return round(rel(y[rows].contiguous()), 6)
 
     b32 = pipeline.W8A8Buffers.allocate(M, N, K, sq.SQ_PER_TOKEN, dev, y_dtype=torch.float32)
     b32.amax_x.copy_(sqb[0].amax_x)

@@ -96,7 +96,8 @@ typedef enum {
     SQ_OP_QUANT_ACT = 3,
     SQ_OP_GEMM_W8A8 = 4,
     SQ_OP_PREPARE_WEIGHTS = 5,
-    SQ_OP_PREPARE_AND_QUANT_ACT = 6
+    SQ_OP_PREPARE_AND_QUANT_ACT = 6,
+    SQ_OP_REL_ERROR = 7
 } sq_op;
 
 /*
@@ -379,6 +380,37 @@ sq_status sq_gather_outliers(const void *x, sq_dtype xt, int64_t M, int64_t K, i
 sq_status sq_gemm_w8a8_outlier(const int8_t *xq, const float *x_scale, const int8_t *wq, const float *w_scale,
                                int64_t M, int64_t N, int64_t K, const void *x_o, const void *w_ot, int64_t kp,
                                const int32_t *count, void *y, sq_dtype yt, hipStream_t stream);
+
+/*
+ * Criterion of the offline migration-strength search (page "4.2 W8A8 量化与
+ * SmoothQuant" section 5.2: a one-time grid search over alpha on calibration
+ * data; section 4 of the same page: 0.5 is the usual value, up to 0.75 for
+ * models with severe activation outliers).  The pages score each alpha by
+ * validation perplexity; without a model, the layer-level reading scores it by
+ * the error of the quantized layer's output: for each alpha the caller runs
+ * steps 2-5 with an fp32 y and compares it with the same product in fp64:
+ *
+ * sq_matmul_f64: y_ref[m, n] = sum_k x[m, k] w[k, n], every product and sum
+ *   in fp64 (bf16 and fp32 inputs widen exactly; the order of the sum over k
+ *   is ascending within chunks of 16 and the chunks ascending, so y_ref is
+ *   within K * 2^-53 * sum_k |x w| of the exact sum).  x [M, K] row-major,
+ *   dtype xt, row stride ldx; w [K, N] row-major, dtype wt, row stride ldw
+ *   (element alignment suffices for both); y_ref [M, N] fp64 out, dense,
+ *   8-byte aligned, owned by the caller.  K % 16 == 0 as everywhere;
+ *   N <= 65535 * 128.  Plain CUDA-core fp64 FMAs: an offline helper, not part
+ *   of the runtime path.
+ * sq_rel_error: err[0] = ||y - y_ref||_F / ||y_ref||_F in fp64 over the M * N
+ *   elements of y [M, N] fp32 (dense, 4-byte aligned) and y_ref [M, N] fp64
+ *   (dense, 8-byte aligned).  err: one fp64 out, device memory.  ws: device
+ *   workspace of sq_workspace_size(SQ_OP_REL_ERROR, M, N, 0, 0) bytes, 8-byte
+ *   aligned, scratch.  The partial sums are added in a fixed order, so the
+ *   result does not depend on scheduling.  A y_ref of all zeros gives the
+ *   quotient's IEEE value (NaN or infinity); M * N == 0 gives NaN.
+ */
+sq_status sq_matmul_f64(const void *x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const void *w,
+                        sq_dtype wt, int64_t N, int64_t ldw, double *y_ref, hipStream_t stream);
+sq_status sq_rel_error(const float *y, const double *y_ref, int64_t M, int64_t N, double *err, void *ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace the call `op` needs for these sizes (0 if none).
  * Sizes the call does not use are ignored. */

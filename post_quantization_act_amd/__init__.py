@@ -24,7 +24,7 @@ __all__ = [
     "sq_gemm_w8a8", "sq_prepare_weights", "sq_prepare_and_quant_act", "SQ_OP_PREPARE_WEIGHTS",
     "SQ_OP_PREPARE_AND_QUANT_ACT", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
     "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier",
-    "sq_gemm_outlier_kernel_name", "sq_workspace_size",
+    "sq_gemm_outlier_kernel_name", "sq_matmul_f64", "sq_rel_error", "SQ_OP_REL_ERROR", "sq_workspace_size",
     "sq_status_str", "sq_last_error", "sq_version", "sq_gemm_kernel_name", "EXPORTED_SYMBOLS",
 ]
 
@@ -34,12 +34,12 @@ _LIB_PATH = os.path.join(_HERE, "libsq.so")
 SQ_F32, SQ_BF16 = 0, 1
 SQ_PER_TOKEN, SQ_PER_TENSOR = 0, 1
 (SQ_OP_CALIB_ABSMAX, SQ_OP_SMOOTH_FACTORS, SQ_OP_QUANT_WEIGHT, SQ_OP_QUANT_ACT, SQ_OP_GEMM_W8A8, SQ_OP_PREPARE_WEIGHTS,
- SQ_OP_PREPARE_AND_QUANT_ACT) = range(7)
+ SQ_OP_PREPARE_AND_QUANT_ACT, SQ_OP_REL_ERROR) = range(8)
 
 EXPORTED_SYMBOLS = (
     "sq_calib_absmax", "sq_calib_reset", "sq_smooth_factors", "sq_quant_weight", "sq_quant_weight_noalloc",
     "sq_quant_act", "sq_gemm_w8a8", "sq_prepare_weights", "sq_prepare_and_quant_act", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm", "sq_layernorm_quant", "sq_outlier_columns",
-    "sq_gather_outliers", "sq_gemm_w8a8_outlier", "sq_workspace_size", "sq_status_str", "sq_last_error",
+    "sq_gather_outliers", "sq_gemm_w8a8_outlier", "sq_matmul_f64", "sq_rel_error", "sq_workspace_size", "sq_status_str", "sq_last_error",
     "sq_version", "sq_gemm_kernel_name", "sq_gemm_outlier_kernel_name",
 )
 
@@ -84,10 +84,13 @@ def lib() -> ctypes.CDLL:
     L.sq_outlier_columns.argtypes = [vp, i64, f32, vp, vp, vp, vp]
     L.sq_gather_outliers.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp, i64, vp, vp, vp]
     L.sq_gemm_w8a8_outlier.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, vp, i64, vp, vp, i32, vp]
+    L.sq_matmul_f64.argtypes = [vp, i32, i64, i64, i64, vp, i32, i64, i64, vp, vp]
+    L.sq_rel_error.argtypes = [vp, vp, i64, i64, vp, vp, sz, vp]
     for f in ("sq_calib_absmax", "sq_smooth_factors", "sq_quant_weight", "sq_quant_weight_noalloc", "sq_quant_act",
               "sq_gemm_w8a8",
               "sq_prepare_weights", "sq_static_act_max", "sq_quant_act_static", "sq_fold_layernorm",
-              "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier"):
+              "sq_layernorm_quant", "sq_outlier_columns", "sq_gather_outliers", "sq_gemm_w8a8_outlier",
+              "sq_matmul_f64", "sq_rel_error"):
         getattr(L, f).restype = ctypes.c_int
     L.sq_workspace_size.argtypes = [i32, i64, i64, i64, i32]
     L.sq_workspace_size.restype = sz
@@ -429,3 +432,28 @@ def sq_gemm_w8a8_outlier(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tens
     _dense(y, "y", (M, N), y.dtype)
     _check(lib().sq_gemm_w8a8_outlier(_ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), M, N, K, _ptr(x_o),
                                       _ptr(w_ot), kp, _ptr(count), _ptr(y), _dtype(y), _stream(_dev(xq), stream)))
+
+
+# ---- alpha-search criterion ---------------------------------------------------------
+
+def sq_matmul_f64(x: torch.Tensor, w: torch.Tensor, y_ref: torch.Tensor, stream=None) -> None:
+    """y_ref [M, N] fp64 = x [M, K] . w [K, N] with every product and sum in fp64."""
+    M, K, ldx = _rows(x)
+    K2, N, ldw = _rows(w)
+    if K2 != K:
+        raise ValueError("x and w disagree on K")
+    _dense(y_ref, "y_ref", (M, N), torch.float64)
+    _check(lib().sq_matmul_f64(_ptr(x), _dtype(x), M, K, ldx, _ptr(w), _dtype(w), N, ldw, _ptr(y_ref),
+                               _stream(_dev(x), stream)))
+
+
+def sq_rel_error(y: torch.Tensor, y_ref: torch.Tensor, err: torch.Tensor, ws: torch.Tensor, stream=None) -> None:
+    """err[0] = ||y - y_ref||_F / ||y_ref||_F in fp64 (y fp32 [M, N], y_ref fp64 [M, N])."""
+    if y.dim() != 2:
+        raise ValueError("y must be 2-D")
+    M, N = y.shape
+    _dense(y, "y", (M, N), torch.float32)
+    _dense(y_ref, "y_ref", (M, N), torch.float64)
+    _dense(err, "err", (1,), torch.float64)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().sq_rel_error(_ptr(y), _ptr(y_ref), M, N, _ptr(err), _ptr(ws), nbytes, _stream(_dev(y), stream)))

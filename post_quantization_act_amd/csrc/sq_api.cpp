@@ -131,6 +131,7 @@ size_t sq_workspace_size(sq_op op, int64_t M, int64_t N, int64_t K, sq_act_gran 
         case SQ_OP_PREPARE_AND_QUANT_ACT:
             return round256(sq_workspace_size(SQ_OP_PREPARE_WEIGHTS, M, N, K, g)) +
                    sq_workspace_size(SQ_OP_QUANT_ACT, M, N, K, g);
+        case SQ_OP_REL_ERROR: return (size_t)sqk::rel_error_workspace_bytes();
         default: return 0;
     }
 }
@@ -530,6 +531,39 @@ sq_status sq_gemm_w8a8_outlier(const int8_t* xq, const float* x_scale, const int
 
 const char* sq_gemm_outlier_kernel_name(int64_t M, int64_t N, int64_t K) {
     return sqk::gemm_kernel_name(M, N, K, true);
+}
+
+sq_status sq_matmul_f64(const void* x, sq_dtype xt, int64_t M, int64_t K, int64_t ldx, const void* w, sq_dtype wt,
+                        int64_t N, int64_t ldw, double* y_ref, hipStream_t stream) {
+    const char* fn = "sq_matmul_f64";
+    SQ_TRY(check_k(fn, K));
+    if (M < 0 || N < 0 || M > kMaxMN || N > sqk::kMatmulF64MaxN)
+        return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld, N = %lld out of range (N <= %lld)", fn, (long long)M,
+                    (long long)N, (long long)sqk::kMatmulF64MaxN);
+    SQ_TRY(check_matrix(fn, "x", x, xt, M, K, ldx, false));
+    SQ_TRY(check_matrix(fn, "w", w, wt, K, N, ldw, false));
+    if (M == 0 || N == 0) return ok();
+    if (!y_ref) return fail(SQ_ERR_INVALID_ARG, "%s: y_ref is NULL", fn);
+    if (reinterpret_cast<uintptr_t>(y_ref) & 7u) return fail(SQ_ERR_INVALID_ARG, "%s: y_ref is not 8-byte aligned", fn);
+    return hip_result(sqk::launch_matmul_f64(x, xt == SQ_BF16, M, K, ldx, w, wt == SQ_BF16, N, ldw, y_ref, stream),
+                      fn);
+}
+
+sq_status sq_rel_error(const float* y, const double* y_ref, int64_t M, int64_t N, double* err, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    const char* fn = "sq_rel_error";
+    if (M < 0 || N < 0 || M > kMaxMN || N > kMaxMN)
+        return fail(SQ_ERR_INVALID_ARG, "%s: M = %lld, N = %lld out of range", fn, (long long)M, (long long)N);
+    SQ_TRY(check_vec(fn, "y", y, M * N));
+    if (M * N > 0 && !y_ref) return fail(SQ_ERR_INVALID_ARG, "%s: y_ref is NULL", fn);
+    if (reinterpret_cast<uintptr_t>(y_ref) & 7u) return fail(SQ_ERR_INVALID_ARG, "%s: y_ref is not 8-byte aligned", fn);
+    if (!err || (reinterpret_cast<uintptr_t>(err) & 7u))
+        return fail(SQ_ERR_INVALID_ARG, "%s: err is NULL or not 8-byte aligned", fn);
+    const size_t need = sq_workspace_size(SQ_OP_REL_ERROR, M, N, 0, SQ_PER_TOKEN);
+    if (!ws || ws_bytes < need || (reinterpret_cast<uintptr_t>(ws) & 7u))
+        return fail(SQ_ERR_WORKSPACE, "%s: workspace of %zu bytes at %p, need %zu bytes, 8-byte aligned", fn,
+                    ws_bytes, ws, need);
+    return hip_result(sqk::launch_rel_error(y, y_ref, M * N, err, static_cast<double*>(ws), stream), fn);
 }
 
 }  // extern "C"

@@ -85,6 +85,17 @@ hipError_t launch_gemm_w8a8_outlier(const int8_t* xq, const float* x_scale, cons
 int64_t noalloc_scratch_cols();
 hipError_t noalloc_scratch(int device, void** out);
 
+// The alpha search's criterion: y[M, N] = x w in fp64 (x [M, K], w [K, N],
+// bf16 or fp32, K % 16 == 0, y dense); err[0] = ||y - y_ref||_F / ||y_ref||_F
+// over n elements through partial sums in rel_error_workspace_bytes() bytes.
+// The product's grid has one y dimension per 128 output columns.
+constexpr int64_t kMatmulF64MaxN = (int64_t)65535 * 128;
+hipError_t launch_matmul_f64(const void* x, bool x_bf16, int64_t M, int64_t K, int64_t ldx, const void* w,
+                             bool w_bf16, int64_t N, int64_t ldw, double* y, hipStream_t st);
+int64_t rel_error_workspace_bytes();
+hipError_t launch_rel_error(const float* y, const double* y_ref, int64_t n, double* err, double* partial,
+                            hipStream_t st);
+
 // Static description of the GEMM kernel launch_gemm_w8a8 (outl: the outlier
 // variant) runs for this shape.
 const char* gemm_kernel_name(int64_t M, int64_t N, int64_t K, bool outl = false);

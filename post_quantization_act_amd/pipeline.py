@@ -9,10 +9,10 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (SQ_OP_PREPARE_AND_QUANT_ACT, SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_PER_TENSOR,
-               SQ_PER_TOKEN, sq_calib_absmax, sq_gather_outliers, sq_gemm_w8a8, sq_gemm_w8a8_outlier,
-               sq_outlier_columns, sq_prepare_and_quant_act, sq_prepare_weights, sq_quant_act, sq_quant_weight,
-               sq_calib_reset, sq_smooth_factors, sq_workspace_size)
+from . import (SQ_OP_PREPARE_AND_QUANT_ACT, SQ_OP_PREPARE_WEIGHTS, SQ_OP_QUANT_ACT, SQ_OP_QUANT_WEIGHT, SQ_OP_REL_ERROR,
+               SQ_PER_TENSOR, SQ_PER_TOKEN, sq_calib_absmax, sq_gather_outliers, sq_gemm_w8a8, sq_gemm_w8a8_outlier,
+               sq_matmul_f64, sq_outlier_columns, sq_prepare_and_quant_act, sq_prepare_weights, sq_quant_act,
+               sq_quant_weight, sq_calib_reset, sq_rel_error, sq_smooth_factors, sq_workspace_size)
 
 
 @dataclass
@@ -138,17 +138,18 @@ def search_alpha(x_sample: torch.Tensor, w: torch.Tensor, amax_x: torch.Tensor, 
     error.  amax_x: the calibration maxima (step 1).  Returns (best alpha,
     {alpha: error}); ties go to the first alpha of the grid.
 
-    The quantization and the INT8 GEMM are the library's kernels; the fp64
-    reference product and the two norms are torch plumbing of this offline
-    helper (they are not part of the runtime path)."""
+    Every step runs in the library: the quantization, the INT8 GEMM, the fp64
+    reference product (sq_matmul_f64) and the error (sq_rel_error); Python only
+    picks the smallest of the returned errors."""
     M, K = x_sample.shape
     N = w.shape[1]
     dev = x_sample.device
     b = W8A8Buffers.allocate(M, N, K, gran, dev, y_dtype=torch.float32)
     b.amax_x.copy_(amax_x)
-    y_ref = x_sample.double() @ w.double()
-    ref = float(torch.linalg.norm(y_ref))
-    errs = {}
+    y_ref = torch.empty(M, N, dtype=torch.float64, device=dev)
+    sq_matmul_f64(x_sample, w, y_ref)
+    ws = torch.empty(sq_workspace_size(SQ_OP_REL_ERROR, M, N, 0), dtype=torch.uint8, device=dev)
+    err = torch.empty(len(alphas), dtype=torch.float64, device=dev)
     for i, a in enumerate(alphas):
         if i == 0:
             sq_smooth_factors(b.amax_x, w, float(a), b.s, b.inv_s, b.amax_w)  # row maxima of W once
@@ -156,7 +157,8 @@ def search_alpha(x_sample: torch.Tensor, w: torch.Tensor, amax_x: torch.Tensor, 
             sq_smooth_factors(b.amax_x, None, float(a), b.s, b.inv_s, b.amax_w)
         sq_quant_weight(w, b.s, b.wq, b.w_scale, b.ws_w)
         forward(x_sample, gran, b, smoothed=True)
-        errs[float(a)] = float(torch.linalg.norm(b.y.double() - y_ref)) / ref
+        sq_rel_error(b.y, y_ref, err[i:i + 1], ws)
+    errs = dict(zip((float(a) for a in alphas), err.tolist()))
     best = min(errs, key=lambda a: (errs[a], list(errs).index(a)))
     return best, errs
 

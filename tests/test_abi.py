@@ -288,6 +288,33 @@ def test_llm_int8_entry_points_reject():
     _expect(L.sq_gemm_w8a8_outlier(*m(yt=9)), -2, "output dtype")
 
 
+def test_alpha_criterion_entry_points_reject():
+    L = _L()
+    mm = lambda **kw: [kw.get("x", FAKE), kw.get("xt", sq.SQ_BF16), 8, kw.get("K", 32), kw.get("ldx", 32), FAKE,
+                       sq.SQ_F32, kw.get("N", 24), kw.get("ldw", 24), kw.get("y", FAKE), None]
+    _expect(L.sq_matmul_f64(*mm(K=24, ldx=24)), -1, "multiple of 16")
+    _expect(L.sq_matmul_f64(*mm(xt=5)), -2, "dtype")
+    _expect(L.sq_matmul_f64(*mm(x=None)), -1, "x is NULL")
+    _expect(L.sq_matmul_f64(*mm(ldx=16)), -1, "row stride")
+    _expect(L.sq_matmul_f64(*mm(ldw=20)), -1, "row stride")
+    _expect(L.sq_matmul_f64(*mm(y=None)), -1, "y_ref is NULL")
+    _expect(L.sq_matmul_f64(*mm(y=MISALIGNED)), -1, "8-byte aligned")
+    _expect(L.sq_matmul_f64(*mm(N=65535 * 128 + 1, ldw=65535 * 128 + 1)), -1, "out of range")
+    assert L.sq_matmul_f64(*mm(N=0, y=None)) == 0  # empty product: nothing enqueued
+    need = sq.sq_workspace_size(sq.SQ_OP_REL_ERROR, 8, 24, 0)
+    assert need == 8192
+    re_ = lambda **kw: [FAKE, kw.get("yr", FAKE), 8, 24, kw.get("err", FAKE), kw.get("ws", FAKE),
+                        kw.get("nb", need), None]
+    _expect(L.sq_rel_error(*re_(nb=need - 8)), -3, "workspace")
+    _expect(L.sq_rel_error(*re_(ws=None)), -3, "workspace")
+    _expect(L.sq_rel_error(*re_(err=None)), -1, "err is NULL")
+    _expect(L.sq_rel_error(*re_(err=MISALIGNED)), -1, "err is NULL or not 8-byte aligned")
+    _expect(L.sq_rel_error(*re_(yr=None)), -1, "y_ref is NULL")
+    _expect(L.sq_rel_error(*re_(yr=MISALIGNED)), -1, "y_ref is not 8-byte aligned")
+    _expect(L.sq_rel_error(None, FAKE, 8, 24, FAKE, FAKE, need, None), -1, "y is NULL")
+    _expect(L.sq_rel_error(FAKE, FAKE, -1, 24, FAKE, FAKE, need, None), -1, "out of range")
+
+
 def test_outlier_gemm_kernel_choice():
     """The outlier variant uses the same tile kernels, and the general one
     where the plain product would stream weights (M <= 16)."""
