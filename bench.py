@@ -107,13 +107,22 @@ def _traffic():
 
 
 def _cpu_model():
+    """The host's model name with its family / model / stepping numbers (some
+    hosts report only a short name) and the count of online logical CPUs."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = (p.strip() for p in line.split(":", 1))
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v
+            elif fields:
+                break
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = ", ".join(f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields)
+    return f"{name} ({ids}; {os.cpu_count()} logical CPUs online)" if ids else name
 
 
 def _say(msg):
@@ -279,6 +288,19 @@ def _step(torch, sq, synth, pipeline, dev, args):
     return head, state
 
 
+def _vendor_gemm(torch, tm, operands, ops):
+    """The same INT8 product through the vendor BLAS for comparison: torch._int_mm
+    (hipBLASLt on ROCm) on the same codes, Xq [M, K] times a column-major view
+    of Wq^T, int32 output (no dequantization epilogue, so it writes twice the
+    bytes of the library's bf16 y)."""
+    n = len(operands)
+    try:
+        t = tm(lambda i: torch._int_mm(operands[i % n][0], operands[i % n][1].t()))
+    except RuntimeError as e:  # an unsupported shape or build: recorded, not fatal
+        return {"error": str(e)[:200]}
+    return _tops(t, ops, kernel="torch._int_mm (hipBLASLt)", note="comparison only: int32 output, same codes")
+
+
 # ---- the judged kernel set ---------------------------------------------------------------
 
 def _judged_large(torch, sq, pipeline, dev, tm, st):
@@ -323,6 +345,8 @@ def _judged_large(torch, sq, pipeline, dev, tm, st):
     out["gemm"] = _tops(tm(lambda i: sq.sq_gemm_w8a8(b.xq, b.x_scale, sq.SQ_PER_TOKEN, b.wq, b.w_scale, b.y)),
                         2.0 * M * N * K, kernel=sq.sq_gemm_kernel_name(M, N, K),
                         note="operands 704 MB per call (Wq 604 MB + Xq 101 MB)")
+    out["gemm_vendor"] = _vendor_gemm(torch, tm, [(b.xq, b.wq)], 2.0 * M * N * K)
+    torch.cuda.empty_cache()
     return out
 
 
@@ -356,6 +380,7 @@ def _judged_mlp_up(torch, sq, synth, pipeline, dev, tm):
     out["gemm"] = _tops(tm(lambda i: sq.sq_gemm_w8a8(ops[i % n][0], b.x_scale, sq.SQ_PER_TOKEN, ops[i % n][1],
                                                      b.w_scale, b.y)), 2.0 * M * N * K,
                         kernel=sq.sq_gemm_kernel_name(M, N, K), pool=f"{n} operand sets of {(M * K + N * K) / 1e6:.0f} MB")
+    out["gemm_vendor"] = _vendor_gemm(torch, tm, ops, 2.0 * M * N * K)
     del ops, inp, b
     torch.cuda.empty_cache()
     return out
@@ -418,6 +443,7 @@ def _judged_attn_gemm(torch, sq, synth, pipeline, dev, tm):
     r = _tops(tm(lambda i: sq.sq_gemm_w8a8(ops[i % n][0], b.x_scale, sq.SQ_PER_TOKEN, ops[i % n][1], b.w_scale,
                                            b.y)), 2.0 * M * N * K, kernel=sq.sq_gemm_kernel_name(M, N, K),
               pool=f"{n} operand sets of {(M * K + N * K) / 1e6:.0f} MB")
+    r = {"gemm": r, "gemm_vendor": _vendor_gemm(torch, tm, ops, 2.0 * M * N * K)}
     del ops, inp, b
     torch.cuda.empty_cache()
     return r
@@ -748,7 +774,7 @@ def main():
     if "judged" in sections:
         judged["mlp_up_4096x4096x14336"] = _judged_mlp_up(torch, sq, synth, pipeline, dev, tm)
         judged["decode_16x8192x28672"] = _judged_decode(torch, sq, synth, pipeline, dev, tm)
-        judged["attn_proj_2048x4096x4096"] = {"gemm": _judged_attn_gemm(torch, sq, synth, pipeline, dev, tm)}
+        judged["attn_proj_2048x4096x4096"] = _judged_attn_gemm(torch, sq, synth, pipeline, dev, tm)
         out["judged"] = judged
     if "attn_proj" in sections:
         out["attn_proj_step"] = _attn_proj_step(torch, sq, synth, pipeline, dev, tm)
