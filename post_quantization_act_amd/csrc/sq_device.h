@@ -142,6 +142,25 @@ __device__ __forceinline__ int code8_finite(float v, float r) {
     return static_cast<int>(__builtin_amdgcn_fmed3f(t, -127.0f, 127.0f));
 }
 
+// The code of v as the low byte of a float's bit pattern, for a group whose
+// max magnitude m bounds |v| and whose r is finite: then |fl(v * r)| is at
+// most 127 (1 + 2^-23)^2 < 127.5, so no clamp is needed, and adding
+// 1.5 * 2^23 rounds fl(v * r) to an integer, half to even (the sum lies in
+// [2^23, 2^24), where the unit in the last place is 1).  The sum's bits are
+// 0x4B400000 + code, whose low byte is the code in two's complement.  The
+// product and the sum round separately (contraction is off), so the byte
+// equals code8_finite(v, r).
+__device__ __forceinline__ uint32_t code8_bounded_bits(float v, float r) {
+    return __float_as_uint(v * r + 12582912.0f);
+}
+
+// Pack the low bytes of four code8_bounded_bits patterns (a first).
+__device__ __forceinline__ uint32_t pack4_low(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a.byte0, b.byte0, 0, 0
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
 // Pack four codes (low byte first) into one dword.
 __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
     return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |

@@ -386,11 +386,20 @@ __device__ __forceinline__ void quant_act_stream_rows(int64_t bid, int64_t nblk,
             for (int q = 0; q < NV; ++q) {
                 const int64_t g = t + (int64_t)q * 256;
                 if (g < groups) {
-                    int c[8];
+                    uint2 pk;
+                    if constexpr (!kStatic && decltype(fast)::value) {
+                        // the row's own max bounds every value: no clamp
+                        uint32_t c[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
-                    const uint2 pk = make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+                        for (int i = 0; i < 8; ++i) c[i] = code8_bounded_bits(v[q][i], r);
+                        pk = make_uint2(pack4_low(c[0], c[1], c[2], c[3]), pack4_low(c[4], c[5], c[6], c[7]));
+                    } else {
+                        int c[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
+                        pk = make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+                    }
                     if constexpr (kKeepOut) *reinterpret_cast<uint2*>(xq + row * K + g * 8) = pk;
                     else st8_stream(xq + row * K + g * 8, pk);
                 }
@@ -776,12 +785,20 @@ __global__ __launch_bounds__(TPB * TEAMS) void k_ln_quant(const bf16_t* __restri
             for (int q = 0; q < NV; ++q) {
                 const int g = t + q * TPB;
                 if (q < NV - 1 || g < groups) {
-                    int c[8];
+                    uint2 pk;
+                    if constexpr (decltype(fast)::value) {
+                        // m is the max of these values: no clamp
+                        uint32_t c[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        c[i] = decltype(fast)::value ? code8_finite(v[q][i], r) : code8(v[q][i], r);
-                    st8_stream(xq + row * K + (int64_t)g * 8,
-                               make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7])));
+                        for (int i = 0; i < 8; ++i) c[i] = code8_bounded_bits(v[q][i], r);
+                        pk = make_uint2(pack4_low(c[0], c[1], c[2], c[3]), pack4_low(c[4], c[5], c[6], c[7]));
+                    } else {
+                        int c[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) c[i] = code8(v[q][i], r);
+                        pk = make_uint2(pack4(c[0], c[1], c[2], c[3]), pack4(c[4], c[5], c[6], c[7]));
+                    }
+                    st8_stream(xq + row * K + (int64_t)g * 8, pk);
                 }
             }
         };

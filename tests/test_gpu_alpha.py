@@ -116,8 +116,8 @@ def test_rel_error_matches_oracle(M, N):
 
 def test_rel_error_special_cases():
     """Equal inputs give exactly 0; an all-zero reference gives the IEEE
-    quotient (x / 0 = inf, 0 / 0 = NaN); the workspace's previous contents do
-    not matter (every partial is rewritten)."""
+    quotient (x / 0 = inf, 0 / 0 = NaN), and so does an empty one; the
+    workspace's previous contents do not matter (every partial is rewritten)."""
     ws = torch.full((sq.sq_workspace_size(sq.SQ_OP_REL_ERROR, 4, 64, 0),), 255, dtype=torch.uint8, device=DEV)
     err = torch.empty(1, dtype=torch.float64, device=DEV)
     y = torch.randn(4, 64, device=DEV)
@@ -128,3 +128,6 @@ def test_rel_error_special_cases():
     assert err.item() == float("inf")
     sq.sq_rel_error(torch.zeros(4, 64, device=DEV), z, err, ws)
     assert np.isnan(err.item())
+    err.fill_(1.0)
+    sq.sq_rel_error(torch.empty(0, 64, device=DEV), torch.empty(0, 64, dtype=torch.float64, device=DEV), err, ws)
+    assert np.isnan(err.item())  # no elements: 0 / 0
