@@ -144,28 +144,24 @@ __device__ __forceinline__ void quant_weight_tile(int64_t bid, const T* __restri
         }
         auto code_all = [&](auto fast) {
 #pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
+            for (int cc = 0; cc < 8; ++cc) {
+                if constexpr (decltype(fast)::value) {
+                    // the column's max (taken over these same fl(s_j w) values)
+                    // bounds each of them: no clamp
+                    uint32_t c[8];
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const float wp = kScaled ? sv[rr] * v[rr][cc] : v[rr][cc];
-                    if constexpr (decltype(fast)::value) {
-                        // code + 128 is an integer in [1, 255]: one byte insert
-                        // (the 0x80 flip below turns it into the int8 code)
-                        const float b = __builtin_amdgcn_fmed3f(__builtin_rintf(wp * rr_[cc]), -127.0f, 127.0f) + 128.0f;
-                        if (rr < 4) lo[cc] = __builtin_amdgcn_cvt_pk_u8_f32(b, rr, lo[cc]);
-                        else hi[cc] = __builtin_amdgcn_cvt_pk_u8_f32(b, rr - 4, hi[cc]);
-                    } else {
+                    for (int rr = 0; rr < 8; ++rr)
+                        c[rr] = code8_bounded_bits(kScaled ? sv[rr] * v[rr][cc] : v[rr][cc], rr_[cc]);
+                    lo[cc] = pack4_low(c[0], c[1], c[2], c[3]);
+                    hi[cc] = pack4_low(c[4], c[5], c[6], c[7]);
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < 8; ++rr) {
+                        const float wp = kScaled ? sv[rr] * v[rr][cc] : v[rr][cc];
                         const uint32_t c = uint32_t(code8(wp, rr_[cc])) & 0xFFu;
                         if (rr < 4) lo[cc] |= c << (8 * rr);
                         else hi[cc] |= c << (8 * (rr - 4));
                     }
-                }
-            }
-            if constexpr (decltype(fast)::value) {
-#pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    lo[cc] ^= 0x80808080u;
-                    hi[cc] ^= 0x80808080u;
                 }
             }
         };
