@@ -48,7 +48,8 @@ def _f64_bound(x, w):
     some order, so each is within K u sum_k |x w| of the exact value (the
     standard bound on a recursive sum): allow twice that between them."""
     K = x.shape[1]
-    return 2.0 * K * U64 * (np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)))
+    xf, wf = oracle.as_f32(x).astype(np.float64), oracle.as_f32(w).astype(np.float64)  # bf16 bits widened
+    return 2.0 * K * U64 * (np.abs(xf) @ np.abs(wf))
 
 
 @pytest.mark.parametrize("M,K,N,xt,wt,padx,padw", [
@@ -131,3 +132,18 @@ def test_rel_error_special_cases():
     err.fill_(1.0)
     sq.sq_rel_error(torch.empty(0, 64, device=DEV), torch.empty(0, 64, dtype=torch.float64, device=DEV), err, ws)
     assert np.isnan(err.item())  # no elements: 0 / 0
+
+
+def test_matmul_f64_unaligned_views():
+    """Operands that start mid-row (element alignment only) and odd strides."""
+    M, K, N = 33, 64, 40
+    print(f"matmul_f64 unaligned views {M}x{K}x{N}", flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(77)
+    x_full = synth.activations(M, K + 5, "normal", None, None, torch.bfloat16, g, "cpu")
+    w_full = synth.weights(K, N + 3, 0.02, torch.float32, g, "cpu")
+    x, w = x_full[:, 3:K + 3], w_full[:, 1:N + 1]
+    y = torch.empty(M, N, dtype=torch.float64, device=DEV)
+    sq.sq_matmul_f64(x_full.to(DEV)[:, 3:K + 3], w_full.to(DEV)[:, 1:N + 1], y)
+    xo, wo = synth.to_numpy(x.contiguous()), synth.to_numpy(w.contiguous())
+    assert np.all(np.abs(y.cpu().numpy() - oracle.matmul_f64(xo, wo)) <= _f64_bound(xo, wo))
