@@ -19,7 +19,7 @@ events on the library's stream.
 
 Besides the headline line, the JSON carries:
   kernels       the step's calls, averaged over the timed steps;
-  judged        every kernel of the judged set as a median of >= 50 HIP-event
+  workloads     every kernel of the per-workload set as a median of >= 50 HIP-event
                 timed calls over input pools of >= 1 GB (or single inputs
                 larger than that): calibration absmax, weight row max +
                 factors, weight codes, activation codes (per token, per
@@ -41,7 +41,7 @@ Besides the headline line, the JSON carries:
                 samples of the step's stages, scaled to the whole step.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
-                    [--sections step,judged,attn_proj,alpha,comparator,probe]
+                    [--sections step,workloads,attn_proj,alpha,comparator,probe]
 """
 from __future__ import annotations
 
@@ -64,8 +64,8 @@ INT8_PEAK_TOPS = 5000.0    # MI355X dense INT8 MFMA, TOPS (5.0 POP/s)
 METRIC = "W8A8 GEMM TOPS (% INT8 MFMA peak); quant-kernel HBM GB/s (% peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_large_8192x12288x49152_traffic.json")
 GEMM_SOURCES = [os.path.join(ROOT, "post_quantization_act_amd", "csrc", f) for f in ("sq_gemm.hip", "sq_device.h")]
-SECTIONS = ("step", "judged", "attn_proj", "alpha", "comparator", "probe")
-RUNS = 50          # HIP-event timed calls per judged row (median reported)
+SECTIONS = ("step", "workloads", "attn_proj", "alpha", "comparator", "probe")
+RUNS = 50          # HIP-event timed calls per workload row (median reported)
 POOL_BYTES = 1e9   # rotate inputs over at least this many bytes
 CPU_THREADS_MAX = 16
 
@@ -78,7 +78,7 @@ def _parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--sections", default=",".join(SECTIONS),
                    help="comma list of parts to run besides the headline step (" + ",".join(SECTIONS) + ")")
-    p.add_argument("--runs", type=int, default=RUNS, help="timed calls per judged row")
+    p.add_argument("--runs", type=int, default=RUNS, help="timed calls per workload row")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU time of the oracle samples")
     p.add_argument("--copy-probe-mb", type=int, default=0,
                    help="after timing, run one device copy of this size (for counter calibration)")
@@ -301,14 +301,14 @@ def _vendor_gemm(torch, tm, operands, ops):
     return _tops(t, ops, kernel="torch._int_mm (hipBLASLt)", note="comparison only: int32 output, same codes")
 
 
-# ---- the judged kernel set ---------------------------------------------------------------
+# ---- the per-workload kernel set -----------------------------------------------------------
 
-def _judged_large(torch, sq, pipeline, dev, tm, st):
+def _workload_large(torch, sq, pipeline, dev, tm, st):
     cfg, inp, xs, b = st["cfg"], st["inp"], st["xs"], st["b"]
     M, K, N, T = cfg.M, cfg.K, cfg.N, cfg.calib_tokens
     nx = len(xs)
     out = {}
-    _say("judged: large workload")
+    _say("workloads: large")
     out["calib_absmax"] = _rate(tm(lambda i: (sq.sq_calib_reset(b.amax_x),
                                               sq.sq_calib_absmax(inp.calib, b.amax_x))), 2 * T * K + 8 * K,
                                 input_bytes=2 * T * K, note="sq_calib_reset + sq_calib_absmax, 6.44 GB per call")
@@ -350,10 +350,10 @@ def _judged_large(torch, sq, pipeline, dev, tm, st):
     return out
 
 
-def _judged_mlp_up(torch, sq, synth, pipeline, dev, tm):
+def _workload_mlp_up(torch, sq, synth, pipeline, dev, tm):
     cfg = synth.CONFIGS[synth.MLP_UP]
     M, K, N = cfg.M, cfg.K, cfg.N
-    _say(f"judged: {cfg.name}")
+    _say(f"workloads: {cfg.name}")
     inp = synth.make(cfg, device=dev)
     b = pipeline.W8A8Buffers.allocate(M, N, K, sq.SQ_PER_TOKEN, dev)
     pipeline.calibrate(inp.calib, b.amax_x)
@@ -386,10 +386,10 @@ def _judged_mlp_up(torch, sq, synth, pipeline, dev, tm):
     return out
 
 
-def _judged_decode(torch, sq, synth, pipeline, dev, tm):
+def _workload_decode(torch, sq, synth, pipeline, dev, tm):
     cfg = synth.CONFIGS[synth.DECODE]
     M, K, N = cfg.M, cfg.K, cfg.N
-    _say(f"judged: {cfg.name}")
+    _say(f"workloads: {cfg.name}")
     inp = synth.make(cfg, device=dev)
     b = pipeline.W8A8Buffers.allocate(M, N, K, sq.SQ_PER_TOKEN, dev)
     pipeline.calibrate(inp.calib, b.amax_x)
@@ -430,7 +430,7 @@ def _judged_decode(torch, sq, synth, pipeline, dev, tm):
     return out
 
 
-def _judged_attn_gemm(torch, sq, synth, pipeline, dev, tm):
+def _workload_attn_gemm(torch, sq, synth, pipeline, dev, tm):
     cfg = synth.CONFIGS[synth.ATTN_PROJ]
     M, K, N = cfg.M, cfg.K, cfg.N
     inp = synth.make(cfg, device=dev)
@@ -763,19 +763,19 @@ def main():
     tm = _Timer(torch, args.runs)
 
     out, st = _step(torch, sq, synth, pipeline, dev, args)
-    if "judged" in sections:
-        judged = {"timing": f"median of {args.runs} HIP-event timed calls after 3 warm-up calls; inputs rotate over "
+    if "workloads" in sections:
+        rows = {"timing": f"median of {args.runs} HIP-event timed calls after 3 warm-up calls; inputs rotate over "
                             f">= {POOL_BYTES / 1e9:.0f} GB of independent copies unless one input is larger"}
-        judged["large_8192x12288x49152"] = _judged_large(torch, sq, pipeline, dev, tm, st)
+        rows["large_8192x12288x49152"] = _workload_large(torch, sq, pipeline, dev, tm, st)
     if "alpha" in sections:
         out["alpha_sweep"] = _alpha_sweep(torch, sq, pipeline, dev, st)
     del st
     torch.cuda.empty_cache()
-    if "judged" in sections:
-        judged["mlp_up_4096x4096x14336"] = _judged_mlp_up(torch, sq, synth, pipeline, dev, tm)
-        judged["decode_16x8192x28672"] = _judged_decode(torch, sq, synth, pipeline, dev, tm)
-        judged["attn_proj_2048x4096x4096"] = _judged_attn_gemm(torch, sq, synth, pipeline, dev, tm)
-        out["judged"] = judged
+    if "workloads" in sections:
+        rows["mlp_up_4096x4096x14336"] = _workload_mlp_up(torch, sq, synth, pipeline, dev, tm)
+        rows["decode_16x8192x28672"] = _workload_decode(torch, sq, synth, pipeline, dev, tm)
+        rows["attn_proj_2048x4096x4096"] = _workload_attn_gemm(torch, sq, synth, pipeline, dev, tm)
+        out["workloads"] = rows
     if "attn_proj" in sections:
         out["attn_proj_step"] = _attn_proj_step(torch, sq, synth, pipeline, dev, tm)
     if "comparator" in sections:
