@@ -59,8 +59,9 @@
  *     M, N and the token count T may be any non-negative value (ragged tails
  *     are handled).
  *     Empty problems (a zero size) enqueue nothing and return SQ_OK, except
- *     sq_gemm_w8a8 with K = 0, which writes y = 0, and sq_rel_error, which
- *     always writes its quotient (NaN over no elements).
+ *     sq_gemm_w8a8 and sq_matmul_f64 with K = 0, which write y = 0 (y_ref = 0),
+ *     and sq_rel_error, which always writes its quotient (NaN over no
+ *     elements).
  *   - Inputs must be finite; results for NaN or Inf inputs are unspecified.
  */
 #ifndef SQ_H

@@ -147,3 +147,14 @@ def test_matmul_f64_unaligned_views():
     sq.sq_matmul_f64(x_full.to(DEV)[:, 3:K + 3], w_full.to(DEV)[:, 1:N + 1], y)
     xo, wo = synth.to_numpy(x.contiguous()), synth.to_numpy(w.contiguous())
     assert np.all(np.abs(y.cpu().numpy() - oracle.matmul_f64(xo, wo)) <= _f64_bound(xo, wo))
+
+
+def test_matmul_f64_empty_sizes():
+    """K = 0 writes zeros (the empty sum); M = 0 or N = 0 enqueues nothing."""
+    y = torch.full((5, 24), 7.0, dtype=torch.float64, device=DEV)
+    sq.sq_matmul_f64(torch.empty(5, 0, dtype=torch.bfloat16, device=DEV),
+                     torch.empty(0, 24, dtype=torch.float32, device=DEV), y)
+    assert torch.count_nonzero(y).item() == 0
+    y0 = torch.empty(0, 24, dtype=torch.float64, device=DEV)
+    sq.sq_matmul_f64(torch.empty(0, 32, dtype=torch.bfloat16, device=DEV),
+                     torch.ones(32, 24, dtype=torch.bfloat16, device=DEV), y0)
