@@ -63,6 +63,7 @@ HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0    # MI355X dense INT8 MFMA, TOPS (5.0 POP/s)
 METRIC = "W8A8 GEMM TOPS (% INT8 MFMA peak); quant-kernel HBM GB/s (% peak)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_large_8192x12288x49152_traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_large_8192x12288x49152.json")
 GEMM_SOURCES = [os.path.join(ROOT, "post_quantization_act_amd", "csrc", f) for f in ("sq_gemm.hip", "sq_device.h")]
 SECTIONS = ("step", "workloads", "attn_proj", "alpha", "comparator", "probe")
 RUNS = 50          # HIP-event timed calls per workload row (median reported)
@@ -104,6 +105,21 @@ def _traffic():
     if t.get("gemm_source_sha256_16") != gemm_source_hash():
         return None
     return t.get("bytes_per_launch")
+
+
+def _mfma_counters():
+    """Sustained shader clock and matrix-core busy share of the large GEMM from
+    the committed counter summary, or None when it is missing or was taken on
+    a different GEMM source."""
+    try:
+        with open(MFMA_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    return {"shader_clock_ghz": t.get("shader_clock_ghz"), "mfma_busy_pct": t.get("mfma_busy_pct"),
+            "source": "profiles/gemm_mfma_large_8192x12288x49152.json (rocprofv3 --pmc, under the profiler)"}
 
 
 def _cpu_model():
@@ -280,7 +296,8 @@ def _step(torch, sq, synth, pipeline, dev, args):
                                         "(the GEMM alone is roofline.achieved)")},
         "roofline": {"bound": "mfma", "kernel": sq.sq_gemm_kernel_name(M, N, K), "achieved": round(gemm_tops, 1),
                      "peak": INT8_PEAK_TOPS, "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-                     "traffic": _traffic(), "launch_us": round(gemm_avg, 2), "alg_ops_per_launch": ops,
+                     "traffic": _traffic(), "counters": _mfma_counters(), "launch_us": round(gemm_avg, 2),
+                     "alg_ops_per_launch": ops,
                      "launches_timed": len(all_gemm), "gemm_source_sha256_16": gemm_source_hash()},
         "kernels": kernels,
     }
