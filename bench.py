@@ -176,7 +176,7 @@ class _Timer:
         self.torch = torch
         self.runs = runs
 
-    def __call__(self, fn, warm=3, runs=None):
+    def __call__(self, fn, warm=5, runs=None):
         torch = self.torch
         runs = self.runs if runs is None else runs
         for i in range(warm):
@@ -781,7 +781,7 @@ def main():
 
     out, st = _step(torch, sq, synth, pipeline, dev, args)
     if "workloads" in sections:
-        rows = {"timing": f"median of {args.runs} HIP-event timed calls after 3 warm-up calls; inputs rotate over "
+        rows = {"timing": f"median of {args.runs} HIP-event timed calls after 5 warm-up calls; inputs rotate over "
                             f">= {POOL_BYTES / 1e9:.0f} GB of independent copies unless one input is larger"}
         rows["large_8192x12288x49152"] = _workload_large(torch, sq, pipeline, dev, tm, st)
     if "alpha" in sections:
