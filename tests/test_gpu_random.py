@@ -1,9 +1,9 @@
 """Seeded random shapes for the calls whose fixed cases live elsewhere: the
 fused LayerNorm + codes kernel (against the library's contract), the steps 2-4
 call sq_prepare_and_quant_act (against the oracle's steps 2, 3 and 4 directly)
-and the static per-tensor scale.  Every output is compared bit for bit; the
-draws cover ragged token counts, channel counts up to the kernels' limits and
-both granularities."""
+the static per-tensor scale and the few-token (decode) GEMM kernels.  Every
+output is compared bit for bit; the draws cover ragged token counts, channel
+counts up to the kernels' limits and both granularities."""
 import numpy as np
 import pytest
 import torch
@@ -130,3 +130,43 @@ def test_random_static_scale(M, K, T, boost):
     xq_o, xs_o = oracle.quant_act_static(_np(x), inv_s.numpy(), a_o)
     np.testing.assert_array_equal(_np(xs), xs_o)
     np.testing.assert_array_equal(_np(xq), xq_o)
+
+
+def _decode_cases(n, seed):
+    """Few-token products: M <= 16, K a multiple of 2048 up to 16384 (the
+    weight-streaming ring, 1 to 8 chunks per wavefront) or any multiple of 16
+    (the other decode kernel), N from one 16-channel group to 40000 (up to the
+    ring's group limit per block), bf16 or fp32 output, either granularity."""
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(r.integers(1, 17))
+        K = 2048 * int(r.integers(1, 9)) if i % 3 else 16 * int(r.integers(1, 700))
+        N = int(r.integers(1, 40001)) if i % 2 else 16 * int(r.integers(1, 200))
+        out.append((M, K, N, bool(r.random() < 0.6), sq.SQ_PER_TOKEN if r.random() < 0.7 else sq.SQ_PER_TENSOR))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,bf16_out,gran", _decode_cases(10, 1616))
+def test_random_decode_gemm(M, K, N, bf16_out, gran):
+    print(f"random decode M={M} K={K} N={N} bf16={bf16_out} gran={gran} {sq.sq_gemm_kernel_name(M, N, K)[:24]}",
+          flush=True)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(M * 131 + K + N)
+    codes = lambda r, c: torch.clamp(torch.round(torch.randn(r, c, generator=g) * 30.0), -127, 127).to(torch.int8)
+    xq, wq = codes(M, K), codes(N, K)
+    xs = (torch.rand(1 if gran == sq.SQ_PER_TENSOR else M, generator=g) * 1e-2 + 1e-4).float()
+    ws = (torch.rand(N, generator=g) * 1e-2 + 1e-4).float()
+    yt = torch.bfloat16 if bf16_out else torch.float32
+    xd, xsd, wd, wsd = xq.to(DEV), xs.to(DEV), wq.to(DEV), ws.to(DEV)
+    y = torch.empty(M, N, dtype=yt, device=DEV)
+    sq.sq_gemm_w8a8(xd, xsd, gran, wd, wsd, y)  # the deployed call: no accumulator store
+    y_acc = torch.empty(M, N, dtype=yt, device=DEV)
+    acc = torch.empty(M, N, dtype=torch.int32, device=DEV)
+    sq.sq_gemm_w8a8(xd, xsd, gran, wd, wsd, y_acc, acc)
+    torch.cuda.synchronize()
+    acc_o = oracle.gemm_i8(xq.numpy(), wq.numpy(), nthreads=8)
+    y32_o, ybf_o = oracle.dequant(acc_o, xs.numpy(), gran, ws.numpy())
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_o)
+    np.testing.assert_array_equal(_np(y), ybf_o if bf16_out else y32_o)
+    np.testing.assert_array_equal(_np(y_acc), ybf_o if bf16_out else y32_o)
