@@ -214,3 +214,19 @@ def test_llm_int8_attention_projection_full_size():
     n, exact = _compare(b, inp.x, inp.w, 6.0, True, rows=rows)
     assert set(inp.out_idx.tolist()) <= set(b.idx.cpu().numpy()[:n].tolist())
     print(f"  outliers {n}, bit-identical fraction {exact:.4f}", flush=True)
+
+
+def _random_cases(n, seed):
+    """Seeded draws: M in [1, 800], K a multiple of 16 up to 4096, N up to
+    3000, 0-60 outlier channels, threshold 3, 6 or 10, bf16 or fp32 output."""
+    r = np.random.default_rng(seed)
+    return [(int(r.integers(1, 801)), 16 * int(r.integers(1, 257)), int(r.integers(1, 3001)),
+             int(r.integers(0, 61)), float(r.choice([3.0, 6.0, 10.0])), bool(r.random() < 0.6)) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,K,N,n_out,thr,out_bf16", _random_cases(8, 6060))
+def test_llm_int8_random_shapes(M, K, N, n_out, thr, out_bf16):
+    print(f"llm_int8 random M={M} K={K} N={N} n_out={n_out} thr={thr} bf16={out_bf16}", flush=True)
+    x, w = _outlier_data(M, K, N, min(n_out, K), M * 11 + K + N, fac=40.0)
+    b = _run(x, w, thr, torch.bfloat16 if out_bf16 else torch.float32)
+    _compare(b, x, w, thr, out_bf16)
