@@ -512,6 +512,36 @@ def test_gemm_largest_k_extremes(M, N):
         np.testing.assert_array_equal(C @ r, A @ (B.T @ r))
 
 
+@pytest.mark.parametrize("M", [40, 8])
+def test_gemm_weight_codes_beyond_4gib(M):
+    """Wq of 65568 x 65536 codes (4.3 GB, past 32-bit byte offsets): the ring
+    and the weight-streaming decode kernels are ruled out, and the kernels that
+    run instead (the register-staged GEMM for M = 40, the general decode kernel
+    for M = 8) must index it with 64-bit offsets; sampled outputs, including
+    the last channels, against the oracle."""
+    N, K = 65568, 65536
+    assert N * K >= 2 ** 32
+    _say(f"gemm beyond 4 GiB M={M} N={N} K={K}: kernel {sq.sq_gemm_kernel_name(M, N, K)}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4 * M + 1)
+    xq = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=DEV, generator=g)
+    wq = torch.randint(-127, 128, (N, K), dtype=torch.int8, device=DEV, generator=g)
+    xs = torch.rand(M, device=DEV, generator=g) * 1e-3 + 1e-5
+    ws = torch.rand(N, device=DEV, generator=g) * 1e-3 + 1e-5
+    y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    acc = torch.empty(M, N, dtype=torch.int32, device=DEV)
+    sq.sq_gemm_w8a8(xq, xs, sq.SQ_PER_TOKEN, wq, ws, y, acc)
+    torch.cuda.synchronize()
+    cols = torch.cat([torch.arange(0, 64, device=DEV), torch.arange(N // 2, N // 2 + 32, device=DEV),
+                      torch.arange(N - 64, N, device=DEV)])
+    acc_o = oracle.gemm_i8(_np(xq), _np(wq[cols]), nthreads=8)
+    _, ybf_o = oracle.dequant(acc_o, _np(xs), oracle.PER_TOKEN, _np(ws[cols]))
+    np.testing.assert_array_equal(_np(acc[:, cols]), acc_o)
+    np.testing.assert_array_equal(_np(y[:, cols]), ybf_o)
+    del xq, wq, y, acc
+    torch.cuda.empty_cache()
+
+
 def test_per_tensor_dynamic_large_x_streams():
     """Dynamic per-tensor codes of an x above 256 MB (16400 x 8192 bf16): the max
     pass takes its nontemporal-load branch (smaller x is read as plain loads).
