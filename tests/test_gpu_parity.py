@@ -542,6 +542,51 @@ def test_gemm_weight_codes_beyond_4gib(M):
     torch.cuda.empty_cache()
 
 
+def test_quantization_inputs_beyond_4gib():
+    """Calibration tokens, activations and weights of 4.3 GB each (bf16,
+    2^31 elements and more: past 32-bit element and byte offsets): the running
+    maximum over all of them, per-token codes of sampled rows (first, middle,
+    last) and weight codes of sampled output channels (each column's codes
+    depend on that column only) against the oracle."""
+    T, K = 131072, 16384
+    Kw, N = 32768, 65568
+    _say(f"quantization beyond 4 GiB: x {T}x{K}, w {Kw}x{N}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(31)
+    x = (torch.randn(T, K, device=DEV, generator=g) * 2).to(torch.bfloat16)
+    x[:, 77] *= 50
+    amax = torch.zeros(K, dtype=torch.float32, device=DEV)
+    sq.sq_calib_absmax(x, amax)
+    inv_s = (torch.rand(K, device=DEV, generator=g) + 0.5).float()
+    xq = torch.empty(T, K, dtype=torch.int8, device=DEV)
+    xs = torch.empty(T, dtype=torch.float32, device=DEV)
+    sq.sq_quant_act(x, inv_s, sq.SQ_PER_TOKEN, xq, xs)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_np(amax), oracle.calib_absmax(_np(x)))
+    rows = torch.cat([torch.arange(0, 16, device=DEV), torch.arange(T // 2, T // 2 + 16, device=DEV),
+                      torch.arange(T - 16, T, device=DEV)])
+    xq_o, xs_o = oracle.quant_act(_np(x[rows]), _np(inv_s), oracle.PER_TOKEN)
+    np.testing.assert_array_equal(_np(xq[rows]), xq_o)
+    np.testing.assert_array_equal(_np(xs[rows]), xs_o)
+    del x, xq, xs
+    torch.cuda.empty_cache()
+
+    w = (torch.randn(Kw, N, device=DEV, generator=g) * 0.02).to(torch.bfloat16)
+    s = (torch.rand(Kw, device=DEV, generator=g) + 0.5).float()
+    wq = torch.empty(N, Kw, dtype=torch.int8, device=DEV)
+    w_scale = torch.empty(N, dtype=torch.float32, device=DEV)
+    nb = sq.sq_workspace_size(sq.SQ_OP_QUANT_WEIGHT, 0, N, Kw)
+    sq.sq_quant_weight(w, s, wq, w_scale, torch.empty(nb, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    cols = torch.cat([torch.arange(0, 32, device=DEV), torch.arange(N // 2, N // 2 + 32, device=DEV),
+                      torch.arange(N - 32, N, device=DEV)])
+    wq_o, ws_o = oracle.quant_weight(_np(w[:, cols]), _np(s))
+    np.testing.assert_array_equal(_np(wq[cols]), wq_o)
+    np.testing.assert_array_equal(_np(w_scale[cols]), ws_o)
+    del w, wq
+    torch.cuda.empty_cache()
+
+
 def test_per_tensor_dynamic_large_x_streams():
     """Dynamic per-tensor codes of an x above 256 MB (16400 x 8192 bf16): the max
     pass takes its nontemporal-load branch (smaller x is read as plain loads).
