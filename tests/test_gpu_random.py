@@ -27,13 +27,16 @@ def _acts(M, K, g, kind="normal", factor=60.0, dtype=torch.bfloat16):
 
 
 def _ln_cases(n, seed):
+    """M up to 900, K a multiple of 16 up to 16384, with or without beta, and
+    every other case a row stride padded by a multiple of 8 elements."""
     r = np.random.default_rng(seed)
-    return [(int(r.integers(1, 901)), 16 * int(r.integers(1, 1025)), bool(r.random() < 0.7)) for _ in range(n)]
+    return [(int(r.integers(1, 901)), 16 * int(r.integers(1, 1025)), bool(r.random() < 0.7),
+             8 * int(r.integers(1, 9)) if i % 2 else 0) for i in range(n)]
 
 
-@pytest.mark.parametrize("M,K,with_beta", _ln_cases(12, 4242))
-def test_random_layernorm_shapes(M, K, with_beta):
-    print(f"random layernorm M={M} K={K} beta={with_beta}", flush=True)
+@pytest.mark.parametrize("M,K,with_beta,pad", _ln_cases(12, 4242))
+def test_random_layernorm_shapes(M, K, with_beta, pad):
+    print(f"random layernorm M={M} K={K} beta={with_beta} pad={pad}", flush=True)
     g = torch.Generator(device="cpu")
     g.manual_seed(M * 31 + K)
     x, idx = _acts(M, K, g, kind="t4", factor=30.0)
@@ -43,7 +46,9 @@ def test_random_layernorm_shapes(M, K, with_beta):
     beta = (torch.randn(K, generator=g) * 0.1).float() if with_beta else None
     xq = torch.empty(M, K, dtype=torch.int8, device=DEV)
     xs = torch.empty(M, dtype=torch.float32, device=DEV)
-    sq.sq_layernorm_quant(x.to(DEV), gamma.to(DEV), None if beta is None else beta.to(DEV), 1e-5, xq, xs)
+    xd = torch.zeros(M, K + pad, dtype=torch.bfloat16, device=DEV)[:, :K] if pad else torch.empty_like(x, device=DEV)
+    xd.copy_(x.to(DEV))
+    sq.sq_layernorm_quant(xd, gamma.to(DEV), None if beta is None else beta.to(DEV), 1e-5, xq, xs)
     torch.cuda.synchronize()
     xq_o, xs_o = oracle.layernorm_quant(_np(x), gamma.numpy(), None if beta is None else beta.numpy(), 1e-5)
     np.testing.assert_array_equal(_np(xs), xs_o)
