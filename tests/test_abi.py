@@ -321,3 +321,35 @@ def test_outlier_gemm_kernel_choice():
     assert sq.sq_gemm_outlier_kernel_name(2048, 4096, 4096) == sq.sq_gemm_kernel_name(2048, 4096, 4096)
     assert sq.sq_gemm_outlier_kernel_name(16, 28672, 8192).startswith("k_gemm_ring")
     assert sq.sq_gemm_outlier_kernel_name(16, 100, 1040).startswith("k_gemm_generic")
+
+
+def test_last_error_is_per_thread():
+    """Each host thread reads the message of its own last failure: threads
+    that provoke different rejections at the same time never see each other's
+    text (the library's only per-call state is thread-local)."""
+    import threading
+    L = _L()
+    results = {}
+    barrier = threading.Barrier(4)
+
+    def worker(i):
+        barrier.wait()
+        for _ in range(200):
+            if i % 2 == 0:
+                rc = L.sq_calib_absmax(FAKE, sq.SQ_BF16, 8, 20 + 16 * i, 20 + 16 * i, FAKE, None)
+                want = f"K = {20 + 16 * i} must be a multiple of 16"
+            else:
+                rc = L.sq_calib_reset(None, 16 * i, None)
+                want = "amax is NULL"
+            msg = sq.sq_last_error()
+            if rc != -1 or want not in msg:
+                results[i] = msg
+                return
+        results[i] = "ok"
+
+    ts = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert results == {i: "ok" for i in range(4)}, results

@@ -58,3 +58,33 @@ def test_graph_replays_match_eager(gran):
         torch.cuda.synchronize()
         for f in FIELDS:
             assert torch.equal(getattr(b, f), ref_c[f]), ("refilled", rep, f)
+
+
+def test_two_streams_at_once_match_one_stream():
+    """Two default-priority streams run the five calls on their own inputs and
+    buffers at the same time, several passes each without waiting for the
+    other; every result equals the same pass run alone (the library keeps no
+    state between calls other than the per-device CU count)."""
+    cfg = synth.CONFIGS[synth.ATTN_PROJ]
+    M, K, N = 1024, 2048, 2048
+    sets = [synth.make(cfg, device=DEV, M=M, K=K, N=N, calib_chunks=2, chunk_tokens=512, variant=v)
+            for v in range(2)]
+    grans = (sq.SQ_PER_TOKEN, sq.SQ_PER_TENSOR)
+    print("two streams", flush=True)
+    refs = []
+    for s, gran in zip(sets, grans):
+        rb = pipeline.W8A8Buffers.allocate(M, N, K, gran, DEV)
+        pipeline.smoothquant_w8a8(s.x, s.w, s.calib, 0.6, gran, rb)
+        torch.cuda.synchronize()
+        refs.append(_snapshot(rb))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs = [pipeline.W8A8Buffers.allocate(M, N, K, gran, DEV) for gran in grans]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for s, gran, b, st in zip(sets, grans, bufs, streams):
+            pipeline.smoothquant_w8a8(s.x, s.w, s.calib, 0.6, gran, b, stream=st)
+    torch.cuda.synchronize()
+    for ref, b in zip(refs, bufs):
+        got = _snapshot(b)
+        for f in FIELDS:
+            assert torch.equal(got[f], ref[f]), f
