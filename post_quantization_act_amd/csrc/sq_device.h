@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace sqk {
@@ -119,10 +120,52 @@ __host__ __device__ inline bool rows_aligned16(const void* p, int64_t ld, int64_
 }
 
 // Max over the wavefront (all 64 lanes end with the result).
+// Cross-lane reductions over a wavefront without the LDS crossbar: DPP moves
+// inside each row of 16 lanes (lane ^ 1, lane ^ 2, the half-row mirror and the
+// row mirror leave every lane of a row with the row's result), then the four
+// rows' results read into scalar registers and combined, so every lane
+// returns the wavefront's result.  Call with the whole wavefront active.
+template <int kCtrl>
+__device__ __forceinline__ int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(v, v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+    auto step = [&](auto ctrl) {
+        v = fmaxf(v, __int_as_float(dpp_move<decltype(ctrl)::value>(__float_as_int(v))));
+    };
+    step(std::integral_constant<int, kDppXor1>{});
+    step(std::integral_constant<int, kDppXor2>{});
+    step(std::integral_constant<int, kDppHalfMirror>{});
+    step(std::integral_constant<int, kDppMirror>{});
+    const int b = __float_as_int(v);
+    return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+                 fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// Sum over a wavefront in fp64, by the same moves (each half of the double
+// moved on its own).  The order of the additions differs from a sequential
+// loop, so it is exact only where every partial sum is (integer values whose
+// sums stay below 2^53, as the callers use it).
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    auto step = [&](auto ctrl) {
+        const uint64_t u = __builtin_bit_cast(uint64_t, v);
+        const int lo = dpp_move<decltype(ctrl)::value>((int)(uint32_t)u);
+        const int hi = dpp_move<decltype(ctrl)::value>((int)(uint32_t)(u >> 32));
+        v += __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+    };
+    step(std::integral_constant<int, kDppXor1>{});
+    step(std::integral_constant<int, kDppXor2>{});
+    step(std::integral_constant<int, kDppHalfMirror>{});
+    step(std::integral_constant<int, kDppMirror>{});
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+    auto lane = [&](int l) {
+        return __builtin_bit_cast(double, ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, l) << 32) |
+                                              (uint32_t)__builtin_amdgcn_readlane(lo, l));
+    };
+    return (lane(0) + lane(16)) + (lane(32) + lane(48));
 }
 
 // Symmetric INT8 code of v with multiplier r: clamp(rne(fl(v*r)), -127, 127).

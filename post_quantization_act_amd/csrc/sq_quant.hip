@@ -618,11 +618,6 @@ hipError_t launch_quant_weight(const void* w, bool bf16, int64_t K, int64_t N, i
 // p = a (x 2^-E) = x^2 2^(39-2E) whenever p >= 1 (both factors are then
 // normal and the product has at most 16 significant bits); a smaller p
 // truncates to 0 whatever its rounding.  Only the sums run in fp64.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
 
 // One token row per TPB threads (TPB / 64 wavefronts), rows walked with a
 // grid stride; TEAMS teams of TPB threads per block each take their own rows
