@@ -284,7 +284,7 @@ __global__ __launch_bounds__(NT) void k_prep_rows(const bf16_t* __restrict__ w, 
                     smooth_factor<false>(axl[rl], rm, alpha, sj, ij);
                 }
             }
-            sj = __shfl(sj, 0);
+            sj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sj), 0));  // lane 0 to the wavefront
             if (ts == 0) {
                 srow[rl] = sj;
                 irow[rl] = ij;
