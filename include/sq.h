@@ -323,7 +323,8 @@ sq_status sq_quant_act_static(const void *x, sq_dtype xt, int64_t M, int64_t K, 
  *                   Steps 3 and 4 write codes in [-127, 127].  Codes of -128
  *                   from elsewhere are multiplied as they are; the int32 sum
  *                   is then still exact except at K = 131072 with every
- *                   product equal to 128 * 128, where it wraps to -2^31.
+ *                   product equal to 128 * 128, whose sum 2^31 does not fit
+ *                   int32 (the result is then undefined).
  *   y               [M, N] out, dense, dtype yt: SQ_BF16 (the deployed output)
  *                   or SQ_F32 (the fp32 value before the bf16 rounding).
  *   acc_out         [M, N] int32 out, or NULL: the exact accumulators (for
