@@ -38,10 +38,13 @@ Besides the headline line, the JSON carries:
                 1 GB pools: what generic kernels reach on this GPU for the
                 quantizers' read + write pattern and for a read stream;
   cpu_baseline  the CPU oracle as it stands, on the host cores, over bounded
-                samples of the step's stages, scaled to the whole step.
+                samples of the step's stages, scaled to the whole step;
+  tile_sweep    (only when asked for) the 256 x 256 GEMM at 4096 tokens over
+                2-6 tiles per CU and K = 2048-8192, with the time of one tile
+                and the launch's fixed part fitted per K.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
-                    [--sections step,workloads,attn_proj,alpha,comparator,probe]
+                    [--sections step,workloads,attn_proj,alpha,comparator,probe[,tile_sweep]]
 """
 from __future__ import annotations
 
@@ -66,6 +69,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w8a8_large_8192x12288x49152_
 MFMA_FILE = os.path.join(ROOT, "profiles", "gemm_mfma_large_8192x12288x49152.json")
 GEMM_SOURCES = [os.path.join(ROOT, "post_quantization_act_amd", "csrc", f) for f in ("sq_gemm.hip", "sq_device.h")]
 SECTIONS = ("step", "workloads", "attn_proj", "alpha", "comparator", "probe")
+EXTRA_SECTIONS = ("tile_sweep",)  # run only when asked for
 RUNS = 50          # HIP-event timed calls per workload row (median reported)
 POOL_BYTES = 1e9   # rotate inputs over at least this many bytes
 CPU_THREADS_MAX = 16
@@ -78,7 +82,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--sections", default=",".join(SECTIONS),
-                   help="comma list of parts to run besides the headline step (" + ",".join(SECTIONS) + ")")
+                   help="comma list of parts to run besides the headline step (default " + ",".join(SECTIONS) +
+                        "; also " + ",".join(EXTRA_SECTIONS) + ")")
     p.add_argument("--runs", type=int, default=RUNS, help="timed calls per workload row")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="target CPU time of the oracle samples")
     p.add_argument("--copy-probe-mb", type=int, default=0,
@@ -316,6 +321,47 @@ def _vendor_gemm(torch, tm, operands, ops):
     except RuntimeError as e:  # an unsupported shape or build: recorded, not fatal
         return {"error": str(e)[:200]}
     return _tops(t, ops, kernel="torch._int_mm (hipBLASLt)", note="comparison only: int32 output, same codes")
+
+
+def _tile_sweep(torch, sq, dev, tm):
+    """Where the 256 x 256 GEMM's time goes: 4096 tokens, 2 to 6 tiles per CU
+    (N = 8192 .. 24576) and 16 to 64 stages of 128 k-bytes per tile (K = 2048
+    .. 8192), operands rotated over >= 1 GB; per K, a least-squares line
+    through the medians over the tiles per CU.  The codes are
+    clamp(round(N(0, 28^2)), -127, 127), shaped like real ones."""
+    import numpy as np
+    M = 4096
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    g = torch.Generator(device=dev)
+    g.manual_seed(4096)
+
+    def codes(r, c):
+        return torch.clamp(torch.round(torch.randn(r, c, device=dev, generator=g) * 28.0), -127, 127).to(torch.int8)
+
+    rows, per_k = [], {}
+    for K in (2048, 4096, 8192):
+        tiles_l, times = [], []
+        for N in (8192, 12288, 16384, 24576):
+            n = max(1, int(-(-POOL_BYTES // (M * K + N * K))))
+            ops = [(codes(M, K), codes(N, K)) for _ in range(n)]
+            xs = torch.rand(M, device=dev, generator=g) * 1e-3
+            ws = torch.rand(N, device=dev, generator=g) * 1e-3
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            us = tm(lambda i: sq.sq_gemm_w8a8(ops[i % n][0], xs, sq.SQ_PER_TOKEN, ops[i % n][1], ws, y))
+            tiles = M * N / (256 * 256) / cus
+            rows.append({"M": M, "N": N, "K": K, "tiles_per_cu": tiles, "stages_per_tile": K // 128,
+                         **_tops(us, 2.0 * M * N * K), "kernel": sq.sq_gemm_kernel_name(M, N, K)[:30]})
+            tiles_l.append(tiles)
+            times.append(us)
+            del ops, y
+            torch.cuda.empty_cache()
+        slope, icpt = np.polyfit(tiles_l, times, 1)
+        per_k[str(K)] = {"stages_per_tile": K // 128, "us_per_tile": round(float(slope), 2),
+                         "intercept_us": round(float(icpt), 2)}
+    return {"shapes": rows, "per_k_fit": per_k,
+            "note": "median HIP-event times; per K a straight line over tiles per CU: the slope is one tile's "
+                    "time (its stages and the change to the next tile), the intercept the launch's fixed part; "
+                    "the clock falls as runs get longer, so the per-stage time differs between the K"}
 
 
 # ---- the per-workload kernel set -----------------------------------------------------------
@@ -762,8 +808,8 @@ def main():
         sys.exit(2)
     sections = [s for s in args.sections.split(",") if s]
     for s in sections:
-        if s not in SECTIONS:
-            print(f"unknown section {s!r}; choose from {','.join(SECTIONS)}", file=sys.stderr)
+        if s not in SECTIONS + EXTRA_SECTIONS:
+            print(f"unknown section {s!r}; choose from {','.join(SECTIONS + EXTRA_SECTIONS)}", file=sys.stderr)
             sys.exit(2)
 
     import torch
@@ -799,6 +845,8 @@ def main():
         out["llm_int8_comparator"] = _comparator(torch, sq, synth, pipeline, dev, tm)
     if "probe" in sections:
         out["hbm_probe"] = _hbm_probe(torch, dev, tm)
+    if "tile_sweep" in sections:
+        out["tile_sweep"] = _tile_sweep(torch, sq, dev, tm)
     if not args.no_cpu:
         out["cpu_baseline"] = _cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
